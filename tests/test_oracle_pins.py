@@ -1,0 +1,438 @@
+"""Pins of the fp64 oracle to facts fixed outside the oracle itself.
+
+Every check here compares the oracle with something it does not compute: published
+known-answer vectors, textbook/library routines in special cases, brute force over all
+choices, the sampling law (chi-square against the distribution the method must
+reproduce), or identities of the mathematics.  Each is chosen so that a plausible slip in
+the oracle (a dropped term, a wrong sign, a wrong index or operand) fails one of them.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------
+# random numbers
+# ------------------------------------------------------------------------------------
+def test_philox_known_answers():
+    """Philox4x32-10 matches the published known-answer vectors of the SC'11 generator."""
+    n = 0
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            w = [int(x, 16) for x in line.split()]
+            got = oracle.philox4x32(w[0:4], w[4:6])
+            assert [int(x) for x in got] == w[6:10], line
+            n += 1
+    assert n == 3
+
+
+def test_uniform_lattice_and_range():
+    u = oracle.uniforms(123, 0, 1, 0, 0, 1 << 16)
+    m = u * 2.0 ** 24
+    assert np.all(m == np.round(m)) and np.all(np.round(m) % 2 == 1)
+    assert u.min() > 0.0 and u.max() < 1.0
+    # exact in fp32
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)
+
+
+def test_uniform_word_mapping_follows_counter_definition():
+    """u(seed,b,k,s,v) is word v mod 4 of Philox(counter=(v div 4, k, b, s), key=seed)."""
+    seed = 0x0123456789ABCDEF
+    for (b, k, s, v) in [(0, 1, 0, 0), (5, 3, 2, 7), (127, 16, 1, 0), (3, 2, 0, 151935)]:
+        words = oracle.philox4x32([v // 4, k, b, s], [seed & 0xFFFFFFFF, seed >> 32])
+        expect = (2.0 * (int(words[v % 4]) >> 9) + 1.0) * 2.0 ** -24
+        assert oracle.uniforms(seed, b, k, s, v, 1)[0] == expect
+
+
+def test_uniform_chi_square_and_stream_independence():
+    u = oracle.uniforms(7, 3, 2, 0, 0, 1 << 20)
+    counts, _ = np.histogram(u, bins=256, range=(0, 1))
+    assert stats.chisquare(counts).pvalue > 1e-6
+    # different (b, k, s) give unrelated sequences
+    u2 = oracle.uniforms(7, 4, 2, 0, 0, 1 << 16)
+    u3 = oracle.uniforms(7, 3, 2, 2, 0, 1 << 16)
+    assert abs(np.corrcoef(u[:1 << 16], u2)[0, 1]) < 0.02
+    assert abs(np.corrcoef(u[:1 << 16], u3)[0, 1]) < 0.02
+
+
+# ------------------------------------------------------------------------------------
+# draft
+# ------------------------------------------------------------------------------------
+def _tiny(seed=0, **kw):
+    cfg = workload.custom(**kw)
+    return workload.generate(cfg, seed)
+
+
+def test_draft_rows_normalised_and_consistent():
+    inp = _tiny(B=3, gamma=4, V=512, r=8)
+    out = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed, want_probs=True)
+    p = out["probs"]
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-12, rtol=0)
+    tok = out["tokens"]
+    picked = np.take_along_axis(p, tok[..., None], axis=-1)[..., 0]
+    assert np.allclose(np.log(picked), out["logp"], atol=1e-12)
+    assert np.all(out["gap"] > 0)
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.7, 2.0])
+def test_draft_without_markov_bias_is_softmax(temperature):
+    """W2 = 0 removes the Markov bias: p_k = softmax(U_k / T) (library softmax)."""
+    inp = _tiny(B=2, gamma=3, V=300, r=4)
+    W2t = np.zeros_like(inp.W2t)
+    out = oracle.draft(inp.U, inp.W1, W2t, inp.anchor, temperature, inp.seed, want_probs=True)
+    ref = special.softmax(inp.U.astype(np.float64) / temperature, axis=-1)
+    assert np.allclose(out["probs"], ref, atol=1e-13, rtol=1e-11)
+
+
+def test_draft_bias_uses_previous_token_row():
+    """Rank 1 with W1[v] = s_v: bias_k = s_{x_{k-1}} * W2t[:, 0], x_0 = anchor."""
+    rng = np.random.default_rng(5)
+    B, G, V = 3, 4, 64
+    U = rng.normal(size=(B, G, V)).astype(np.float32)
+    s = rng.normal(size=(V, 1)) * 3
+    W2t = rng.normal(size=(V, 1))
+    anchor = rng.integers(0, V, size=B).astype(np.int32)
+    out = oracle.draft(U, s, W2t, anchor, 1.3, 99, want_probs=True)
+    tok = out["tokens"]
+    for b in range(B):
+        prev = [anchor[b]] + list(tok[b, :-1])
+        for k in range(G):
+            z = (U[b, k].astype(np.float64) + s[prev[k], 0] * W2t[:, 0]) / 1.3
+            assert np.allclose(out["probs"][b, k], special.softmax(z), atol=1e-13)
+
+
+def test_draft_gumbel_max_sampling_law():
+    """argmax(z + G) with G = -ln(-ln u) is distributed as softmax(z) (chi-square).
+
+    200k requests share the same logits; each request draws its own uniforms.  Position 2
+    checks the law conditioned on position 1's token (Markov bias through W1)."""
+    rng = np.random.default_rng(11)
+    B, G, V, r = 200000, 2, 8, 2
+    U1 = rng.normal(size=(G, V)) * 1.5
+    U = np.broadcast_to(U1, (B, G, V)).astype(np.float32)
+    W1 = rng.normal(size=(V, r))
+    W2t = rng.normal(size=(V, r))
+    anchor = np.full(B, 3, np.int32)
+    out = oracle.draft(U, W1, W2t, anchor, 1.0, 2024, want_probs=False)
+    tok = out["tokens"]
+    z1 = U1[0].astype(np.float32).astype(np.float64) + W1[3] @ W2t.T
+    p1 = special.softmax(z1)
+    c1 = np.bincount(tok[:, 0], minlength=V)
+    assert stats.chisquare(c1, p1 * B).pvalue > 1e-4
+    for x in range(V):
+        sel = tok[:, 0] == x
+        if sel.sum() < 2000:
+            continue
+        z2 = U1[1].astype(np.float32).astype(np.float64) + W1[x] @ W2t.T
+        p2 = special.softmax(z2)
+        c2 = np.bincount(tok[sel, 1], minlength=V)
+        assert stats.chisquare(c2, p2 * sel.sum()).pvalue > 1e-4
+    # negative control: the law of the wrong-sign Gumbel is far from p
+    assert stats.chisquare(np.bincount(np.argmax(z1[None, :] + np.log(-np.log(
+        rng.uniform(size=(B, V)))), 1), minlength=V), p1 * B).pvalue < 1e-10
+
+
+def test_draft_forced_prefix_reproduces_free_run():
+    inp = _tiny(B=4, gamma=5, V=257, r=8)
+    free = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed)
+    forced = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed,
+                          forced=free["tokens"])
+    for key in ("tokens", "logp", "lse", "gap"):
+        assert np.array_equal(free[key], forced[key])
+
+
+def test_draft_global_request_id_keys_randomness():
+    inp = _tiny(B=4, gamma=3, V=200, r=4)
+    full = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed)
+    sub = oracle.draft(inp.U[2:], inp.W1, inp.W2t, inp.anchor[2:], 1.0, inp.seed, gid=[2, 3])
+    assert np.array_equal(full["tokens"][2:], sub["tokens"])
+
+
+# ------------------------------------------------------------------------------------
+# confidence head
+# ------------------------------------------------------------------------------------
+def test_confidence_special_cases():
+    inp = _tiny(B=3, gamma=4, V=100, r=5, d=7)
+    tokens = np.random.default_rng(1).integers(0, 100, size=(3, 4)).astype(np.int32)
+    d, r = 7, 5
+    w = np.zeros(d + r)
+    assert np.all(oracle.confidence(inp.h, inp.W1, w, inp.anchor, tokens) == 0.5)
+    for j in (0, 3, 6):
+        w = np.zeros(d + r); w[j] = 1.0
+        c = oracle.confidence(inp.h, inp.W1, w, inp.anchor, tokens)
+        assert np.allclose(c, special.expit(inp.h[:, :, j].astype(np.float64)), atol=1e-15)
+    W1 = np.asarray(inp.W1, np.float64)
+    for i in (0, 4):
+        w = np.zeros(d + r); w[d + i] = 2.0
+        c = oracle.confidence(inp.h, inp.W1, w, inp.anchor, tokens)
+        prev = np.concatenate([inp.anchor[:, None], tokens[:, :-1]], axis=1)
+        assert np.allclose(c, special.expit(2.0 * W1[prev, i]), atol=1e-15)
+
+
+# ------------------------------------------------------------------------------------
+# scheduler
+# ------------------------------------------------------------------------------------
+def _theta(c, sps, ell):
+    """Theta(ell) = (B + sum_b sum_{j<=ell_b} prod_{i<=j} c_bi) * SPS(B + sum ell)."""
+    B = c.shape[0]
+    tau = float(B)
+    for b in range(B):
+        a = 1.0
+        for j in range(ell[b]):
+            a *= c[b, j]
+            tau += a
+    return tau * sps[B + int(sum(ell))]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_schedule_matches_brute_force_on_convex_tables(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 4))
+    G = int(rng.integers(1, 5))
+    c = rng.uniform(0.05, 1.0, size=(B, G)).astype(np.float32)
+    N = np.arange(B * (G + 1) + 1, dtype=np.float64)
+    t = rng.uniform(5, 15) + rng.uniform(0, 2) * N + rng.uniform(0, 0.3) * N * N   # convex
+    sps = 1000.0 / t
+    ell, theta, n_total = oracle.schedule(c, sps, 0)
+    c64 = c.astype(np.float64)
+    best = max(_theta(c64, sps, e) for e in itertools.product(range(G + 1), repeat=B))
+    assert abs(theta - best) <= 1e-12 * best
+    assert abs(_theta(c64, sps, ell) - theta) <= 1e-12 * best
+    assert n_total == B + int(ell.sum())
+
+
+def test_schedule_closed_form_half_confidences():
+    """c = 1/2 gives a_j = 2^-j; with t(N) = 10 + N the stop point has a closed form."""
+    B, G = 2, 6
+    c = np.full((B, G), 0.5, np.float32)
+    sps = 1000.0 / (10.0 + np.arange(B * (G + 1) + 1))
+    ell, theta, n_total = oracle.schedule(c, sps, 0)
+    # admitting a token is worth it iff a > tau * dt / t = tau / (10 + N)
+    tau, N, expect = 2.0, 2, [0, 0]
+    order = [(0.5 ** j, b, j) for j in range(1, G + 1) for b in range(B)]
+    order.sort(key=lambda x: (-x[0], x[1], x[2]))
+    for a, b, j in order:
+        if (tau + a) / (10 + N + 1) <= tau / (10 + N):
+            break
+        tau, N = tau + a, N + 1
+        expect[b] = j
+    assert list(ell) == expect and n_total == N
+    assert theta == pytest.approx(1000.0 * tau / (10 + N), rel=1e-15)
+
+
+def test_schedule_flat_and_steep_tables():
+    rng = np.random.default_rng(3)
+    B, G = 5, 4
+    c = rng.uniform(0.01, 0.99, size=(B, G)).astype(np.float32)
+    flat = np.full(B * (G + 1) + 1, 7.0)
+    ell, _, n = oracle.schedule(c, flat, 0)
+    assert np.all(ell == G) and n == B * (G + 1)
+    steep = 1000.0 / (1.0 + 1e6 * np.arange(B * (G + 1) + 1))
+    ell, theta, n = oracle.schedule(c, steep, 0)
+    assert np.all(ell == 0) and n == B and theta == B * steep[B]
+    ell, _, n = oracle.schedule(c, steep, 1)
+    assert np.all(ell == G) and n == B * (G + 1)
+
+
+def test_schedule_tie_order_request_then_position():
+    """Equal survival: the lower request index is admitted first, then the lower j."""
+    c = np.array([[0.5], [0.5]], np.float32)
+    sps = np.array([0.0, 0.0, 1.0, 1.0, 0.8])
+    ell, theta, n = oracle.schedule(c, sps, 0)
+    assert list(ell) == [1, 0] and theta == 2.5 and n == 3
+    c = np.array([[1.0, 1.0, 0.5]], np.float32)
+    sps = np.array([0, 1.0, 1.0, 1.0, 0.5])
+    ell, theta, n = oracle.schedule(c, sps, 0)
+    assert list(ell) == [2] and theta == 3.0
+
+
+# ------------------------------------------------------------------------------------
+# verification
+# ------------------------------------------------------------------------------------
+def test_verify_identical_target_accepts_everything():
+    inp = _tiny(B=4, gamma=4, V=256, r=8)
+    W2t = np.zeros_like(inp.W2t)
+    d = oracle.draft(inp.U, inp.W1, W2t, inp.anchor, 0.8, inp.seed)
+    T = np.concatenate([inp.U, inp.U_extra[:, None, :]], axis=1)
+    ell = np.array([4, 2, 0, 3], np.int32)
+    v = oracle.verify(inp.U, inp.W1, W2t, inp.anchor, d["tokens"], T, ell, 0.8, inp.seed)
+    assert np.array_equal(v["n_accept"], ell)
+    assert np.all(v["kind"] == 0)
+    for b in range(4):
+        assert np.array_equal(v["out_tokens"][b, :ell[b]], d["tokens"][b, :ell[b]])
+        assert np.all(v["out_tokens"][b, ell[b] + 1:] == -1)
+
+
+def test_verify_one_hot_target_rejects_and_corrects():
+    inp = _tiny(B=3, gamma=3, V=128, r=4)
+    d = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed)
+    T = np.full((3, 4, 128), -1e4, np.float32)
+    vstar = (d["tokens"][:, 0] + 5) % 128
+    T[np.arange(3), 0, vstar] = 0.0
+    v = oracle.verify(inp.U, inp.W1, inp.W2t, inp.anchor, d["tokens"], T,
+                      np.full(3, 3, np.int32), 1.0, inp.seed)
+    assert np.all(v["n_accept"] == 0)
+    assert np.array_equal(v["out_tokens"][:, 0], vstar)
+    assert np.all(v["out_tokens"][:, 1:] == -1) and np.all(v["kind"] == 1)
+
+
+def _markov_tables(rng, G, V, conc):
+    """log p_t,k(. | prev) for k = 1..G+1, shape [G+1][V(prev)][V]."""
+    p = rng.dirichlet(np.full(V, conc), size=(G + 1, V))
+    return np.log(p)
+
+
+def _complete_and_histogram(rng, out_tokens, logpt, anchor, G, V):
+    """Complete each emitted prefix with the target chain; histogram full strings."""
+    B = out_tokens.shape[0]
+    seq = out_tokens.astype(np.int64).copy()
+    pt = np.exp(logpt)
+    for k in range(G + 1):
+        need = seq[:, k] < 0
+        if not need.any():
+            continue
+        prev = anchor[need] if k == 0 else seq[need, k - 1]
+        cdf = np.cumsum(pt[k][prev], axis=1)
+        u = rng.uniform(size=need.sum())[:, None]
+        seq[need, k] = np.minimum((u > cdf).sum(1), V - 1)
+    code = np.zeros(B, np.int64)
+    for k in range(G + 1):
+        code = code * V + seq[:, k]
+    return np.bincount(code, minlength=V ** (G + 1))
+
+
+def _target_law(logpt, a0, G, V):
+    prob = np.zeros(V ** (G + 1))
+    for i, ys in enumerate(itertools.product(range(V), repeat=G + 1)):
+        lp, prev = 0.0, a0
+        for k, y in enumerate(ys):
+            lp += logpt[k][prev][y]
+            prev = y
+        prob[i] = np.exp(lp)
+    return prob
+
+
+def _lossless_round(rng, B, G, V, r, ell_rule, seed):
+    """Draft with a Markov head, build Markov target rows, verify with ell from ell_rule."""
+    U1 = rng.normal(size=(G, V)) * 1.2
+    U = np.broadcast_to(U1, (B, G, V)).astype(np.float32)
+    W1 = rng.normal(size=(V, r))
+    W2t = rng.normal(size=(V, r))
+    anchor = np.full(B, 1, np.int32)
+    logpt = _markov_tables(rng, G, V, 1.0)
+    d = oracle.draft(U, W1, W2t, anchor, 1.0, seed)
+    tok = d["tokens"]
+    prev = np.concatenate([anchor[:, None], tok], axis=1)             # x_0..x_G
+    T = np.stack([logpt[k][prev[:, k]] for k in range(G + 1)], axis=1).astype(np.float64)
+    ell = ell_rule(tok, d, T).astype(np.int32)
+    v = oracle.verify(U, W1, W2t, anchor, tok, T, ell, 1.0, seed)
+    hist = _complete_and_histogram(rng, v["out_tokens"], logpt, anchor, G, V)
+    law = _target_law(logpt, 1, G, V)
+    return hist, law, v
+
+
+def _chi2_p(hist, law):
+    n = hist.sum()
+    keep = law * n > 5
+    obs = np.append(hist[keep], hist[~keep].sum())
+    exp = np.append(law[keep], law[~keep].sum()) * n
+    return stats.chisquare(obs, exp).pvalue
+
+
+@pytest.mark.parametrize("rule", ["full", "fixed_mix", "scheduler"])
+def test_verify_is_lossless_monte_carlo(rule):
+    """The emitted tokens, completed with the target chain, follow the target law."""
+    rng = np.random.default_rng({"full": 1, "fixed_mix": 2, "scheduler": 3}[rule])
+    B, G, V, r = 200000, 3, 4, 2
+
+    def ell_rule(tok, d, T):
+        if rule == "full":
+            return np.full(B, G)
+        if rule == "fixed_mix":
+            return np.arange(B) % (G + 1)
+        # confidence head + greedy scheduler: admission of x_k uses c_1..c_k only,
+        # and c_k depends on x_{k-1}, never on x_k (non-anticipating)
+        h = rng.normal(size=(B, G, 3))
+        w = rng.normal(size=3 + r)
+        c = oracle.confidence(h, np.eye(V, r) * 3.0, w, np.full(B, 1), tok).astype(np.float32)
+        N = np.arange(B * (G + 1) + 1, dtype=np.float64)
+        sps = 1000.0 / (10.0 + 3.0 * N / B + 1.0 * (N / B) ** 2)
+        return oracle.schedule(c, sps, 0)[0]
+
+    hist, law, v = _lossless_round(rng, B, G, V, r, ell_rule, seed=77 + len(rule))
+    assert _chi2_p(hist, law) > 1e-4
+    if rule != "fixed_mix":
+        assert (v["kind"] == 1).any()
+
+
+def test_verify_losslessness_check_has_power():
+    """Negative control: truncating on the drafted token itself (anticipating) is biased."""
+    rng = np.random.default_rng(9)
+    B, G, V, r = 200000, 3, 4, 2
+
+    def anticipating(tok, d, T):
+        # stop right before the first token the target likes less than the draft
+        pt = np.exp(np.take_along_axis(T[:, :G], tok[..., None], axis=2)[..., 0])
+        bad = pt < np.exp(d["logp"])
+        first = np.where(bad.any(1), bad.argmax(1), G)
+        return first
+
+    hist, law, _ = _lossless_round(rng, B, G, V, r, anticipating, seed=5)
+    assert _chi2_p(hist, law) < 1e-12
+
+
+def test_verify_acceptance_frequency_equals_tv_rate():
+    """P(accept x_1) = sum_v min(p_d, p_t) = alpha (Monte Carlo, 5-sigma)."""
+    rng = np.random.default_rng(4)
+    B, G, V, r = 100000, 1, 16, 3
+    U = np.broadcast_to(rng.normal(size=(G, V)), (B, G, V)).astype(np.float32)
+    W1 = rng.normal(size=(V, r)) * 0.5
+    W2t = rng.normal(size=(V, r)) * 0.5
+    anchor = np.full(B, 2, np.int32)
+    T1 = rng.normal(size=(G + 1, V)) * 1.5
+    T = np.broadcast_to(T1, (B, G + 1, V)).astype(np.float64)
+    d = oracle.draft(U, W1, W2t, anchor, 1.0, 31)
+    v = oracle.verify(U, W1, W2t, anchor, d["tokens"], T, np.ones(B, np.int32), 1.0, 31)
+    alpha, l1 = oracle.accept_tv(U[:1], W1, W2t, anchor[:1], d["tokens"][:1], T[:1], 1.0)
+    freq = v["n_accept"].mean()
+    a = alpha[0, 0]
+    assert abs(freq - a) < 5 * np.sqrt(a * (1 - a) / B)
+
+
+# ------------------------------------------------------------------------------------
+# analytic accept rate
+# ------------------------------------------------------------------------------------
+def test_tv_identity_and_bounds():
+    inp = _tiny(B=3, gamma=4, V=300, r=6)
+    d = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed, want_probs=True)
+    T = workload.synthesize_target(inp, d["tokens"])
+    alpha, l1 = oracle.accept_tv(inp.U, inp.W1, inp.W2t, inp.anchor, d["tokens"], T, 1.0)
+    assert np.allclose(alpha, l1, atol=1e-13)
+    assert np.all((alpha > 0) & (alpha < 1))
+    # alpha = sum_x p_d(x) min(1, p_t(x)/p_d(x)): the exact acceptance probability
+    pt = special.softmax(T[:, :4].astype(np.float64), axis=-1)
+    pd = d["probs"]
+    assert np.allclose(alpha, (pd * np.minimum(1.0, pt / pd)).sum(-1), atol=1e-13)
+
+
+def test_tv_is_one_for_identical_and_zero_for_disjoint():
+    inp = _tiny(B=2, gamma=2, V=64, r=4)
+    W2t = np.zeros_like(inp.W2t)
+    tok = np.zeros((2, 2), np.int32)
+    T = np.concatenate([inp.U, inp.U_extra[:, None]], axis=1) / 0.5
+    alpha, _ = oracle.accept_tv(inp.U, inp.W1, W2t, inp.anchor, tok, T * 0.5, 1.0)
+    assert np.allclose(alpha, 1.0, atol=1e-13)
+    U = np.full((2, 2, 64), -1e4, np.float32); U[:, :, :32] = 0
+    T = np.full((2, 3, 64), -1e4, np.float32); T[:, :, 32:] = 0
+    alpha, _ = oracle.accept_tv(U, inp.W1, W2t, inp.anchor, tok, T, 1.0)
+    assert np.all(alpha < 1e-300)
