@@ -1,0 +1,281 @@
+"""Python binding of libdspark.so, the gfx950 library for one DSpark draft/verify round.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current stream.  The functions carry the C names of include/dspark.h
+and take/return torch tensors on the GPU:
+
+    dspark_draft_markov      Markov-head draft (gamma sequential softmax + Gumbel-max draws)
+    dspark_confidence        c_k = sigmoid(w . [h_k ; W1[x_{k-1}]])
+    dspark_schedule          greedy prefix scheduler maximising tau * SPS(N)
+    dspark_verify            lossless rejection-sampling verification
+    dspark_accept_rate_tv    analytic accept rate sum_v min(p_d, p_t)
+    dspark_rng_uniforms      the uniforms of the random-number definition (generator check)
+
+bf16 tensors may be given as torch.bfloat16 or as int16 views of the raw bits.
+There is no fallback: if the library is not built, importing succeeds but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdspark.so")
+
+F32, BF16 = 0, 1
+SCHED_GREEDY, SCHED_FULL = 0, 1
+OP_DRAFT, OP_CONFIDENCE, OP_SCHEDULE, OP_VERIFY, OP_TV = 0, 1, 2, 3, 4
+
+_lib = None
+_lock = threading.Lock()
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("hidden", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m draft_verify_sampling_step_amd.build` (hipcc, gfx950)")
+            L = ctypes.CDLL(LIB_PATH)
+            D = ctypes.POINTER(Dims)
+            L.dspark_workspace_bytes.argtypes = [_I, D]
+            L.dspark_workspace_bytes.restype = _SZ
+            L.dspark_status_string.argtypes = [_I]
+            L.dspark_status_string.restype = ctypes.c_char_p
+            L.dspark_version.restype = _I
+            L.dspark_draft_markov.argtypes = [D, _P, _P, _P, _I, _P, _P, _F, _U64, _P, _P, _P,
+                                              _P, _SZ, _P]
+            L.dspark_confidence.argtypes = [D, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P]
+            L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _I, _P, _P,
+                                          _P, _P, _SZ, _P]
+            L.dspark_verify.argtypes = [D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _F, _U64,
+                                        _P, _P, _P, _P, _SZ, _P]
+            L.dspark_accept_rate_tv.argtypes = [D, _P, _P, _P, _I, _P, _P, _P, _P, _F, _P, _P,
+                                                _SZ, _P]
+            L.dspark_rng_uniforms.argtypes = [_U64, ctypes.c_uint32, ctypes.c_uint32,
+                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
+                                              _P, _P]
+            for fn in ("dspark_draft_markov", "dspark_confidence", "dspark_schedule",
+                       "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms"):
+                getattr(L, fn).restype = _I
+            _lib = L
+    return _lib
+
+
+class DsparkError(RuntimeError):
+    pass
+
+
+def _check(status: int):
+    if status != 0:
+        raise DsparkError(lib().dspark_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _wdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    return t
+
+
+def _f32(t: torch.Tensor, name: str):
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32")
+    return t
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_bytes(op: int, B: int, gamma: int, V: int, r: int, d: int = 0) -> int:
+    dm = Dims(B, gamma, V, r, d)
+    return int(lib().dspark_workspace_bytes(op, ctypes.byref(dm)))
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int, ws: Optional[torch.Tensor]):
+    """Caller-given workspace, or a per-device cached buffer (calls on one stream only)."""
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    key = (device.type, device.index)
+    cur = _ws_cache.get(key)
+    if cur is None or cur.numel() < nbytes:
+        cur = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = cur
+    return cur
+
+
+# ------------------------------------------------------------------------------------
+# the calls
+# ------------------------------------------------------------------------------------
+def dspark_draft_markov(U, W1, W2t, anchor, temperature: float, seed: int, forced=None,
+                        out=None, ws=None, stream=None):
+    """Markov-head draft.  U [B][gamma][V] f32, W1/W2t [V][r], anchor [B] int32.
+
+    Returns (tokens [B][gamma] int32, logp [B][gamma] f32, lse [B][gamma] f32)."""
+    B, G, V = U.shape
+    r = W1.shape[1]
+    _f32(U, "U")
+    _i32(anchor, "anchor")
+    if forced is not None:
+        _i32(forced, "forced")
+    wdt = _wdtype(W1)
+    if _wdtype(W2t) != wdt:
+        raise ValueError("W1 and W2t must have the same dtype")
+    if out is None:
+        out = (torch.empty((B, G), dtype=torch.int32, device=U.device),
+               torch.empty((B, G), dtype=torch.float32, device=U.device),
+               torch.empty((B, G), dtype=torch.float32, device=U.device))
+    tokens, logp, lse = out
+    dm = Dims(B, G, V, r, 0)
+    need = int(lib().dspark_workspace_bytes(OP_DRAFT, ctypes.byref(dm)))
+    w = _workspace(U.device, need, ws)
+    _check(lib().dspark_draft_markov(ctypes.byref(dm), _ptr(U), _ptr(W1), _ptr(W2t), wdt,
+                                     _ptr(anchor), _ptr(forced), float(temperature),
+                                     int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens), _ptr(logp),
+                                     _ptr(lse), _ptr(w), w.numel(), _stream_handle(stream)))
+    return tokens, logp, lse
+
+
+def dspark_confidence(h, W1, w, anchor, tokens, out=None, stream=None):
+    """c [B][gamma] f32 = sigmoid(w . [h_k ; W1[x_{k-1}]])."""
+    B, G, d = h.shape
+    V, r = W1.shape
+    _i32(anchor, "anchor")
+    _i32(tokens, "tokens")
+    c = out if out is not None else torch.empty((B, G), dtype=torch.float32, device=h.device)
+    dm = Dims(B, G, V, r, d)
+    _check(lib().dspark_confidence(ctypes.byref(dm), _ptr(h), _wdtype(h), _ptr(W1), _wdtype(W1),
+                                   _ptr(w), _wdtype(w), _ptr(anchor), _ptr(tokens), _ptr(c),
+                                   _stream_handle(stream)))
+    return c
+
+
+def dspark_schedule(c, sps, mode: int = SCHED_GREEDY, out=None, stream=None):
+    """Greedy prefix scheduler.  Returns (ell [B] int32, theta [1] f64, n_total [1] int32)."""
+    B, G = c.shape
+    _f32(c, "c")
+    if sps.dtype != torch.float64:
+        raise ValueError("sps must be float64")
+    if sps.numel() < B * (G + 1) + 1:
+        raise ValueError("sps must have B*(gamma+1)+1 entries")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=c.device),
+               torch.empty(1, dtype=torch.float64, device=c.device),
+               torch.empty(1, dtype=torch.int32, device=c.device))
+    ell, theta, n_total = out
+    _check(lib().dspark_schedule(B, G, _ptr(c), _ptr(sps), int(mode), _ptr(ell), _ptr(theta),
+                                 _ptr(n_total), None, 0, _stream_handle(stream)))
+    return ell, theta, n_total
+
+
+def dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temperature: float,
+                  seed: int, want_pt: bool = True, out=None, ws=None, stream=None):
+    """Rejection-sampling verification.
+
+    Returns (n_accept [B] int32, out_tokens [B][gamma+1] int32, pt_tok [B][gamma] f32|None)."""
+    B, G, V = U.shape
+    r = W1.shape[1]
+    for t, n in ((U, "U"), (logp, "logp"), (lse, "lse"), (T, "T")):
+        _f32(t, n)
+    for t, n in ((anchor, "anchor"), (tokens, "tokens"), (ell, "ell")):
+        _i32(t, n)
+    if tuple(T.shape) != (B, G + 1, V):
+        raise ValueError("T must be [B][gamma+1][V]")
+    wdt = _wdtype(W1)
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=U.device),
+               torch.empty((B, G + 1), dtype=torch.int32, device=U.device),
+               torch.empty((B, G), dtype=torch.float32, device=U.device) if want_pt else None)
+    n_acc, out_tok, pt = out
+    dm = Dims(B, G, V, r, 0)
+    need = int(lib().dspark_workspace_bytes(OP_VERIFY, ctypes.byref(dm)))
+    w = _workspace(U.device, need, ws)
+    _check(lib().dspark_verify(ctypes.byref(dm), _ptr(U), _ptr(W1), _ptr(W2t), wdt,
+                               _ptr(anchor), _ptr(tokens), _ptr(logp), _ptr(lse), _ptr(T),
+                               _ptr(ell), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                               _ptr(n_acc), _ptr(out_tok), _ptr(pt), _ptr(w), w.numel(),
+                               _stream_handle(stream)))
+    return n_acc, out_tok, pt
+
+
+def dspark_accept_rate_tv(U, W1, W2t, anchor, tokens, lse, T, temperature: float, out=None,
+                          ws=None, stream=None):
+    """alpha [B][gamma] f32 = sum_v min(p_d, p_t)."""
+    B, G, V = U.shape
+    r = W1.shape[1]
+    alpha = out if out is not None else torch.empty((B, G), dtype=torch.float32,
+                                                    device=U.device)
+    dm = Dims(B, G, V, r, 0)
+    need = int(lib().dspark_workspace_bytes(OP_TV, ctypes.byref(dm)))
+    w = _workspace(U.device, need, ws)
+    _check(lib().dspark_accept_rate_tv(ctypes.byref(dm), _ptr(U), _ptr(W1), _ptr(W2t),
+                                       _wdtype(W1), _ptr(anchor), _ptr(tokens), _ptr(lse),
+                                       _ptr(T), float(temperature), _ptr(alpha), _ptr(w),
+                                       w.numel(), _stream_handle(stream)))
+    return alpha
+
+
+def dspark_rng_uniforms(seed: int, b: int, k: int, s: int, v0: int, n: int, device="cuda",
+                        stream=None):
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    _check(lib().dspark_rng_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, b, k, s, v0, n, _ptr(out),
+                                     _stream_handle(stream)))
+    return out
+
+
+# ------------------------------------------------------------------------------------
+# host <-> device helpers for the synthetic inputs
+# ------------------------------------------------------------------------------------
+def to_device(a, device="cuda"):
+    """numpy -> torch on the GPU; uint16 arrays (bf16 bit patterns) become bfloat16."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)

@@ -1,0 +1,98 @@
+// confidence.hip -- confidence head [CSDN Eq. 7; XTL §5]:
+//   c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]),  x_0 = anchor, no bias term.
+// One wave per (request, position): a wave-reduced dot product of length d + r with
+// coalesced 16-byte loads where the element type allows.
+#include "dspark_dev.h"
+#include "dspark_host.h"
+
+namespace dspark {
+
+// Sum of w[j] * x[j] over j < n, lanes striding 8 elements (16-byte loads for bf16 when
+// both pointers are 16-byte aligned), element by element otherwise.
+template <typename TA, typename TB>
+__device__ __forceinline__ float lane_dot(const TA* w, const TB* x, int n, int lane) {
+  float acc = 0.f;
+  for (int j = lane; j < n; j += kWave) acc = fmaf(Elem<TA>::get(w, j), Elem<TB>::get(x, j), acc);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float lane_dot<uint16_t, uint16_t>(const uint16_t* w,
+                                                             const uint16_t* x, int n,
+                                                             int lane) {
+  float acc = 0.f;
+  const bool aligned = ((((uintptr_t)w) | ((uintptr_t)x)) & 15) == 0;
+  int j0 = 0;
+  if (aligned) {
+    const int nv = n & ~511;   // whole 64-lane x 8-element rounds
+    for (int j = lane * 8; j < nv; j += kWave * 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(w + j);
+      const uint4 b = *reinterpret_cast<const uint4*>(x + j);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc);
+        acc = fmaf(__uint_as_float(av[q] & 0xFFFF0000u), __uint_as_float(bv[q] & 0xFFFF0000u),
+                   acc);
+      }
+    }
+    j0 = nv;
+  }
+  for (int j = j0 + lane; j < n; j += kWave) acc = fmaf(bf16_to_f32(w[j]), bf16_to_f32(x[j]), acc);
+  return acc;
+}
+
+template <typename TH, typename TW1, typename TWV>
+__global__ __launch_bounds__(256) void k_confidence(const TH* __restrict__ h,
+                                                    const TW1* __restrict__ W1,
+                                                    const TWV* __restrict__ w,
+                                                    const int32_t* __restrict__ anchor,
+                                                    const int32_t* __restrict__ tokens,
+                                                    float* __restrict__ c, int B, int G, int d,
+                                                    int r) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= B * G) return;
+  const int b = wid / G, k = wid % G + 1;
+  const int prev = (k == 1) ? anchor[b] : tokens[(size_t)b * G + (k - 2)];
+  float acc = lane_dot<TWV, TH>(w, h + (size_t)wid * d, d, lane);
+  acc += lane_dot<TWV, TW1>(w + d, W1 + (size_t)prev * r, r, lane);
+  acc = wave_sum(acc);
+  if (lane == 0) c[wid] = 1.0f / (1.0f + expf(-acc));
+}
+
+template <typename TH, typename TW1, typename TWV>
+static void launch_conf(const dspark_dims* dm, const void* h, const void* W1, const void* w,
+                        const int32_t* anchor, const int32_t* tokens, float* c,
+                        hipStream_t st) {
+  const int n = dm->batch * dm->gamma;
+  hipLaunchKernelGGL((k_confidence<TH, TW1, TWV>), dim3((n + 3) / 4), dim3(256), 0, st,
+                     (const TH*)h, (const TW1*)W1, (const TWV*)w, anchor, tokens, c,
+                     dm->batch, dm->gamma, dm->hidden, dm->rank);
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" dspark_status dspark_confidence(const dspark_dims* dm, const void* h, int hdt,
+                                           const void* W1, int wdt, const void* w, int wvdt,
+                                           const int32_t* anchor, const int32_t* tokens,
+                                           float* c, void* stream) {
+  if (!dm || !W1 || !w || !anchor || !tokens || !c) return DSPARK_E_NULL;
+  if (!dims_ok(dm)) return DSPARK_E_SHAPE;
+  if (dm->hidden > 0 && !h) return DSPARK_E_NULL;
+  if (!dtype_ok(hdt) || !dtype_ok(wdt) || !dtype_ok(wvdt)) return DSPARK_E_DTYPE;
+  hipStream_t st = (hipStream_t)stream;
+  const int code = (hdt << 2) | (wdt << 1) | wvdt;
+  switch (code) {
+    case 0: launch_conf<float, float, float>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 1: launch_conf<float, float, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 2: launch_conf<float, uint16_t, float>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 3: launch_conf<float, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 4: launch_conf<uint16_t, float, float>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 5: launch_conf<uint16_t, float, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 6: launch_conf<uint16_t, uint16_t, float>(dm, h, W1, w, anchor, tokens, c, st); break;
+    default: launch_conf<uint16_t, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
+  }
+  return launch_status();
+}

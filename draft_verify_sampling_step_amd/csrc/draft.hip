@@ -1,0 +1,207 @@
+// draft.hip -- Markov-head draft step [CSDN Eq. 4; XTL §3-4]: gamma sequential positions,
+// each a rank-r bias added to the backbone logits, a full-vocabulary softmax and a
+// Gumbel-max draw.
+//
+// One kernel launch per position: the launch boundary is the device-wide dependency
+// x_{k-1} -> bias of position k (on MI355X a kernel boundary is several times cheaper
+// than an in-kernel grid barrier).  Each workgroup covers a vocabulary slice and reports
+//   - a packed (score, index) candidate through a 64-bit atomic max (order-free), and
+//   - its partial softmax state (m, l) plus its local winner's logit, to a fixed slot.
+// The next position decodes x_{k-1} from the atomic word; a final kernel merges the
+// partial states in slice order into lse and log p_d(x_k).
+#include "dspark_dev.h"
+#include "dspark_host.h"
+#include "mfma_bias.h"
+#include "rowbias.h"
+
+namespace dspark {
+
+__global__ void k_fill_u64(unsigned long long* p, size_t n, unsigned long long v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__device__ __forceinline__ int draft_prev(const int32_t* anchor, const int32_t* forced,
+                                          const unsigned long long* best_prev, int b, int G,
+                                          int k) {
+  if (k == 1) return anchor[b];
+  if (forced) return forced[(size_t)b * G + (k - 2)];
+  return (int)packed_index(best_prev[b]);
+}
+
+// Row path: grid (slices, B), 256 threads.  Thread t of a tile owns vocab row tile0 + t.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_draft_row(
+    const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ forced,
+    const unsigned long long* __restrict__ best_prev, unsigned long long* __restrict__ best_cur,
+    float4* __restrict__ part, int B, int G, int V, int r, int k, float invT, uint32_t key0,
+    uint32_t key1, int slice_len) {
+  extern __shared__ float smem[];
+  float* w1s = smem;            // [r]
+  float* bias_s = smem + r;     // [256]
+  float* red = bias_s + 256;    // [16]
+  const int b = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const int v_begin = s * slice_len;
+  const int v_end = min(V, v_begin + slice_len);
+  const int prev = draft_prev(anchor, forced, best_prev, b, G, k);
+  load_w1_row<WT>(W1, prev, r, w1s);
+  __syncthreads();
+  const float* Urow = U + ((size_t)b * G + (k - 1)) * V;
+  ML st{-INFINITY, 0.f};
+  Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+  for (int tile0 = v_begin; tile0 < v_end; tile0 += kRowTile) {
+    row_bias_tile<WT>(W2t, w1s, bias_s, r, tile0, v_end);
+    __syncthreads();
+    const int v = tile0 + tid;
+    if (v < v_end) {
+      const float z = (Urow[v] + bias_s[tid]) * invT;
+      const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 0u, key0, key1);
+      const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
+      const float score = z + gumbel_from_uniform(word_to_uniform(word));
+      if (z > st.m) {
+        st.l = st.l * fast_exp(st.m - z) + 1.f;
+        st.m = z;
+      } else {
+        st.l += fast_exp(z - st.m);
+      }
+      if (score > best.s) best = Cand{score, (uint32_t)v, z};
+    }
+    __syncthreads();
+  }
+  st = block_ml(st, red, red + 4);
+  best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
+  if (tid == 0) {
+    part[(size_t)s * B + b] = make_float4(st.m, st.l, best.z, __uint_as_float(best.i));
+    atomic_max_u64(&best_cur[b], pack_score(best.s, best.i));
+  }
+}
+
+// Final merge: one wave per (b, k).  part is [gamma][slices][B].
+__global__ __launch_bounds__(256) void k_draft_final(
+    const float4* __restrict__ part, const unsigned long long* __restrict__ best, int B, int G,
+    int nslices, int32_t* __restrict__ tokens, float* __restrict__ logp,
+    float* __restrict__ lse) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= B * G) return;
+  const int b = wid % B, kk = wid / B;
+  const uint32_t idx = packed_index(best[(size_t)kk * B + b]);
+  ML st{-INFINITY, 0.f};
+  float zx = 0.f;
+  int found = 0;
+  for (int s = lane; s < nslices; s += kWave) {
+    const float4 p = part[((size_t)kk * nslices + s) * B + b];
+    st = ml_merge(st, ML{p.x, p.y});
+    if (__float_as_uint(p.w) == idx) { zx = p.z; found = 1; }
+  }
+  st = wave_ml(st);
+  // exactly one slice holds the winner
+  const unsigned long long m = __ballot(found);
+  const int src = m ? __ffsll((long long)m) - 1 : 0;
+  zx = __shfl(zx, src, kWave);
+  if (lane == 0) {
+    const float l = st.m + fast_log(st.l);
+    const size_t o = (size_t)b * G + kk;
+    tokens[o] = (int32_t)idx;
+    lse[o] = l;
+    logp[o] = zx - l;
+  }
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+namespace {
+
+struct DraftPlan {
+  bool mfma;
+  int nslices;     // partial-state slots per (position, request)
+  int slice_len;   // row path only
+};
+
+DraftPlan draft_plan(const dspark_dims* d, int wdt) {
+  DraftPlan p{};
+  p.mfma = mfma_bias_supported(d->batch, d->rank, wdt);
+  if (p.mfma) {
+    p.nslices = mfma_grid(d->vocab, d->batch);
+    p.slice_len = 0;
+  } else {
+    RowSlices s = row_slices(d->vocab, d->batch);
+    p.nslices = s.count;
+    p.slice_len = s.len;
+  }
+  return p;
+}
+
+size_t draft_ws(const dspark_dims* d, int nslices, unsigned long long** best, float4** part,
+                void* base) {
+  Carve c(base);
+  *best = c.take<unsigned long long>((size_t)d->gamma * d->batch);
+  *part = c.take<float4>((size_t)d->gamma * nslices * d->batch);
+  return align_up(c.off, 256);
+}
+
+}  // namespace
+
+size_t dspark_draft_workspace(const dspark_dims* d) {
+  unsigned long long* b;
+  float4* p;
+  const int ns = std::max(row_slices(d->vocab, d->batch).count, mfma_workgroups(d->vocab));
+  return draft_ws(d, ns, &b, &p, nullptr);
+}
+
+extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float* U,
+                                             const void* W1, const void* W2t, int wdt,
+                                             const int32_t* anchor, const int32_t* forced,
+                                             float temperature, uint64_t seed,
+                                             int32_t* tokens, float* logp, float* lse,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  if (!dm || !U || !W1 || !W2t || !anchor || !tokens || !logp || !lse) return DSPARK_E_NULL;
+  if (!dims_ok(dm)) return DSPARK_E_SHAPE;
+  if (!dtype_ok(wdt)) return DSPARK_E_DTYPE;
+  if (!temp_ok(temperature)) return DSPARK_E_VALUE;
+  const size_t need = dspark_draft_workspace(dm);
+  if (!ws || ws_bytes < need) return DSPARK_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int B = dm->batch, G = dm->gamma, V = dm->vocab, r = dm->rank;
+  const DraftPlan plan = draft_plan(dm, wdt);
+  unsigned long long* best;
+  float4* part;
+  draft_ws(dm, plan.nslices, &best, &part, ws);
+  const float invT = 1.0f / temperature;
+  const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+
+  hipLaunchKernelGGL(k_fill_u64, dim3(std::min(1024, (G * B + 255) / 256)), dim3(256), 0, st,
+                     best, (size_t)G * B, 0ull);
+  for (int k = 1; k <= G; ++k) {
+    const unsigned long long* bprev = k > 1 ? best + (size_t)(k - 2) * B : nullptr;
+    unsigned long long* bcur = best + (size_t)(k - 1) * B;
+    float4* pk = part + (size_t)(k - 1) * plan.nslices * B;
+    if (plan.mfma) {
+      MfmaBiasArgs a{};
+      a.mode = kModeDraft;
+      a.U = U; a.W1 = (const uint16_t*)W1; a.W2t = (const uint16_t*)W2t;
+      a.anchor = anchor; a.forced = forced; a.tokens = nullptr; a.best_prev = bprev;
+      a.best_cur = bcur; a.part = pk;
+      a.B = B; a.G = G; a.V = V; a.r = r; a.k = k; a.invT = invT; a.key0 = key0; a.key1 = key1;
+      a.ncols = B;
+      if (launch_mfma_bias(a, plan.nslices, st) != DSPARK_OK) return DSPARK_E_HIP;
+    } else {
+      const size_t sh = sizeof(float) * (r + 256 + 16);
+      dim3 grid(plan.nslices, B);
+      if (wdt == DSPARK_BF16)
+        hipLaunchKernelGGL(k_draft_row<uint16_t>, grid, dim3(256), sh, st, U,
+                           (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced, bprev,
+                           bcur, pk, B, G, V, r, k, invT, key0, key1, plan.slice_len);
+      else
+        hipLaunchKernelGGL(k_draft_row<float>, grid, dim3(256), sh, st, U, (const float*)W1,
+                           (const float*)W2t, anchor, forced, bprev, bcur, pk, B, G, V, r, k,
+                           invT, key0, key1, plan.slice_len);
+    }
+  }
+  hipLaunchKernelGGL(k_draft_final, dim3((B * G + 3) / 4), dim3(256), 0, st, part, best, B, G,
+                     plan.nslices, tokens, logp, lse);
+  return launch_status();
+}

@@ -1,0 +1,67 @@
+// mfma_bias.h -- the batched Markov bias on bf16 matrix cores, fused with the per-element
+// work that consumes it.
+//
+// For a set of columns c (a request b_c at a position k_c with conditioning token
+// prev_c), the bias of every vocab row v is
+//     bias[v][c] = sum_i W2t[v][i] * W1[prev_c][i]          ([XTL §4]: W1 embedding,
+//                                                           W2 bias-free projection)
+// i.e. the product of the streamed W2t [V][r] with the gathered W1 rows, a dense
+// [V x r] x [r x ncols] contraction done with v_mfma_f32_32x32x16_bf16.  The bias never
+// leaves registers: the epilogue of each 32 x 32 output tile reads the matching base
+// logits (and target logits) and does one of
+//   kModeDraft  z = (U + bias)/T; online (max, sum-exp); Gumbel-max race   [CSDN Eq. 4]
+//   kModeResid  rho = max(0, p_t - p_d); Gumbel race on ln rho            (verification)
+//   kModeTV     sum_v min(p_d, p_t)                                      [CSDN Eq. 8]
+//
+// Layout (per workgroup of 4 waves): the gathered W1 rows of all columns sit in LDS
+// (16-byte padded rows, the MFMA B operand); each wave streams its own 32-row W2t tiles
+// straight from HBM into registers (the A operand, prefetched one tile ahead), so W2t is
+// read exactly once per launch.  Output lane l of a tile holds column l%32 and the
+// vocab rows 8g + 4(l/32) + j (g, j < 4): four runs of four consecutive rows, which is
+// exactly one Philox4x32 call per run.
+#pragma once
+
+#include "dspark_dev.h"
+#include "dspark_host.h"
+
+namespace dspark {
+
+enum { kModeDraft = 0, kModeResid = 1, kModeTV = 2 };
+
+struct MfmaBiasArgs {
+  int mode;
+  const float* U;
+  const uint16_t* W1;
+  const uint16_t* W2t;
+  const int32_t* anchor;
+  const int32_t* forced;                 // draft: teacher-forced prefix or NULL
+  const int32_t* tokens;                 // resid/tv: drafted tokens [B][G]
+  const unsigned long long* best_prev;   // draft: packed winners of position k-1
+  unsigned long long* best_cur;          // draft: packed winners of position k
+  float4* part;                          // draft: [slices][B] (m, l, z_win, idx_win)
+  const float* T;                        // resid/tv: target logits [B][G+1][V]
+  const float* lse_d;                    // resid/tv: draft lse [B][G]
+  const float* lse_t_row;                // resid: lse of target row j_b [B]
+  const int32_t* jrow;                   // resid: row j_b (1-based), 0 = no residual
+  unsigned long long* res_best;          // resid: packed residual winner [B]
+  unsigned long long* fb_best;           // resid: packed fallback (p_t) winner [B]
+  const float* lse_t;                    // tv: target lse [B][G]
+  float* tv_part;                        // tv: [slices][B*G] partial sums of min(p_d, p_t)
+  int B, G, V, r, k;
+  float invT;
+  uint32_t key0, key1;
+  int ncols;                             // columns of this launch (<= 256)
+  int col0;                              // first global column of this launch
+};
+
+// The MFMA path handles bf16 weights with r = 256 (16 k-steps of 16).
+inline bool mfma_bias_supported(int ncols, int r, int wdt) {
+  return wdt == DSPARK_BF16 && r == 256 && ncols >= 32;
+}
+
+// Workgroups of one launch over V for `ncols` columns (all resident at once).
+int mfma_grid(int V, int ncols);
+
+dspark_status launch_mfma_bias(const MfmaBiasArgs& a, int nwg, hipStream_t st);
+
+}  // namespace dspark

@@ -1,0 +1,111 @@
+// schedule.hip -- hardware-aware prefix scheduler [XTL §6; CSDN throughput objective
+// Theta = tau * SPS(B); paper Sec. 3.2.2 as quoted in the CSDN roundtable], entirely on
+// the GPU in one workgroup.
+//
+//  1. prefix survival a_{b,j} = prod_{i<=j} c_{b,i}: one thread per request, fp64,
+//     multiplied left to right (the same rounding sequence as the plain definition);
+//  2. all (b, j) candidates sorted by (a descending, b ascending, j ascending) with a
+//     bitonic network in LDS -- the key (a, b*gamma + j - 1) is a total order;
+//  3. the greedy walk in one thread: tau and Theta accumulate in fp64 in sorted order,
+//     stopping at the first candidate that does not raise Theta.
+// Since a_{b,j} is non-increasing in j (c <= 1) and ties go to the lower j, admissions
+// are always prefixes of each request's block.
+#include "dspark_dev.h"
+#include "dspark_host.h"
+
+namespace dspark {
+
+__device__ __forceinline__ bool sched_before(double a1, uint32_t i1, double a2, uint32_t i2) {
+  return a1 > a2 || (a1 == a2 && i1 < i2);
+}
+
+__global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
+                                                   const double* __restrict__ sps, int B,
+                                                   int G, int mode, int np,
+                                                   int32_t* __restrict__ ell,
+                                                   double* __restrict__ theta,
+                                                   int32_t* __restrict__ n_total) {
+#pragma clang fp contract(off)
+  extern __shared__ __align__(16) unsigned char smem[];
+  double* key_a = reinterpret_cast<double*>(smem);               // [np]
+  uint32_t* key_i = reinterpret_cast<uint32_t*>(key_a + np);     // [np]
+  const int tid = threadIdx.x, n = B * G;
+  for (int b = tid; b < B; b += blockDim.x) {
+    double a = 1.0;
+    for (int j = 0; j < G; ++j) {
+      a = a * (double)c[(size_t)b * G + j];
+      key_a[b * G + j] = a;
+      key_i[b * G + j] = (uint32_t)(b * G + j);
+    }
+    ell[b] = 0;
+  }
+  for (int i = n + tid; i < np; i += blockDim.x) {
+    key_a[i] = -1.0;               // padding sorts after every real candidate
+    key_i[i] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  // bitonic sort into "before" order
+  for (int size = 2; size <= np; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int p = tid; p < (np >> 1); p += blockDim.x) {
+        const int lo = 2 * stride * (p / stride) + (p % stride);
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const double al = key_a[lo], ah = key_a[hi];
+        const uint32_t il = key_i[lo], ih = key_i[hi];
+        const bool swap = up ? sched_before(ah, ih, al, il) : sched_before(al, il, ah, ih);
+        if (swap) {
+          key_a[lo] = ah; key_a[hi] = al;
+          key_i[lo] = ih; key_i[hi] = il;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    int N = B;
+    double tau = (double)B;
+    double best = tau * sps[N];
+    for (int t = 0; t < n; ++t) {
+      const double tau_next = tau + key_a[t];
+      const double th = tau_next * sps[N + 1];
+      if (mode == DSPARK_SCHED_GREEDY && th <= best) break;
+      tau = tau_next;
+      N = N + 1;
+      best = th;
+      const uint32_t i = key_i[t];
+      ell[i / G] = (int32_t)(i % G) + 1;
+    }
+    theta[0] = best;
+    n_total[0] = N;
+  }
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, const double* sps,
+                                         int mode, int32_t* ell, double* theta,
+                                         int32_t* n_total, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!c || !sps || !ell || !theta || !n_total) return DSPARK_E_NULL;
+  if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
+  if (mode != DSPARK_SCHED_GREEDY && mode != DSPARK_SCHED_FULL) return DSPARK_E_VALUE;
+  int np = 1;
+  while (np < B * G) np <<= 1;
+  if (np < 2) np = 2;
+  const size_t sh = (size_t)np * (sizeof(double) + sizeof(uint32_t));
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((size_t)kMaxSchedCandidates * 12)) != hipSuccess)
+      return DSPARK_E_HIP;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, (hipStream_t)stream, c, sps, B, G,
+                     mode, np, ell, theta, n_total);
+  return launch_status();
+}

@@ -1,0 +1,204 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) library for one DSpark draft/verify round.
+ *
+ * The round, per batch of B requests (sources cited by short name):
+ *   [XTL]   "[DeepSeek-6] DSpark: From Draft Models to Serving-Aware Speculative
+ *           Decoding" (xutianle.me), sections 1-7.
+ *   [CSDN]  "DSpark: Confidence-Scheduled Speculative Decoding with Semi-Autoregressive
+ *           Generation -- 研读报告" (devpress.csdn.net), key formulas Eq. 4, 7, 8 and the
+ *           throughput objective Theta = tau * SPS(B).
+ *   [AIMSG] "DeepSeek DSpark 深度解读：系统工程与模型协同的极致优化" (aimsg.uk), concepts 2, 8, 9.
+ *
+ *   1. dspark_draft_markov   Markov-head draft: gamma sequential softmax + sampling steps
+ *                            over base logits plus a rank-r transition bias  [CSDN Eq. 4; XTL §3-4]
+ *   2. dspark_confidence     c_k = sigmoid(w . [h_k ; W1[x_{k-1}]])          [CSDN Eq. 7; XTL §5]
+ *   3. dspark_schedule       greedy prefix scheduler maximising tau * SPS(N)  [XTL §6; CSDN]
+ *   4. dspark_verify         lossless rejection-sampling verification         [XTL §1; AIMSG 2]
+ *   5. dspark_accept_rate_tv analytic accept rate 1 - |p_d - p_t|_1 / 2       [CSDN Eq. 8; XTL §5]
+ *
+ * Conventions shared by every call:
+ *   - Tensor arguments are DEVICE pointers to row-major contiguous arrays owned by the
+ *     caller.  The library never allocates or frees memory and never reads device memory
+ *     on the host.  Scratch memory is the caller's `ws` buffer of at least
+ *     dspark_workspace_bytes(op, dims) bytes; its contents are undefined afterwards.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     return without synchronising.  Arguments are validated on the host first: on any
+ *     error a non-zero dspark_status is returned and nothing is enqueued.  Faults inside
+ *     kernels surface at the caller's next synchronisation, as usual in HIP.
+ *   - Token ids are int32 in [0, V); ids out of range are the caller's error and are not
+ *     checked on the device.  Inputs containing NaN give unspecified (but finite-time)
+ *     results.
+ *   - Identical inputs give bit-identical outputs (all cross-workgroup reductions have a
+ *     fixed order or are order-free).  The calls keep no state between invocations and
+ *     may run concurrently on different streams with different workspaces.
+ *   - Randomness: u(seed, b, k, s, v) = (2 * (W >> 9) + 1) * 2^-24 where W is word
+ *     (v mod 4) of Philox4x32-10 (Salmon et al., SC'11) applied to counter
+ *     (v div 4, k, b, s) with key (seed mod 2^32, seed div 2^32).  b is the request row,
+ *     k the 1-based position, s the stream: 0 draft sample, 1 accept test (v = 0),
+ *     2 residual/bonus sample.  Gumbel noise is G = -ln(-ln u).
+ *
+ * Shapes: B = batch, gamma = draft length, V = vocabulary, r = Markov rank, d = hidden.
+ * Limits: 1 <= B <= 65535, 1 <= gamma <= 64, 2 <= V <= 2^28, r a multiple of 8 with
+ * 8 <= r <= 1024, 0 <= d <= 65536; dspark_schedule also needs B * gamma <= 4096.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSPARK_OK = 0,
+    DSPARK_E_NULL = 1,        /* a required pointer is NULL                               */
+    DSPARK_E_SHAPE = 2,       /* a dimension is out of the supported range                */
+    DSPARK_E_DTYPE = 3,       /* unknown dtype code                                       */
+    DSPARK_E_VALUE = 4,       /* temperature <= 0 or not finite, unknown scheduler mode   */
+    DSPARK_E_WORKSPACE = 5,   /* ws is NULL or ws_bytes < dspark_workspace_bytes(...)     */
+    DSPARK_E_HIP = 6          /* the HIP runtime refused a launch                         */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+typedef enum { DSPARK_SCHED_GREEDY = 0, DSPARK_SCHED_FULL = 1 } dspark_sched_mode;
+
+typedef enum {
+    DSPARK_OP_DRAFT = 0, DSPARK_OP_CONFIDENCE = 1, DSPARK_OP_SCHEDULE = 2,
+    DSPARK_OP_VERIFY = 3, DSPARK_OP_TV = 4
+} dspark_op;
+
+typedef struct {
+    int32_t batch;   /* B */
+    int32_t gamma;   /* draft length */
+    int32_t vocab;   /* V */
+    int32_t rank;    /* r */
+    int32_t hidden;  /* d (only dspark_confidence reads it) */
+} dspark_dims;
+
+/* Scratch bytes the call `op` needs for `dims` (0 when it needs none).  Returns 0 for an
+ * unknown op or invalid dims (the call itself then reports the error). */
+size_t dspark_workspace_bytes(int op, const dspark_dims* dims);
+
+/* Human-readable name of a status code (static storage). */
+const char* dspark_status_string(int status);
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int dspark_version(void);
+
+/*
+ * Markov-head draft [CSDN Eq. 4; XTL §3 "Semi-Autoregressive", §4 "Markov Head"].
+ * For k = 1..gamma (sequentially) and every request b:
+ *   prev_b = x_{b,k-1}, with x_{b,0} = anchor[b] (the anchor is the first predicted
+ *            position, [XTL §3]), or forced[b][k-2] when `forced` is not NULL;
+ *   z_v    = (U[b][k-1][v] + sum_i W1[prev_b][i] * W2t[v][i]) / temperature;
+ *   lse    = log sum_v exp(z_v);
+ *   x_{b,k}= argmax_v (z_v + G(seed, b, k, 0, v)) -- a draw from p = softmax(z)
+ *            (Gumbel-max; the lowest v wins exact ties);
+ *   logp   = z_{x_{b,k}} - lse.
+ * Arguments:
+ *   U        [B][gamma][V] fp32 base logits of the parallel backbone.
+ *   W1       [V][r] Markov embedding (`wdt`: F32 or BF16).
+ *   W2t      [V][r] = W2 transposed, W2 being the [r][V] bias-free projection (same dtype).
+ *   anchor   [B] int32 anchor tokens.
+ *   forced   [B][gamma] int32 or NULL: teacher forcing -- position k conditions on
+ *            forced[b][k-2] instead of the token drawn at k-1 (scores a given block; the
+ *            call still draws and outputs its own tokens).
+ *   tokens   out [B][gamma] int32 drawn tokens x_{b,1..gamma}.
+ *   logp     out [B][gamma] fp32 log p_d(x_{b,k}).
+ *   lse      out [B][gamma] fp32 log-partition of z at each position.
+ */
+dspark_status dspark_draft_markov(const dspark_dims* dims, const float* U, const void* W1,
+                                  const void* W2t, int wdt, const int32_t* anchor,
+                                  const int32_t* forced, float temperature, uint64_t seed,
+                                  int32_t* tokens, float* logp, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * Confidence head [CSDN Eq. 7; XTL §5 "Confidence Head"]:
+ *   c[b][k-1] = 1 / (1 + exp(-(sum_j w[j] h[b][k-1][j] + sum_i w[d+i] W1[x_{b,k-1}][i])))
+ * with x_{b,0} = anchor[b] and x_{b,k-1} = tokens[b][k-2]; no bias term.
+ *   h [B][gamma][d] (`hdt`), W1 [V][r] (`wdt`), w [d + r] (`wvdt`, order [h ; W1-row]),
+ *   tokens [B][gamma] int32, c out [B][gamma] fp32.  Needs no workspace.
+ */
+dspark_status dspark_confidence(const dspark_dims* dims, const void* h, int hdt,
+                                const void* W1, int wdt, const void* w, int wvdt,
+                                const int32_t* anchor, const int32_t* tokens, float* c,
+                                void* stream);
+
+/*
+ * Hardware-aware prefix scheduler [XTL §6; CSDN throughput objective and the quotes of
+ * paper Sec. 3.2.2 in its roundtable], run entirely on the GPU.
+ *   a_{b,j} = prod_{i<=j} c_{b,i}   (fp64, multiplied left to right from 1)
+ *   N       = sum_b (ell_b + 1)     (the +1 is the target's bonus/corrected slot)
+ *   tau     = sum_b (1 + sum_{j<=ell_b} a_{b,j})
+ *   Theta   = tau * sps[N]
+ * GREEDY: candidates (b, j) ordered by a descending, then b ascending, then j ascending,
+ * are admitted one at a time from ell = 0 (tau = B, N = B), tau and Theta updated in fp64
+ * in that order; the walk stops at the first candidate whose Theta <= the best Theta so
+ * far.  FULL: every candidate is admitted (ell_b = gamma).
+ *   c      [B][gamma] fp32 confidences in [0, 1].
+ *   sps    [B*(gamma+1)+1] fp64 target steps per second at N verify tokens.
+ *   ell    out [B] int32 verify lengths in 0..gamma.
+ *   theta  out [1] fp64 final Theta; n_total out [1] int32 final N.
+ * Needs no workspace (pass NULL, 0); B * gamma <= 4096.
+ */
+dspark_status dspark_schedule(int32_t batch, int32_t gamma, const float* c, const double* sps,
+                              int mode, int32_t* ell, double* theta, int32_t* n_total,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification [XTL §1; AIMSG concept 2; accept probability
+ * min(1, p_t/p_d) as quoted in the CSDN roundtable].  For every request b, with
+ * p_t,k = softmax(T[b][k-1] / temperature) and p_d,k the draft distribution:
+ *   for k = 1..ell_b: accept x_k iff u(seed, b, k, 1, 0) * p_d,k(x_k) < p_t,k(x_k),
+ *                     with p_d,k(x_k) = exp(logp[b][k-1]); stop at the first rejection;
+ *   n_b = number of leading accepts;
+ *   if n_b < ell_b:   j = n_b + 1, y = argmax_{v: rho_v > 0} (ln rho_v + G(seed,b,j,2,v))
+ *                     where rho = max(0, p_t,j - p_d,j) (the normalised residual; p_d,j is
+ *                     recomputed from U, W1, W2t with lse[b][j-1]); if rounding leaves
+ *                     every rho_v = 0, y is drawn from p_t,j with the same noise;
+ *   else:             y = argmax_v (T[b][ell_b][v] / temperature + G(seed, b, ell_b+1, 2, v)),
+ *                     the bonus token drawn from p_t at position ell_b + 1.
+ * Arguments:
+ *   U, W1, W2t, wdt, anchor, tokens as for the draft; logp, lse: the draft's outputs.
+ *   T          [B][gamma+1][V] fp32 target logits (row k-1 is position k).
+ *   ell        [B] int32 verify lengths (e.g. from dspark_schedule).
+ *   n_accept   out [B] int32.
+ *   out_tokens out [B][gamma+1] int32: x_1..x_{n_b}, y, then -1.
+ *   pt_tok     out [B][gamma] fp32 p_t,k(x_k) for k <= ell_b (NaN elsewhere), or NULL.
+ */
+dspark_status dspark_verify(const dspark_dims* dims, const float* U, const void* W1,
+                            const void* W2t, int wdt, const int32_t* anchor,
+                            const int32_t* tokens, const float* logp, const float* lse,
+                            const float* T, const int32_t* ell, float temperature,
+                            uint64_t seed, int32_t* n_accept, int32_t* out_tokens,
+                            float* pt_tok, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Analytic accept rate [CSDN Eq. 8; XTL §5: 1 - |p_d - p_t|_1 / 2, computed on the
+ * softmaxed draft and target logits]:
+ *   alpha[b][k-1] = sum_v min(p_d,k(v), p_t,k(v)),   k = 1..gamma,
+ * with the tempered draft distribution of position k given tokens (p_d,k = exp(z - lse),
+ * lse from the draft) and p_t,k = softmax(T[b][k-1] / temperature).
+ */
+dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, const void* W1,
+                                    const void* W2t, int wdt, const int32_t* anchor,
+                                    const int32_t* tokens, const float* lse, const float* T,
+                                    float temperature, float* alpha, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/*
+ * The uniforms of the random-number definition above, for checking the generator:
+ *   out[i] = u(seed, b, k, s, v0 + i), i < n   (fp32; every value is exact in fp32).
+ */
+dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t k, uint32_t s,
+                                  uint32_t v0, int64_t n, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,103 @@
+"""The C ABI: the library loads, exports every declared symbol, and rejects bad arguments
+on the host (status codes, nothing launched).  Runs without a GPU: every call here fails
+validation before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verify_sampling_step_amd as ds
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dspark.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"dspark_draft_markov", "dspark_confidence", "dspark_schedule", "dspark_verify",
+            "dspark_accept_rate_tv", "dspark_workspace_bytes"} <= set(names)
+    L = ds.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = ds.lib()
+    for s in range(7):
+        assert L.dspark_status_string(s).startswith(b"DSPARK_")
+    assert L.dspark_version() >= 100
+
+
+def _dims(B=4, G=4, V=1024, r=16, d=64):
+    return ds.Dims(B, G, V, r, d)
+
+
+P = ctypes.c_void_p(256)   # a non-null pointer; never dereferenced on these error paths
+
+
+def _draft(dm, temp=1.0, wdt=0, ws=P, ws_bytes=1 << 30, U=P):
+    return ds.lib().dspark_draft_markov(ctypes.byref(dm) if dm is not None else None, U, P, P,
+                                        wdt, P, None, temp, 1, P, P, P, ws, ws_bytes, None)
+
+
+def test_draft_argument_validation():
+    assert _draft(None) == 1
+    assert _draft(_dims(), U=None) == 1
+    for bad in (_dims(B=0), _dims(G=0), _dims(G=65), _dims(V=1), _dims(r=12), _dims(r=0),
+                _dims(V=(1 << 28) + 1), _dims(B=70000)):
+        assert _draft(bad) == 2
+    assert _draft(_dims(), wdt=7) == 3
+    for t in (0.0, -1.0, float("inf"), float("nan")):
+        assert _draft(_dims(), temp=t) == 4
+    assert _draft(_dims(), ws=None) == 5
+    assert _draft(_dims(), ws_bytes=16) == 5
+
+
+def test_schedule_argument_validation():
+    L = ds.lib()
+    assert L.dspark_schedule(4, 4, None, P, 0, P, P, P, None, 0, None) == 1
+    assert L.dspark_schedule(0, 4, P, P, 0, P, P, P, None, 0, None) == 2
+    assert L.dspark_schedule(4097, 1, P, P, 0, P, P, P, None, 0, None) == 2
+    assert L.dspark_schedule(4, 4, P, P, 2, P, P, P, None, 0, None) == 4
+
+
+def test_verify_confidence_tv_validation():
+    L = ds.lib()
+    dm = _dims()
+    assert L.dspark_verify(ctypes.byref(dm), P, P, P, 0, P, P, P, P, None, P, 1.0, 1, P, P,
+                           None, P, 1 << 30, None) == 1
+    assert L.dspark_verify(ctypes.byref(dm), P, P, P, 0, P, P, P, P, P, P, 0.0, 1, P, P, None,
+                           P, 1 << 30, None) == 4
+    assert L.dspark_verify(ctypes.byref(dm), P, P, P, 0, P, P, P, P, P, P, 1.0, 1, P, P, None,
+                           P, 8, None) == 5
+    assert L.dspark_confidence(ctypes.byref(dm), P, 0, P, 0, P, 3, P, P, P, None) == 3
+    assert L.dspark_confidence(ctypes.byref(dm), None, 0, P, 0, P, 0, P, P, P, None) == 1
+    assert L.dspark_accept_rate_tv(ctypes.byref(dm), P, P, P, 0, P, P, P, P, -2.0, P, P,
+                                   1 << 30, None) == 4
+    assert L.dspark_rng_uniforms(1, 0, 1, 0, 0, -5, P, None) == 2
+
+
+def test_workspace_sizes_are_consistent():
+    L = ds.lib()
+    for (B, G, V, r) in [(4, 4, 1024, 16), (1, 16, 151936, 256), (128, 16, 151936, 256),
+                         (256, 5, 129280, 256), (64, 16, 262144, 256)]:
+        for op in (ds.OP_DRAFT, ds.OP_VERIFY, ds.OP_TV):
+            n = ds.workspace_bytes(op, B, G, V, r)
+            assert n > 0 and n % 256 == 0
+        assert ds.workspace_bytes(ds.OP_SCHEDULE, B, G, V, r) == 0
+        assert ds.workspace_bytes(ds.OP_CONFIDENCE, B, G, V, r) == 0
+    assert ds.workspace_bytes(0, 0, 4, 1024, 16) == 0        # invalid dims -> 0
+    assert ds.workspace_bytes(9, 4, 4, 1024, 16) == 0        # unknown op -> 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(ds, "_lib", None)
+    monkeypatch.setattr(ds, "LIB_PATH", "/nonexistent/libdspark.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        ds.lib()

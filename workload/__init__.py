@@ -46,6 +46,7 @@ class Config:
     sigma_mix: bool         # per-request sigma scale from {0.2, 0.5, 1.0}
     table: str              # "tiny" | "serve" | "serve15"
     tv: bool                # analytic accept rate on every position
+    wsigma: float = 0.0     # weight s.d. (0: 0.02 for bf16 weights, 0.1 for fp32)
 
 
 CONFIGS = {
@@ -65,10 +66,10 @@ CONFIG_ORDER = ["tiny", "qwen1", "serve128", "v4dspark5", "bigvocab"]
 
 def custom(name="custom", B=4, gamma=4, V=1024, r=16, d=64, bf16=False, temperature=1.0,
            sched_mode=0, logits="gauss2", sigma0=0.5, sigma1=0.1, sigma_mix=False,
-           table="tiny", tv=True) -> Config:
+           table="tiny", tv=True, wsigma=0.0) -> Config:
     """A configuration of arbitrary shape with the distributions of a named family."""
     return Config(name, 99, B, gamma, V, r, d, bf16, temperature, sched_mode, logits, sigma0,
-                  sigma1, sigma_mix, table, tv)
+                  sigma1, sigma_mix, table, tv, wsigma)
 
 
 def step_time_ms(table: str, N: np.ndarray) -> np.ndarray:
@@ -179,7 +180,7 @@ class RoundInputs:
 def generate(cfg: Config, seed: int = 0) -> RoundInputs:
     """Draw every input of one round of `cfg` from `seed`."""
     B, G, V, r, d = cfg.B, cfg.gamma, cfg.V, cfg.r, cfg.d
-    wsig = 0.02 if cfg.bf16 else 0.1
+    wsig = cfg.wsigma if cfg.wsigma > 0 else (0.02 if cfg.bf16 else 0.1)
     rng_w = _rng(seed, cfg, 1)
     W1 = _normal(rng_w, (V, r), wsig)
     W2t = _normal(rng_w, (V, r), wsig)
