@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of one DSpark draft/verify round on one MI355X.
+
+A step is one pass of the whole hot path over one batch: Markov-head draft (gamma positions)
+-> confidence head -> greedy prefix scheduler -> rejection-sampling verification (+ the TV
+accept rate for workloads that ask for it).  Inputs are resident in HBM before timing; the
+target logits (the stand-in for the target model's forward) are synthesised once, untimed,
+from the round's drafted tokens -- every step re-drafts the identical tokens (same seed).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serve128]
+
+Prints one JSON line.  `value` = drafted+verified positions per second = B * gamma / step.
+`roofline` covers the draft (the dominant kernel sequence): algorithmic bytes per call
+(W2t and the base-logit rows, once per position) over the call's average duration,
+measured with HIP events on the launch stream inside the timed region.
+`cpu_baseline` times the fp64 oracle on a bounded sample of requests on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+METRIC = "draft+verify positions/s at B=128,gamma=16,V=151936; % of HBM peak BW"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="serve128")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the round is "
+              "sharded by request across GPUs by design, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import draft_verify_sampling_step_amd as ds
+    import workload
+
+    ds.lib()   # fail loudly before any work if the library is missing
+    cfg = workload.CONFIGS[args.workload]
+    B, G, V, r, d = cfg.B, cfg.gamma, cfg.V, cfg.r, cfg.d
+    temp = cfg.temperature
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    log(f"generating {cfg.name} inputs")
+    inp = workload.generate(cfg, args.seed)
+    U = ds.to_device(inp.U)
+    W1 = ds.to_device(inp.W1)
+    W2t = ds.to_device(inp.W2t)
+    h = ds.to_device(inp.h)
+    w = ds.to_device(inp.w)
+    anchor = ds.to_device(inp.anchor)
+    sps = ds.to_device(inp.sps)
+    stream = torch.cuda.current_stream()
+
+    # outputs and workspaces allocated once
+    tokens = torch.empty((B, G), dtype=torch.int32, device=dev)
+    logp = torch.empty((B, G), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, G), dtype=torch.float32, device=dev)
+    conf = torch.empty((B, G), dtype=torch.float32, device=dev)
+    ell = torch.empty(B, dtype=torch.int32, device=dev)
+    theta = torch.empty(1, dtype=torch.float64, device=dev)
+    ntot = torch.empty(1, dtype=torch.int32, device=dev)
+    nacc = torch.empty(B, dtype=torch.int32, device=dev)
+    outtok = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    alpha = torch.empty((B, G), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(ds.workspace_bytes(ds.OP_DRAFT, B, G, V, r), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(ds.workspace_bytes(ds.OP_VERIFY, B, G, V, r), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(max(256, ds.workspace_bytes(ds.OP_TV, B, G, V, r)), dtype=torch.uint8,
+                       device=dev)
+
+    # untimed: draft once, synthesise the target logits for those tokens
+    ds.dspark_draft_markov(U, W1, W2t, anchor, temp, inp.seed, out=(tokens, logp, lse), ws=ws_d)
+    torch.cuda.synchronize()
+    log("synthesising target logits")
+    T = ds.to_device(workload.synthesize_target(inp, tokens.cpu().numpy()))
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    ev_d0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_d1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev_d0[i].record(stream)
+        ds.dspark_draft_markov(U, W1, W2t, anchor, temp, inp.seed, out=(tokens, logp, lse),
+                               ws=ws_d)
+        if i is not None:
+            ev_d1[i].record(stream)
+        ds.dspark_confidence(h, W1, w, anchor, tokens, out=conf)
+        ds.dspark_schedule(conf, sps, cfg.sched_mode, out=(ell, theta, ntot))
+        ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, inp.seed,
+                         out=(nacc, outtok, None), ws=ws_v)
+        if cfg.tv:
+            ds.dspark_accept_rate_tv(U, W1, W2t, anchor, tokens, lse, T, temp, out=alpha,
+                                     ws=ws_t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    draft_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_d0, ev_d1)]))
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
+        f"draft {draft_ms:.3f} ms")
+
+    # algorithmic bytes (what the method must move), from this round's realised ell, n
+    ell_h = ell.cpu().numpy().astype(np.int64)
+    n_h = nacc.cpu().numpy().astype(np.int64)
+    w2t_bytes = V * r * 2
+    draft_bytes = G * (w2t_bytes + B * V * 4)
+    conf_bytes = B * G * (d + r) * 2
+    n_rej = int((n_h < ell_h).sum())
+    verify_bytes = int((ell_h + 1).sum()) * V * 4 + (w2t_bytes + n_rej * 2 * V * 4 if n_rej else 0)
+    tv_bytes = (G * w2t_bytes + 3 * B * G * V * 4) if cfg.tv else 0
+    step_bytes = draft_bytes + conf_bytes + verify_bytes + tv_bytes
+    positions = B * G
+    value = positions / (ms_step * 1e-3)
+    achieved = draft_bytes / (draft_ms * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={B} gamma={G} V={V} r={r} d={d} bf16 weights, fp32 "
+                        f"logits, temperature {temp}, "
+                        f"{'greedy scheduler' if cfg.sched_mode == 0 else 'full-block verify'}",
+            "global_batch": B, "gamma": G, "vocab": V, "rank": r, "hidden": d,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "draft: gamma launches of the fused MFMA bias + softmax + Gumbel kernel "
+                      "(+ init and merge), per dspark_draft_markov call",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": draft_bytes,
+            "ms_per_launch": round(draft_ms, 4),
+        },
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_bytes": step_bytes,
+        "accepted_mean": round(float(n_h.mean()), 3),
+        "verify_tokens": int((ell_h + 1).sum()),
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle, single-threaded, on the first S requests of the same workload
+    (full vocabulary, all positions): draft, confidence, schedule over those S, verify.
+    Target logits for the sample are synthesised from the oracle's own tokens, untimed."""
+    import oracle
+    import workload
+
+    cfg = inp.cfg
+    G = cfg.gamma
+    temp = cfg.temperature
+
+    def run(rows):
+        t_draft = time.perf_counter()
+        od = oracle.draft(inp.U[rows], inp.W1, inp.W2t, inp.anchor[rows], temp, inp.seed,
+                          gid=rows)
+        c = oracle.confidence(inp.h[rows], inp.W1, inp.w, inp.anchor[rows], od["tokens"])
+        sps = 1000.0 / workload.step_time_ms(cfg.table, np.arange(len(rows) * (G + 1) + 1))
+        ell, _, _ = oracle.schedule(c.astype(np.float32), sps, cfg.sched_mode)
+        t_mid = time.perf_counter()
+        T = workload.synthesize_target(inp, _tokens_full(cfg, rows, od["tokens"]), rows=rows)
+        t_ver = time.perf_counter()
+        oracle.verify(inp.U[rows], inp.W1, inp.W2t, inp.anchor[rows], od["tokens"], T, ell,
+                      temp, inp.seed, gid=rows)
+        if cfg.tv:
+            oracle.accept_tv(inp.U[rows], inp.W1, inp.W2t, inp.anchor[rows], od["tokens"], T,
+                             temp)
+        t_end = time.perf_counter()
+        return (t_mid - t_draft) + (t_end - t_ver)
+
+    t1 = run(np.array([0]))
+    S = int(max(1, min(cfg.B, budget_s // max(t1, 1e-3))))
+    rows = np.arange(S)
+    secs = run(rows) if S > 1 else t1
+    return {
+        "value": round(S * G / secs, 3),
+        "unit": "positions/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"requests 0..{S - 1} of {cfg.name} (all {G} positions, full V={cfg.V}): "
+                  f"draft+confidence+schedule+verify{'+TV' if cfg.tv else ''} in fp64, "
+                  f"{secs:.1f} s on 1 thread",
+    }
+
+
+def _tokens_full(cfg, rows, toks):
+    full = np.zeros((cfg.B, cfg.gamma), np.int32)
+    full[rows] = toks
+    return full
+
+
+if __name__ == "__main__":
+    main()
