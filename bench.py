@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "reference for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -57,6 +60,16 @@ def main():
     import torch
     import draft_verify_sampling_step_amd as ds
     import workload
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
 
     ds.lib()   # fail loudly before any work if the library is missing
     cfg = workload.CONFIGS[args.workload]

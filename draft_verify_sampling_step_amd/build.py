@@ -16,13 +16,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 ARCH = os.environ.get("DSPARK_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are kept off (see the build notes of the design document)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
 ]
 
 

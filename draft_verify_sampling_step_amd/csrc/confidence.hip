@@ -49,11 +49,11 @@ __global__ __launch_bounds__(256) void k_confidence(const TH* __restrict__ h,
                                                     const int32_t* __restrict__ anchor,
                                                     const int32_t* __restrict__ tokens,
                                                     float* __restrict__ c, int B, int G, int d,
-                                                    int r) {
+                                                    int r, int V) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wid >= B * G) return;
   const int b = wid / G, k = wid % G + 1;
-  const int prev = (k == 1) ? anchor[b] : tokens[(size_t)b * G + (k - 2)];
+  const int prev = clamp_tok((k == 1) ? anchor[b] : tokens[(size_t)b * G + (k - 2)], V);
   float acc = lane_dot<TWV, TH>(w, h + (size_t)wid * d, d, lane);
   acc += lane_dot<TWV, TW1>(w + d, W1 + (size_t)prev * r, r, lane);
   acc = wave_sum(acc);
@@ -67,7 +67,7 @@ static void launch_conf(const dspark_dims* dm, const void* h, const void* W1, co
   const int n = dm->batch * dm->gamma;
   hipLaunchKernelGGL((k_confidence<TH, TW1, TWV>), dim3((n + 3) / 4), dim3(256), 0, st,
                      (const TH*)h, (const TW1*)W1, (const TWV*)w, anchor, tokens, c,
-                     dm->batch, dm->gamma, dm->hidden, dm->rank);
+                     dm->batch, dm->gamma, dm->hidden, dm->rank, dm->vocab);
 }
 
 }  // namespace dspark

@@ -2,13 +2,16 @@
 // each a rank-r bias added to the backbone logits, a full-vocabulary softmax and a
 // Gumbel-max draw.
 //
-// One kernel launch per position: the launch boundary is the device-wide dependency
+// One launch per position; the launch boundary carries the device-wide dependency
 // x_{k-1} -> bias of position k (on MI355X a kernel boundary is several times cheaper
-// than an in-kernel grid barrier).  Each workgroup covers a vocabulary slice and reports
-//   - a packed (score, index) candidate through a 64-bit atomic max (order-free), and
-//   - its partial softmax state (m, l) plus its local winner's logit, to a fixed slot.
-// The next position decodes x_{k-1} from the atomic word; a final kernel merges the
-// partial states in slice order into lse and log p_d(x_k).
+// than an in-kernel grid barrier).  Each workgroup covers a vocabulary slice for every
+// request and reports
+//   - its best Gumbel candidate as a packed (score, index) word through a 64-bit atomic
+//     max per request (order-free, so the winner is deterministic), and
+//   - its base-2 softmax state (max, sum) to a fixed slot.
+// The next position decodes x_{k-1} from the atomic word.  After the last position one
+// merge kernel reduces the slots in slice order into lse and log p_d(x_k) (the winner's
+// logit is recomputed from U, W1 and W2t).
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_bias.h"
@@ -22,21 +25,24 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n, unsigned long long v
     p[i] = v;
 }
 
+// Token that position k conditions on: the anchor, the forced prefix, or the winner of
+// position k-1 decoded from its packed atomic word.
 __device__ __forceinline__ int draft_prev(const int32_t* anchor, const int32_t* forced,
                                           const unsigned long long* best_prev, int b, int G,
-                                          int k) {
-  if (k == 1) return anchor[b];
-  if (forced) return forced[(size_t)b * G + (k - 2)];
-  return (int)packed_index(best_prev[b]);
+                                          int k, int V) {
+  if (k == 1) return clamp_tok(anchor[b], V);
+  if (forced) return clamp_tok(forced[(size_t)b * G + (k - 2)], V);
+  return clamp_tok((int)packed_index(best_prev[b]), V);
 }
 
 // Row path: grid (slices, B), 256 threads.  Thread t of a tile owns vocab row tile0 + t.
+// Base-2 logits z2 = z log2 e; the partial is (max z2, sum 2^(z2 - max)).
 template <typename WT>
 __global__ __launch_bounds__(256) void k_draft_row(
     const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ forced,
     const unsigned long long* __restrict__ best_prev, unsigned long long* __restrict__ best_cur,
-    float4* __restrict__ part, int B, int G, int V, int r, int k, float invT, uint32_t key0,
+    float2* __restrict__ part, int B, int G, int V, int r, int k, float invT, uint32_t key0,
     uint32_t key1, int slice_len) {
   extern __shared__ float smem[];
   float* w1s = smem;            // [r]
@@ -45,67 +51,102 @@ __global__ __launch_bounds__(256) void k_draft_row(
   const int b = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
   const int v_begin = s * slice_len;
   const int v_end = min(V, v_begin + slice_len);
-  const int prev = draft_prev(anchor, forced, best_prev, b, G, k);
+  const int prev = draft_prev(anchor, forced, best_prev, b, G, k, V);
+  const float s2 = invT * 1.4426950408889634f;
   load_w1_row<WT>(W1, prev, r, w1s);
   __syncthreads();
   const float* Urow = U + ((size_t)b * G + (k - 1)) * V;
-  ML st{-INFINITY, 0.f};
+  float m = -3.0e38f, l = 0.f;
   Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
   for (int tile0 = v_begin; tile0 < v_end; tile0 += kRowTile) {
     row_bias_tile<WT>(W2t, w1s, bias_s, r, tile0, v_end);
     __syncthreads();
     const int v = tile0 + tid;
     if (v < v_end) {
-      const float z = (Urow[v] + bias_s[tid]) * invT;
+      const float z = (Urow[v] + bias_s[tid]) * s2;
       const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 0u, key0, key1);
       const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-      const float score = z + gumbel_from_uniform(word_to_uniform(word));
-      if (z > st.m) {
-        st.l = st.l * fast_exp(st.m - z) + 1.f;
-        st.m = z;
-      } else {
-        st.l += fast_exp(z - st.m);
-      }
-      if (score > best.s) best = Cand{score, (uint32_t)v, z};
+      const float score =
+          z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
+      const float mn = fmaxf(m, z);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
+      m = mn;
+      if (score > best.s) best = Cand{score, (uint32_t)v, 0.f};
     }
     __syncthreads();
   }
-  st = block_ml(st, red, red + 4);
+  // workgroup merge of the base-2 state, then of the candidates
+  {
+    const int wv = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+      const float mn = fmaxf(m, om);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+      m = mn;
+    }
+    if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
+    __syncthreads();
+    m = red[0];
+    l = red[4];
+    for (int i = 1; i < 4; ++i) {
+      const float mn = fmaxf(m, red[i]);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + red[4 + i] * __builtin_amdgcn_exp2f(red[i] - mn);
+      m = mn;
+    }
+    __syncthreads();
+  }
   best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
   if (tid == 0) {
-    part[(size_t)s * B + b] = make_float4(st.m, st.l, best.z, __uint_as_float(best.i));
-    atomic_max_u64(&best_cur[b], pack_score(best.s, best.i));
+    part[(size_t)s * B + b] = make_float2(m, l);
+    if (best.i != 0xFFFFFFFFu) atomic_max_u64(&best_cur[b], pack_score(best.s, best.i));
   }
 }
 
-// Final merge: one wave per (b, k).  part is [gamma][slices][B].
+// Final merge: one wave per (request, position).  part is [gamma][slices][B] base-2
+// states merged in slice order; the winner's logit z_x = (U[x] + W1[prev] . W2t[x]) / T
+// is recomputed here (one dot of length r).
+template <typename WT>
 __global__ __launch_bounds__(256) void k_draft_final(
-    const float4* __restrict__ part, const unsigned long long* __restrict__ best, int B, int G,
-    int nslices, int32_t* __restrict__ tokens, float* __restrict__ logp,
+    const float2* __restrict__ part, const unsigned long long* __restrict__ best,
+    const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ forced, int B, int G, int V,
+    int r, float invT, int nslices, int32_t* __restrict__ tokens, float* __restrict__ logp,
     float* __restrict__ lse) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wid >= B * G) return;
   const int b = wid % B, kk = wid / B;
   const uint32_t idx = packed_index(best[(size_t)kk * B + b]);
-  ML st{-INFINITY, 0.f};
-  float zx = 0.f;
-  int found = 0;
+  float m = -3.0e38f, l = 0.f;
   for (int s = lane; s < nslices; s += kWave) {
-    const float4 p = part[((size_t)kk * nslices + s) * B + b];
-    st = ml_merge(st, ML{p.x, p.y});
-    if (__float_as_uint(p.w) == idx) { zx = p.z; found = 1; }
+    const float2 p = part[((size_t)kk * nslices + s) * B + b];
+    const float mn = fmaxf(m, p.x);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + p.y * __builtin_amdgcn_exp2f(p.x - mn);
+    m = mn;
   }
-  st = wave_ml(st);
-  // exactly one slice holds the winner
-  const unsigned long long m = __ballot(found);
-  const int src = m ? __ffsll((long long)m) - 1 : 0;
-  zx = __shfl(zx, src, kWave);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+    const float mn = fmaxf(m, om);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+    m = mn;
+  }
+  const int prev = draft_prev(anchor, forced, kk > 0 ? best + (size_t)(kk - 1) * B : nullptr,
+                              b, G, kk + 1, V);
+  const bool won = idx < (uint32_t)V;   // false only if no candidate had a finite score
+  const int x = won ? (int)idx : 0;
+  float dot = 0.f;
+  for (int i = lane; i < r; i += kWave)
+    dot = fmaf(Elem<WT>::get(W1, (size_t)prev * r + i), Elem<WT>::get(W2t, (size_t)x * r + i),
+               dot);
+  dot = wave_sum(dot);
   if (lane == 0) {
-    const float l = st.m + fast_log(st.l);
+    const float lz = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+    const float zx = (U[((size_t)b * G + kk) * V + x] + dot) * invT;
     const size_t o = (size_t)b * G + kk;
-    tokens[o] = (int32_t)idx;
-    lse[o] = l;
-    logp[o] = zx - l;
+    tokens[o] = won ? (int32_t)idx : -1;
+    lse[o] = lz;
+    logp[o] = won ? zx - lz : __builtin_nanf("");
   }
 }
 
@@ -117,7 +158,7 @@ namespace {
 
 struct DraftPlan {
   bool mfma;
-  int nslices;     // partial-state slots per (position, request)
+  int nslices;     // partial slots per (position, request)
   int slice_len;   // row path only
 };
 
@@ -125,7 +166,7 @@ DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   DraftPlan p{};
   p.mfma = mfma_bias_supported(d->batch, d->rank, wdt);
   if (p.mfma) {
-    p.nslices = mfma_grid(d->vocab, d->batch);
+    p.nslices = mfma_grid(d->vocab, d->batch, kModeDraft);
     p.slice_len = 0;
   } else {
     RowSlices s = row_slices(d->vocab, d->batch);
@@ -135,11 +176,11 @@ DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   return p;
 }
 
-size_t draft_ws(const dspark_dims* d, int nslices, unsigned long long** best, float4** part,
+size_t draft_ws(const dspark_dims* d, int nslices, unsigned long long** best, float2** part,
                 void* base) {
   Carve c(base);
   *best = c.take<unsigned long long>((size_t)d->gamma * d->batch);
-  *part = c.take<float4>((size_t)d->gamma * nslices * d->batch);
+  *part = c.take<float2>((size_t)d->gamma * nslices * d->batch);
   return align_up(c.off, 256);
 }
 
@@ -147,7 +188,7 @@ size_t draft_ws(const dspark_dims* d, int nslices, unsigned long long** best, fl
 
 size_t dspark_draft_workspace(const dspark_dims* d) {
   unsigned long long* b;
-  float4* p;
+  float2* p;
   const int ns = std::max(row_slices(d->vocab, d->batch).count, mfma_workgroups(d->vocab));
   return draft_ws(d, ns, &b, &p, nullptr);
 }
@@ -168,7 +209,7 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
   const int B = dm->batch, G = dm->gamma, V = dm->vocab, r = dm->rank;
   const DraftPlan plan = draft_plan(dm, wdt);
   unsigned long long* best;
-  float4* part;
+  float2* part;
   draft_ws(dm, plan.nslices, &best, &part, ws);
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
@@ -178,13 +219,13 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
   for (int k = 1; k <= G; ++k) {
     const unsigned long long* bprev = k > 1 ? best + (size_t)(k - 2) * B : nullptr;
     unsigned long long* bcur = best + (size_t)(k - 1) * B;
-    float4* pk = part + (size_t)(k - 1) * plan.nslices * B;
+    float2* pk = part + (size_t)(k - 1) * plan.nslices * B;
     if (plan.mfma) {
       MfmaBiasArgs a{};
       a.mode = kModeDraft;
       a.U = U; a.W1 = (const uint16_t*)W1; a.W2t = (const uint16_t*)W2t;
-      a.anchor = anchor; a.forced = forced; a.tokens = nullptr; a.best_prev = bprev;
-      a.best_cur = bcur; a.part = pk;
+      a.anchor = anchor; a.forced = forced; a.best_prev = bprev; a.best_cur = bcur;
+      a.part = pk;
       a.B = B; a.G = G; a.V = V; a.r = r; a.k = k; a.invT = invT; a.key0 = key0; a.key1 = key1;
       a.ncols = B;
       if (launch_mfma_bias(a, plan.nslices, st) != DSPARK_OK) return DSPARK_E_HIP;
@@ -201,7 +242,13 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
                            invT, key0, key1, plan.slice_len);
     }
   }
-  hipLaunchKernelGGL(k_draft_final, dim3((B * G + 3) / 4), dim3(256), 0, st, part, best, B, G,
-                     plan.nslices, tokens, logp, lse);
+  if (wdt == DSPARK_BF16)
+    hipLaunchKernelGGL(k_draft_final<uint16_t>, dim3((B * G + 3) / 4), dim3(256), 0, st, part,
+                       best, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced, B, G,
+                       V, r, invT, plan.nslices, tokens, logp, lse);
+  else
+    hipLaunchKernelGGL(k_draft_final<float>, dim3((B * G + 3) / 4), dim3(256), 0, st, part, best,
+                       U, (const float*)W1, (const float*)W2t, anchor, forced, B, G, V, r, invT,
+                       plan.nslices, tokens, logp, lse);
   return launch_status();
 }

@@ -56,6 +56,13 @@ __device__ __forceinline__ float fast_log(float x) {
   return 0.69314718055994531f * __builtin_amdgcn_logf(x);
 }
 
+// A token id used as an index, clamped into [0, V): ids outside the vocabulary (caller
+// error, or a position whose logits were all -inf/NaN so that no candidate won) never
+// address memory outside the tables.
+__device__ __forceinline__ int clamp_tok(int x, int V) {
+  return x < 0 ? 0 : (x >= V ? V - 1 : x);
+}
+
 // ------------------------------------------------------------------------------------
 // bf16 / fp32 element access
 // ------------------------------------------------------------------------------------

@@ -7,7 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/dspark.h"
+#include "dspark.h"
 
 namespace dspark {
 

@@ -13,12 +13,14 @@
 //   kModeResid  rho = max(0, p_t - p_d); Gumbel race on ln rho            (verification)
 //   kModeTV     sum_v min(p_d, p_t)                                      [CSDN Eq. 8]
 //
-// Layout (per workgroup of 4 waves): the gathered W1 rows of all columns sit in LDS
-// (16-byte padded rows, the MFMA B operand); each wave streams its own 32-row W2t tiles
-// straight from HBM into registers (the A operand, prefetched one tile ahead), so W2t is
-// read exactly once per launch.  Output lane l of a tile holds column l%32 and the
-// vocab rows 8g + 4(l/32) + j (g, j < 4): four runs of four consecutive rows, which is
-// exactly one Philox4x32 call per run.
+// Layout (per workgroup of 4 waves): each wave keeps the gathered W1 rows of its column
+// block in registers (the MFMA B operand).  Per step the workgroup stages the next
+// 32-row W2t tile(s) and the matching 32-entry slices of every column's logit rows in
+// LDS with coalesced 1 KB loads (one HBM read each, issued a step ahead), and the waves
+// read their MFMA A fragments and epilogue operands from there.  Output lane l of a tile
+// holds column l%32 and the vocab rows 8g + 4(l/32) + j (g, j < 4): four runs of four
+// consecutive rows, which is exactly one Philox4x32 call per run.  The draft epilogue
+// works in base 2 (z2 = z log2 e), branch-free.
 #pragma once
 
 #include "dspark_dev.h"
@@ -37,14 +39,14 @@ struct MfmaBiasArgs {
   const int32_t* forced;                 // draft: teacher-forced prefix or NULL
   const int32_t* tokens;                 // resid/tv: drafted tokens [B][G]
   const unsigned long long* best_prev;   // draft: packed winners of position k-1
-  unsigned long long* best_cur;          // draft: packed winners of position k
-  float4* part;                          // draft: [slices][B] (m, l, z_win, idx_win)
+  unsigned long long* best_cur;          // draft: packed winners of position k (atomic max)
+  float2* part;                          // draft: [slices][B] base-2 softmax state (max, sum)
+  float4* rpart;                         // resid: [slices][B] (residual score, index,
+                                         //        fallback score, index)
   const float* T;                        // resid/tv: target logits [B][G+1][V]
   const float* lse_d;                    // resid/tv: draft lse [B][G]
   const float* lse_t_row;                // resid: lse of target row j_b [B]
   const int32_t* jrow;                   // resid: row j_b (1-based), 0 = no residual
-  unsigned long long* res_best;          // resid: packed residual winner [B]
-  unsigned long long* fb_best;           // resid: packed fallback (p_t) winner [B]
   const float* lse_t;                    // tv: target lse [B][G]
   float* tv_part;                        // tv: [slices][B*G] partial sums of min(p_d, p_t)
   int B, G, V, r, k;
@@ -59,8 +61,8 @@ inline bool mfma_bias_supported(int ncols, int r, int wdt) {
   return wdt == DSPARK_BF16 && r == 256 && ncols >= 32;
 }
 
-// Workgroups of one launch over V for `ncols` columns (all resident at once).
-int mfma_grid(int V, int ncols);
+// Workgroups of one launch over V for `ncols` columns in `mode` (all resident at once).
+int mfma_grid(int V, int ncols, int mode);
 
 dspark_status launch_mfma_bias(const MfmaBiasArgs& a, int nwg, hipStream_t st);
 

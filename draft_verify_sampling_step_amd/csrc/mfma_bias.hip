@@ -6,31 +6,77 @@ namespace dspark {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kR = 256;               // Markov rank handled by this path
 constexpr int kKS = kR / 16;          // MFMA k-steps
 constexpr int kRowStride = kR + 8;    // bf16 per LDS row of the gathered W1 (16-byte pad)
-constexpr int kMetaBytes = 5 * 256 * 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -3.0e38f;   // finite "minus infinity" of the running max
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int NCB, int MODE>
-__global__ __launch_bounds__(256, (NCB > 4 ? 1 : 2)) void k_mfma_bias(const MfmaBiasArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  int* col_b = reinterpret_cast<int*>(smem);
-  int* col_k = col_b + 256;
-  int* col_prev = col_k + 256;
-  float* col_ld = reinterpret_cast<float*>(col_prev + 256);
-  float* col_lt = col_ld + 256;
-  uint16_t* w1g = reinterpret_cast<uint16_t*>(smem + kMetaBytes);
-  constexpr int NC = NCB * 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = a.G, V = a.V;
-  const float invT = a.invT;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
-  // ---- column metadata: request, position, conditioning token, lse values
+// Base-2 Gumbel score offset: -log2(-log2 u) (the common constant -log2(ln 2) is dropped,
+// it shifts every candidate of a race equally).
+__device__ __forceinline__ float neg_lglg(uint32_t w) {
+  return -lg2(-lg2(word_to_uniform(w)));
+}
+
+template <int NCB, int MODE>
+struct Shape {
+  static constexpr int CBW = NCB >= 4 ? NCB / 4 : 1;     // column blocks per wave
+  static constexpr int NCW = NCB >= 4 ? 4 : NCB;         // distinct column sets
+  static constexpr int TSPLIT = 4 / NCW;                 // tiles per step
+  static constexpr int NC = NCB * 32;                    // columns
+  static constexpr bool HAS_T = MODE != kModeDraft;
+  static constexpr int kUStride = 36;                    // floats per staged logit row
+  static constexpr int kARows = TSPLIT * 32;             // staged W2t rows per step
+  static constexpr int kURows = TSPLIT * NC;             // staged logit rows per step
+  static constexpr int kAChunks = kARows * (kR / 8);     // 16-byte chunks
+  static constexpr int kUChunks = kURows * 8;
+  static constexpr int kAPer = kAChunks / 256;
+  static constexpr int kUPer = kUChunks / 256;
+  // LDS byte offsets
+  static constexpr size_t kOffA = 0;
+  static constexpr size_t kOffU = kOffA + (size_t)kARows * kRowStride * 2;
+  static constexpr size_t kOffT = kOffU + (size_t)kURows * kUStride * 4;
+  static constexpr size_t kOffMeta = kOffT + (HAS_T ? (size_t)kURows * kUStride * 4 : 0);
+  static constexpr size_t kMetaBytes = (size_t)NC * (8 + 8 + 4 + 4 + 4 + 4 + 4);
+  static constexpr size_t kRed = (size_t)TSPLIT * NC * 4 * 4;
+  static constexpr size_t kLds = kOffMeta + kMetaBytes;
+  static_assert(kAChunks % 256 == 0 && kUChunks % 256 == 0, "chunk split");
+  static_assert(kRed <= kOffMeta, "reduction scratch reuses the staging area");
+};
+
+template <int NCB, int MODE>
+__global__ __launch_bounds__(256, (NCB > 4 ? 1 : 2)) void
+k_mfma_bias(const MfmaBiasArgs a) {
+  using S = Shape<NCB, MODE>;
+  constexpr int CBW = S::CBW, NCW = S::NCW, TSPLIT = S::TSPLIT, NC = S::NC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* sA = reinterpret_cast<uint16_t*>(smem + S::kOffA);     // [kARows][kRowStride]
+  float* sU = reinterpret_cast<float*>(smem + S::kOffU);           // [kURows][kUStride]
+  float* sT = reinterpret_cast<float*>(smem + S::kOffT);
+  long long* col_urow = reinterpret_cast<long long*>(smem + S::kOffMeta);   // [NC]
+  long long* col_trow = col_urow + NC;
+  int* col_b = reinterpret_cast<int*>(col_trow + NC);
+  int* col_k = col_b + NC;
+  int* col_prev = col_k + NC;
+  float* col_ld = reinterpret_cast<float*>(col_prev + NC);
+  float* col_lt = col_ld + NC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n32 = lane & 31;
+  const int cb0 = wave % NCW, toff = wave / NCW;
+  const int G = a.G, V = a.V;
+  const float s2 = a.invT * kLog2e;   // logit -> base-2 scale
+  const bool vec4 = (V & 3) == 0;
+
+  // ---- column metadata: request, position, conditioning token, logit row offsets, lse
   for (int c = tid; c < NC; c += 256) {
     int b = -1, k = 0, prev = 0;
     float ld = 0.f, lt = 0.f;
@@ -48,212 +94,282 @@ __global__ __launch_bounds__(256, (NCB > 4 ? 1 : 2)) void k_mfma_bias(const Mfma
           b = gc;
           k = j;
           prev = (j == 1) ? a.anchor[b] : a.tokens[(size_t)b * G + (j - 2)];
-          ld = a.lse_d[(size_t)b * G + (j - 1)];
-          lt = a.lse_t_row[b];
+          ld = a.lse_d[(size_t)b * G + (j - 1)] * kLog2e;
+          lt = a.lse_t_row[b] * kLog2e;
         }
       } else {
         b = gc / G;
         k = gc % G + 1;
         prev = (k == 1) ? a.anchor[b] : a.tokens[(size_t)b * G + (k - 2)];
-        ld = a.lse_d[(size_t)b * G + (k - 1)];
-        lt = a.lse_t[(size_t)b * G + (k - 1)];
+        ld = a.lse_d[(size_t)b * G + (k - 1)] * kLog2e;
+        lt = a.lse_t[(size_t)b * G + (k - 1)] * kLog2e;
       }
     }
     col_b[c] = b;
     col_k[c] = k;
-    col_prev[c] = prev;
+    col_prev[c] = clamp_tok(prev, V);
     col_ld[c] = ld;
     col_lt[c] = lt;
-  }
-  __syncthreads();
-  // ---- gather W1[prev_c] rows into LDS (the MFMA B operand), zero for unused columns
-  for (int q = tid; q < NC * (kR / 8); q += 256) {
-    const int c = q / (kR / 8), ch = q % (kR / 8);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (col_b[c] >= 0)
-      v = *reinterpret_cast<const uint4*>(a.W1 + (size_t)col_prev[c] * kR + ch * 8);
-    *reinterpret_cast<uint4*>(w1g + c * kRowStride + ch * 8) = v;
+    col_urow[c] = b >= 0 ? ((long long)b * G + (k - 1)) * V : -1;
+    col_trow[c] = b >= 0 ? ((long long)b * (G + 1) + (k - 1)) * V : -1;
   }
   __syncthreads();
 
-  // ---- this workgroup's contiguous range of 32-row vocab tiles.  Waves split the
-  // column blocks (NCB >= 4: wave w owns blocks w, w+4, ...) or, with fewer blocks, the
-  // tiles (every TSPLIT-th tile); all waves of a column set read the same W2t tiles, so
-  // HBM sees each tile once and the repeats are L1/L2 hits.
-  constexpr int CBW = NCB >= 4 ? NCB / 4 : 1;        // column blocks per wave
-  constexpr int NCW = NCB >= 4 ? 4 : NCB;            // distinct column sets over waves
-  constexpr int TSPLIT = 4 / NCW;                    // tile interleave
+  // ---- this workgroup's contiguous range of 32-row vocab tiles, TSPLIT per step
   const int ntiles = (V + 31) >> 5;
   const int nwg = gridDim.x, wg = blockIdx.x;
   const int per = ntiles / nwg, rem = ntiles % nwg;
   const int t0 = wg * per + min(wg, rem);
   const int t1 = t0 + per + (wg < rem ? 1 : 0);
-  const int h = lane >> 5, n32 = lane & 31;
-  const int cb0 = wave % NCW, toff = wave / NCW;
-  const bool vec4 = (V & 3) == 0;
+  const int nsteps = (t1 - t0 + TSPLIT - 1) / TSPLIT;
 
-  // per-lane running state for the lane's column in each owned column block
-  float s_m[CBW], s_l[CBW], s_s[CBW], s_z[CBW], s_s2[CBW];
-  uint32_t s_i[CBW], s_i2[CBW];
+  // ---- staging: coalesced global loads of a step's tiles into registers, then LDS
+  u32x4_t RA[S::kAPer];
+  f32x4_t RU[S::kUPer], RT[S::HAS_T ? S::kUPer : 1];
+  auto stage_load = [&](int step) {
+#pragma unroll
+    for (int i = 0; i < S::kAPer; ++i) {
+      const int chunk = tid + 256 * i;
+      const int row = chunk / (kR / 8), col = chunk % (kR / 8);
+      const int v = min((t0 + step * TSPLIT) * 32 + row, V - 1);   // tile-major rows
+      RA[i] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)v * kR + col * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < S::kUPer; ++i) {
+      const int chunk = tid + 256 * i;
+      const int ur = chunk >> 3, p = chunk & 7;
+      const int tl = ur / NC, c = ur % NC;
+      const int v = (t0 + step * TSPLIT + tl) * 32 + 4 * p;
+      const long long uo = col_urow[c];
+      f32x4_t qu = {0.f, 0.f, 0.f, 0.f}, qt = {0.f, 0.f, 0.f, 0.f};
+      if (uo >= 0) {
+        if (vec4) {
+          if (v < V) {
+            qu = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.U + uo + v));
+            if (S::HAS_T)
+              qt = __builtin_nontemporal_load(
+                  reinterpret_cast<const f32x4_t*>(a.T + col_trow[c] + v));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v + j < V) {
+              qu[j] = a.U[uo + v + j];
+              if (S::HAS_T) qt[j] = a.T[col_trow[c] + v + j];
+            }
+        }
+      }
+      RU[i] = qu;
+      if (S::HAS_T) RT[i] = qt;
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < S::kAPer; ++i) {
+      const int chunk = tid + 256 * i;
+      const int row = chunk / (kR / 8), col = chunk % (kR / 8);
+      *reinterpret_cast<u32x4_t*>(sA + row * kRowStride + col * 8) = RA[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::kUPer; ++i) {
+      const int chunk = tid + 256 * i;
+      const int ur = chunk >> 3, p = chunk & 7;
+      *reinterpret_cast<f32x4_t*>(sU + ur * S::kUStride + 4 * p) = RU[i];
+      if (S::HAS_T) *reinterpret_cast<f32x4_t*>(sT + ur * S::kUStride + 4 * p) = RT[i];
+    }
+  };
+
+  if (nsteps > 0) stage_load(0);   // first tiles in flight before the dependent gathers
+
+  // ---- this lane's column in each owned block; gathered W1 row = MFMA B operand
+  int cbb[CBW], cbk[CBW];
+  float cbld[CBW], cblt[CBW];
+  uint4 Bop[CBW][kKS];
 #pragma unroll
   for (int q = 0; q < CBW; ++q) {
-    s_m[q] = -INFINITY;
-    s_l[q] = 0.f;
-    s_s[q] = -INFINITY;
-    s_z[q] = 0.f;
-    s_s2[q] = -INFINITY;
-    s_i[q] = 0xFFFFFFFFu;
-    s_i2[q] = 0xFFFFFFFFu;
+    const int c = (cb0 + 4 * q) * 32 + n32;
+    cbb[q] = col_b[c];
+    cbk[q] = col_k[c];
+    cbld[q] = col_ld[c];
+    cblt[q] = col_lt[c];
+    const uint16_t* wrow = a.W1 + (size_t)col_prev[c] * kR + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk)
+      Bop[q][kk] = cbb[q] >= 0 ? *reinterpret_cast<const uint4*>(wrow + kk * 16)
+                               : make_uint4(0u, 0u, 0u, 0u);
   }
 
-  uint4 A[kKS], An[kKS];
-  int t = t0 + toff;
-  if (t < t1) {
-    const int v = min(t * 32 + n32, V - 1);
-    const uint16_t* row = a.W2t + (size_t)v * kR + 8 * h;
+  // per-lane running state of the lane's column in each owned block
+  float st_m[CBW], st_l[CBW], st_s[CBW], st_s2[CBW];
+  uint32_t st_v[CBW], st_v2[CBW];
 #pragma unroll
-    for (int kk = 0; kk < kKS; ++kk) A[kk] = *reinterpret_cast<const uint4*>(row + kk * 16);
+  for (int q = 0; q < CBW; ++q) {
+    st_m[q] = kNegBig;
+    st_l[q] = 0.f;
+    st_s[q] = -INFINITY;
+    st_s2[q] = -INFINITY;
+    st_v[q] = 0xFFFFFFFFu;
+    st_v2[q] = 0xFFFFFFFFu;
   }
-  for (; t < t1; t += TSPLIT) {
-    const bool more = t + TSPLIT < t1;
-    if (more) {
-      const int v = min((t + TSPLIT) * 32 + n32, V - 1);
-      const uint16_t* row = a.W2t + (size_t)v * kR + 8 * h;
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) An[kk] = *reinterpret_cast<const uint4*>(row + kk * 16);
-    }
+
+  if (nsteps > 0) stage_store();
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const bool more = step + 1 < nsteps;
+    if (more) stage_load(step + 1);            // in flight while this step computes
+    const int t = t0 + step * TSPLIT + toff;
+    const bool active = t < t1;                // wave-uniform
+    const bool full = (t + 1) * 32 <= V;       // every row of this tile is a vocab entry
+    const int vrow = t * 32 + 4 * h;           // first row of this lane's runs
+    const uint16_t* At = sA + (toff * 32 + n32) * kRowStride + 8 * h;
 #pragma unroll
     for (int q = 0; q < CBW; ++q) {
-      const int cb = cb0 + 4 * q;
+      const int b = cbb[q];
+      if (!active) continue;
       f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                       0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const uint16_t* bp = w1g + (cb * 32 + n32) * kRowStride + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < kKS; ++kk) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(bp + kk * 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[kk]), as_bf16x8(bv), acc, 0,
-                                                      0, 0);
+        const uint4 av = *reinterpret_cast<const uint4*>(At + kk * 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(Bop[q][kk]), acc,
+                                                      0, 0, 0);
       }
-      const int c = cb * 32 + n32;
-      const int b = col_b[c];
       if (b < 0) continue;
-      const int k = col_k[c];
-      const float* urow = a.U + ((size_t)b * G + (k - 1)) * V;
-      const float* trow = (MODE == kModeDraft) ? nullptr : a.T + ((size_t)b * (G + 1) + (k - 1)) * V;
-      const float ld = col_ld[c], lt = col_lt[c];
+      const int k = cbk[q];
+      const int ur = toff * NC + (cb0 + 4 * q) * 32 + n32;   // staged logit row
+      f32x4_t uq[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int v0 = t * 32 + 8 * g + 4 * h;
-        if (v0 >= V) continue;
-        float u[4], tt[4];
-        if (vec4) {
-          const f32x4_t qv = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(urow + v0));
-          u[0] = qv[0]; u[1] = qv[1]; u[2] = qv[2]; u[3] = qv[3];
-          if (MODE != kModeDraft) {
-            const f32x4_t p = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(trow + v0));
-            tt[0] = p[0]; tt[1] = p[1]; tt[2] = p[2]; tt[3] = p[3];
-          }
-        } else {
+      for (int g = 0; g < 4; ++g)
+        uq[g] = *reinterpret_cast<const f32x4_t*>(sU + ur * S::kUStride + 8 * g + 4 * h);
+      // base-2 logits of the 16 rows; rows past V become -inf
+      float z[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[4 * g + j] = (uq[g][j] + acc[4 * g + j]) * s2;
+      if (!full) {   // wave-uniform: only the last tile of the vocabulary is partial
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (vrow + 8 * g + j >= V) z[4 * g + j] = -INFINITY;
+      }
+      if (MODE == kModeDraft) {
+        float mx = z[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, z[i]);
+        const float mnew = fmaxf(st_m[q], mx);
+        float l = st_l[q] * ex2(st_m[q] - mnew);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) l += ex2(z[i] - mnew);
+        st_m[q] = mnew;
+        st_l[q] = l;
+        float bs = st_s[q];
+        uint32_t bvx = st_v[q];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const U4 w = philox10((uint32_t)(t * 8 + 2 * g + h), (uint32_t)k, (uint32_t)b, 0u,
+                                a.key0, a.key1);
+          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            u[j] = (v0 + j < V) ? urow[v0 + j] : 0.f;
-            if (MODE != kModeDraft) tt[j] = (v0 + j < V) ? trow[v0 + j] : 0.f;
+            const float sc = z[4 * g + j] + neg_lglg(wd[j]);
+            const bool better = sc > bs;
+            bs = better ? sc : bs;
+            bvx = better ? (uint32_t)(vrow + 8 * g + j) : bvx;
           }
         }
-        const int nvalid = min(4, V - v0);
-        if (MODE == kModeDraft) {
-          const U4 w = philox10((uint32_t)v0 >> 2, (uint32_t)k, (uint32_t)b, 0u, a.key0, a.key1);
-          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-          float z[4];
-          float gm = -INFINITY;
+        st_s[q] = bs;
+        st_v[q] = bvx;
+      } else {
+        const float ld = cbld[q], lt = cblt[q];
+        f32x4_t tq[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            z[j] = (u[j] + acc[4 * g + j]) * invT;
-            if (j < nvalid) gm = fmaxf(gm, z[j]);
-          }
-          if (gm > s_m[q]) {
-            s_l[q] *= fast_exp(s_m[q] - gm);
-            s_m[q] = gm;
-          }
+        for (int g = 0; g < 4; ++g)
+          tq[g] = *reinterpret_cast<const f32x4_t*>(sT + ur * S::kUStride + 8 * g + 4 * h);
+        float zt[16];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (j < nvalid) {
-              s_l[q] += fast_exp(z[j] - s_m[q]);
-              const float sc = z[j] + gumbel_from_uniform(word_to_uniform(wd[j]));
-              if (sc > s_s[q]) {
-                s_s[q] = sc;
-                s_i[q] = (uint32_t)(v0 + j);
-                s_z[q] = z[j];
-              }
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) zt[4 * g + j] = tq[g][j] * s2;
+        if (!full) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (vrow + 8 * g + j >= V) zt[4 * g + j] = -INFINITY;
+        }
+        if (MODE == kModeResid) {
+          float bs = st_s[q], bs2 = st_s2[q];
+          uint32_t bvx = st_v[q], bvx2 = st_v2[q];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const U4 w = philox10((uint32_t)(t * 8 + 2 * g + h), (uint32_t)k, (uint32_t)b, 2u,
+                                  a.key0, a.key1);
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * g + j;
+              const float gn = neg_lglg(wd[j]);
+              const float rho = ex2(zt[i] - lt) - ex2(z[i] - ld);
+              const float sc = rho > 0.f ? lg2(rho) + gn : -INFINITY;
+              const bool better = sc > bs;
+              bs = better ? sc : bs;
+              bvx = better ? (uint32_t)(vrow + 8 * g + j) : bvx;
+              const float sc2 = zt[i] + gn;
+              const bool better2 = sc2 > bs2;
+              bs2 = better2 ? sc2 : bs2;
+              bvx2 = better2 ? (uint32_t)(vrow + 8 * g + j) : bvx2;
             }
           }
-        } else if (MODE == kModeResid) {
-          const U4 w = philox10((uint32_t)v0 >> 2, (uint32_t)k, (uint32_t)b, 2u, a.key0, a.key1);
-          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (j < nvalid) {
-              const float zd = (u[j] + acc[4 * g + j]) * invT;
-              const float zt = tt[j] * invT;
-              const float rho = fast_exp(zt - lt) - fast_exp(zd - ld);
-              const float gn = gumbel_from_uniform(word_to_uniform(wd[j]));
-              if (rho > 0.f) {
-                const float sc = fast_log(rho) + gn;
-                if (sc > s_s[q]) { s_s[q] = sc; s_i[q] = (uint32_t)(v0 + j); }
-              }
-              const float sc2 = zt + gn;
-              if (sc2 > s_s2[q]) { s_s2[q] = sc2; s_i2[q] = (uint32_t)(v0 + j); }
-            }
-          }
+          st_s[q] = bs;
+          st_v[q] = bvx;
+          st_s2[q] = bs2;
+          st_v2[q] = bvx2;
         } else {
+          float sum = st_l[q];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (j < nvalid) {
-              const float pd = fast_exp((u[j] + acc[4 * g + j]) * invT - ld);
-              const float pt = fast_exp(tt[j] * invT - lt);
-              s_l[q] += fminf(pd, pt);
-            }
-          }
+          for (int i = 0; i < 16; ++i) sum += fminf(ex2(z[i] - ld), ex2(zt[i] - lt));
+          st_l[q] = sum;
         }
       }
     }
+    __syncthreads();                // every wave is done reading this step's tiles
     if (more) {
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) A[kk] = An[kk];
+      stage_store();
+      __syncthreads();
     }
   }
 
   // ---- merge the two lane halves holding the same column, then the TSPLIT waves that
-  // covered disjoint tiles of it (fixed order: deterministic)
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem + kMetaBytes);   // [TSPLIT][NC][5]
+  // covered disjoint tiles of it, in a fixed order: deterministic
+  float* red = reinterpret_cast<float*>(smem);   // [TSPLIT][NC][4] over the staging area
 #pragma unroll
   for (int q = 0; q < CBW; ++q) {
     const int cb = cb0 + 4 * q;
-    const float om = __shfl_xor(s_m[q], 32, kWave);
-    const float ol = __shfl_xor(s_l[q], 32, kWave);
-    const float os = __shfl_xor(s_s[q], 32, kWave);
-    const float oz = __shfl_xor(s_z[q], 32, kWave);
-    const uint32_t oi = (uint32_t)__shfl_xor((int)s_i[q], 32, kWave);
-    const float os2 = __shfl_xor(s_s2[q], 32, kWave);
-    const uint32_t oi2 = (uint32_t)__shfl_xor((int)s_i2[q], 32, kWave);
-    float m = s_m[q], l = s_l[q], sc = s_s[q], z = s_z[q], sc2 = s_s2[q];
-    uint32_t i = s_i[q], i2 = s_i2[q];
+    float m = st_m[q], l = st_l[q], sc = st_s[q], sc2 = st_s2[q];
+    uint32_t v = st_v[q], v2 = st_v2[q];
+    const float om = __shfl_xor(m, 32, kWave);
+    const float ol = __shfl_xor(l, 32, kWave);
+    const float os = __shfl_xor(sc, 32, kWave);
+    const uint32_t ov = (uint32_t)__shfl_xor((int)v, 32, kWave);
+    const float os2 = __shfl_xor(sc2, 32, kWave);
+    const uint32_t ov2 = (uint32_t)__shfl_xor((int)v2, 32, kWave);
     if (MODE == kModeDraft) {
-      const ML mm = ml_merge(ML{m, l}, ML{om, ol});
-      m = mm.m;
-      l = mm.l;
+      const float mm = fmaxf(m, om);
+      l = l * ex2(m - mm) + ol * ex2(om - mm);
+      m = mm;
     } else {
       l = l + ol;
     }
-    if (os > sc || (os == sc && oi < i)) { sc = os; i = oi; z = oz; }
-    if (os2 > sc2 || (os2 == sc2 && oi2 < i2)) { sc2 = os2; i2 = oi2; }
+    if (os > sc || (os == sc && ov < v)) { sc = os; v = ov; }
+    if (os2 > sc2 || (os2 == sc2 && ov2 < v2)) { sc2 = os2; v2 = ov2; }
     if (h == 0) {
-      float* e = red + ((size_t)toff * NC + cb * 32 + n32) * 5;
+      float* e = red + ((size_t)toff * NC + cb * 32 + n32) * 4;
       if (MODE == kModeDraft) {
-        e[0] = m; e[1] = l; e[2] = sc; e[3] = z; e[4] = __uint_as_float(i);
+        e[0] = m; e[1] = l; e[2] = sc; e[3] = __uint_as_float(v);
       } else if (MODE == kModeResid) {
-        e[0] = sc; e[1] = __uint_as_float(i); e[2] = sc2; e[3] = __uint_as_float(i2);
+        e[0] = sc; e[1] = __uint_as_float(v); e[2] = sc2; e[3] = __uint_as_float(v2);
       } else {
         e[0] = l;
       }
@@ -264,44 +380,39 @@ __global__ __launch_bounds__(256, (NCB > 4 ? 1 : 2)) void k_mfma_bias(const Mfma
     const int b = col_b[c];
     if (b < 0) continue;
     if (MODE == kModeDraft) {
-      ML st{-INFINITY, 0.f};
-      Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+      float m = kNegBig, l = 0.f, sc = -INFINITY;
+      uint32_t v = 0xFFFFFFFFu;
       for (int w = 0; w < TSPLIT; ++w) {
-        const float* e = red + ((size_t)w * NC + c) * 5;
-        st = ml_merge(st, ML{e[0], e[1]});
-        const Cand o{e[2], __float_as_uint(e[4]), e[3]};
-        if (cand_better(o, best)) best = o;
+        const float* e = red + ((size_t)w * NC + c) * 4;
+        const float mm = fmaxf(m, e[0]);
+        l = l * ex2(m - mm) + e[1] * ex2(e[0] - mm);
+        m = mm;
+        const uint32_t ev = __float_as_uint(e[3]);
+        if (e[2] > sc || (e[2] == sc && ev < v)) { sc = e[2]; v = ev; }
       }
-      a.part[(size_t)wg * a.B + b] = make_float4(st.m, st.l, best.z, __uint_as_float(best.i));
-      atomic_max_u64(&a.best_cur[b], pack_score(best.s, best.i));
+      a.part[(size_t)wg * a.B + b] = make_float2(m, l);
+      if (v != 0xFFFFFFFFu) atomic_max_u64(&a.best_cur[b], pack_score(sc, v));
     } else if (MODE == kModeResid) {
-      Cand b1{-INFINITY, 0xFFFFFFFFu, 0.f}, b2{-INFINITY, 0xFFFFFFFFu, 0.f};
+      float sc = -INFINITY, sc2 = -INFINITY;
+      uint32_t v = 0xFFFFFFFFu, v2 = 0xFFFFFFFFu;
       for (int w = 0; w < TSPLIT; ++w) {
-        const float* e = red + ((size_t)w * NC + c) * 5;
-        const Cand o1{e[0], __float_as_uint(e[1]), 0.f}, o2{e[2], __float_as_uint(e[3]), 0.f};
-        if (cand_better(o1, b1)) b1 = o1;
-        if (cand_better(o2, b2)) b2 = o2;
+        const float* e = red + ((size_t)w * NC + c) * 4;
+        const uint32_t ev = __float_as_uint(e[1]), ev2 = __float_as_uint(e[3]);
+        if (e[0] > sc || (e[0] == sc && ev < v)) { sc = e[0]; v = ev; }
+        if (e[2] > sc2 || (e[2] == sc2 && ev2 < v2)) { sc2 = e[2]; v2 = ev2; }
       }
-      if (b1.i != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[b], pack_score(b1.s, b1.i));
-      if (b2.i != 0xFFFFFFFFu) atomic_max_u64(&a.fb_best[b], pack_score(b2.s, b2.i));
+      a.rpart[(size_t)wg * a.B + b] = make_float4(sc, __uint_as_float(v), sc2, __uint_as_float(v2));
     } else {
       float sum = 0.f;
-      for (int w = 0; w < TSPLIT; ++w) sum += red[((size_t)w * NC + c) * 5];
+      for (int w = 0; w < TSPLIT; ++w) sum += red[((size_t)w * NC + c) * 4];
       a.tv_part[(size_t)wg * ((size_t)a.B * a.G) + (a.col0 + c)] = sum;
     }
   }
 }
 
-template <int NCB>
-static size_t lds_bytes() {
-  const size_t w1g = (size_t)NCB * 32 * kRowStride * 2;
-  const size_t red = (size_t)4 * NCB * 32 * 5 * 4;
-  return kMetaBytes + (w1g > red ? w1g : red);
-}
-
 template <int NCB, int MODE>
 static dspark_status launch_t(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
-  const size_t sh = lds_bytes<NCB>();
+  const size_t sh = Shape<NCB, MODE>::kLds;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)k_mfma_bias<NCB, MODE>,
@@ -322,11 +433,12 @@ static dspark_status launch_mode(const MfmaBiasArgs& a, int nwg, hipStream_t st)
   return launch_t<8, MODE>(a, nwg, st);
 }
 
-int mfma_grid(int V, int ncols) {
+int mfma_grid(int V, int ncols, int mode) {
+  // one resident wave of workgroups: per-CU occupancy of each variant (registers, LDS)
   const int ntiles = (V + 31) / 32;
   const int ncb = (std::min(ncols, 256) + 31) / 32;
-  const int resident = (ncb > 4 ? 1 : 2) * 256;
-  return std::max(1, std::min(ntiles, resident));
+  const int per_cu = (ncb > 4 || ncb == 1) ? 1 : 2;
+  return std::max(1, std::min(ntiles, per_cu * 256));
 }
 
 dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st) {

@@ -6,8 +6,10 @@
 //     multiplied left to right (the same rounding sequence as the plain definition);
 //  2. all (b, j) candidates sorted by (a descending, b ascending, j ascending) with a
 //     bitonic network in LDS -- the key (a, b*gamma + j - 1) is a total order;
-//  3. the greedy walk in one thread: tau and Theta accumulate in fp64 in sorted order,
-//     stopping at the first candidate that does not raise Theta.
+//  3. the greedy walk: tau accumulates in fp64 in sorted order (a sequential chain, the
+//     plain definition's rounding); the stop tests of 64 candidates at a time run in
+//     parallel on one wave; the walk stops at the first candidate that does not raise
+//     Theta.
 // Since a_{b,j} is non-increasing in j (c <= 1) and ties go to the lower j, admissions
 // are always prefixes of each request's block.
 #include "dspark_dev.h"
@@ -37,7 +39,6 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
       key_a[b * G + j] = a;
       key_i[b * G + j] = (uint32_t)(b * G + j);
     }
-    ell[b] = 0;
   }
   for (int i = n + tid; i < np; i += blockDim.x) {
     key_a[i] = -1.0;               // padding sorts after every real candidate
@@ -62,21 +63,59 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
       __syncthreads();
     }
   }
-  if (tid == 0) {
-    int N = B;
+  // greedy walk on wave 0, 64 candidates per chunk.  tau_t follows the sequential fp64
+  // chain tau_{t+1} = tau_t + a_(t) exactly (lane 0 order, broadcast per step); the best
+  // Theta before candidate t is tau_t * sps[B + t] (each admission raises it to exactly
+  // that product), so the stop tests of a chunk are independent and run in parallel.
+  __shared__ int stop_s;
+  __shared__ double tau_s;
+  if (tid < 64) {
+    const int lane = tid;
     double tau = (double)B;
-    double best = tau * sps[N];
-    for (int t = 0; t < n; ++t) {
-      const double tau_next = tau + key_a[t];
-      const double th = tau_next * sps[N + 1];
-      if (mode == DSPARK_SCHED_GREEDY && th <= best) break;
-      tau = tau_next;
-      N = N + 1;
-      best = th;
-      const uint32_t i = key_i[t];
-      ell[i / G] = (int32_t)(i % G) + 1;
+    int stop = n;
+    for (int base = 0; base < n; base += 64) {
+      const int t = base + lane;
+      const double at = t < n ? key_a[t] : 0.0;
+      const int cnt = min(64, n - base);
+      double before = 0.0, after = 0.0, cur = tau;
+      for (int i = 0; i < cnt; ++i) {
+        const double ai = __shfl(at, i, 64);
+        before = (lane == i) ? cur : before;
+        cur = cur + ai;
+        after = (lane == i) ? cur : after;
+      }
+      bool halt = false;
+      if (mode == DSPARK_SCHED_GREEDY && t < n) {
+        const double th_next = after * sps[B + t + 1];
+        const double th_best = before * sps[B + t];
+        halt = th_next <= th_best;
+      }
+      const unsigned long long hm = __ballot(halt);
+      if (hm) {
+        const int first = __ffsll((long long)hm) - 1;
+        stop = base + first;
+        tau = __shfl(before, first, 64);
+        break;
+      }
+      tau = cur;   // every lane ran the same chain: cur is the chunk's final tau
     }
-    theta[0] = best;
+    if (lane == 0) {
+      stop_s = stop;
+      tau_s = tau;
+    }
+  }
+  __syncthreads();
+  const int stop = stop_s;
+  for (int b = tid; b < B; b += blockDim.x) ell[b] = 0;
+  __syncthreads();
+  // admitted candidates form a prefix of each request's block: ell_b = the largest j
+  for (int t = tid; t < stop; t += blockDim.x) {
+    const uint32_t i = key_i[t];
+    atomicMax(&ell[i / G], (int)(i % G) + 1);
+  }
+  if (tid == 0) {
+    const int N = B + stop;
+    theta[0] = tau_s * sps[N];
     n_total[0] = N;
   }
 }

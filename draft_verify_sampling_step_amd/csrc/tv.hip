@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_tv_row(
   float* red = bias_s + 256;
   const int s = blockIdx.x, col = blockIdx.y, tid = threadIdx.x;
   const int b = col / G, k = col % G + 1;
-  const int prev = (k == 1) ? anchor[b] : tokens[(size_t)b * G + (k - 2)];
+  const int prev = clamp_tok((k == 1) ? anchor[b] : tokens[(size_t)b * G + (k - 2)], V);
   const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
   load_w1_row<WT>(W1, prev, r, w1s);
   __syncthreads();
@@ -121,7 +121,7 @@ TvWs tv_ws(const dspark_dims* d, int nrow_slices, int nsum_slices, void* base) {
 
 int tv_sum_slices(const dspark_dims* d, bool mfma) {
   const long long n = (long long)d->batch * d->gamma;
-  return mfma ? mfma_grid(d->vocab, (int)std::min<long long>(n, 256))
+  return mfma ? mfma_grid(d->vocab, (int)std::min<long long>(n, 256), kModeTV)
               : row_slices(d->vocab, n).count;
 }
 

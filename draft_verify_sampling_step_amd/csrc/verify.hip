@@ -28,50 +28,167 @@ __global__ void k_vfill_u64(unsigned long long* p, size_t n) {
     p[i] = 0ull;
 }
 
-// grid (slices, B, gamma+1), 256 threads
+// Flattened ragged row list: rows (b, k) with k <= ell_b + 1, in request order.  One
+// workgroup; writes the list, its length and the number of (row, slice) work items.
+__global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__ ell, int B,
+                                                     int G, int nslices,
+                                                     int32_t* __restrict__ rows,
+                                                     int32_t* __restrict__ counts) {
+  __shared__ int32_t scan[256];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    int n = 0;
+    if (b < B) {
+      const int L = ell[b];
+      n = (L < 0 ? 0 : (L > G ? G : L)) + 1;
+    }
+    scan[tid] = n;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int add = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int start = carry + scan[tid] - n;
+    for (int i = 0; i < n; ++i) rows[start + i] = b * (G + 1) + i;   // row id b*(G+1) + (k-1)
+    __syncthreads();
+    if (tid == 255) carry += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[0] = carry;
+    counts[1] = carry * nslices;
+  }
+}
+
+// Grid-stride over (row, slice) items: split-vocabulary (max, sum-exp) partials of
+// T/temperature; on row ell_b + 1 also the bonus token's Gumbel race.
 __global__ __launch_bounds__(256) void k_verify_rows(
-    const float* __restrict__ T, const int32_t* __restrict__ ell, int B, int G, int V,
+    const float* __restrict__ T, const int32_t* __restrict__ ell,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, int G, int V,
     int slice_len, int nslices, float invT, uint32_t key0, uint32_t key1,
     float2* __restrict__ part, unsigned long long* __restrict__ bonus) {
   __shared__ float red[16];
-  const int s = blockIdx.x, b = blockIdx.y, kk = blockIdx.z, k = kk + 1;
-  const int L = ell[b];
-  if (k > L + 1) return;
-  const bool is_bonus = (k == L + 1);
-  const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
-  const float* row = T + ((size_t)b * (G + 1) + kk) * V;
-  ML st{-INFINITY, 0.f};
-  Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
-  for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
-    const float z = __builtin_nontemporal_load(row + v) * invT;
-    if (z > st.m) {
-      st.l = st.l * fast_exp(st.m - z) + 1.f;
-      st.m = z;
+  const int nitems = counts[1];
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int row = rows[item / nslices], s = item % nslices;
+    const int b = row / (G + 1), k = row % (G + 1) + 1;
+    const int Lb = ell[b];
+    const bool is_bonus = (k == (Lb < 0 ? 0 : (Lb > G ? G : Lb)) + 1);
+    const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
+    const float* trow = T + (size_t)row * V;
+    const float s2 = invT * 1.4426950408889634f;
+    float m = -3.0e38f, l = 0.f;
+    Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+    auto visit = [&](float t, int v) {
+      const float z = t * s2;
+      const float mn = fmaxf(m, z);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
+      m = mn;
+      if (is_bonus) {
+        const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
+        const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
+        const float sc =
+            z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
+        if (sc > best.s) best = Cand{sc, (uint32_t)v, 0.f};
+      }
+    };
+    if ((V & 3) == 0) {
+      // all of this thread's 16-byte loads are issued before any is consumed
+      constexpr int kQ = 8;   // float4 per thread per 8192-entry slice
+      typedef float f4 __attribute__((ext_vector_type(4)));
+      f4 q[kQ];
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
+        q[i] = v < v_end ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(trow + v))
+                         : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
+        if (v < v_end) {
+          // four consecutive entries share one Philox call (words 0..3)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float z = q[i][j] * s2;
+            const float mn = fmaxf(m, z);
+            l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
+            m = mn;
+          }
+          if (is_bonus) {
+            const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float sc = q[i][j] * s2 -
+                               __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(wd[j])));
+              if (sc > best.s) best = Cand{sc, (uint32_t)(v + j), 0.f};
+            }
+          }
+        }
+      }
+      for (int v = v_begin + 4 * 256 * kQ + 4 * threadIdx.x; v < v_end; v += 1024) {
+        const f4 t4 = *reinterpret_cast<const f4*>(trow + v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) visit(t4[j], v + j);
+      }
     } else {
-      st.l += fast_exp(z - st.m);
+      for (int v = v_begin + threadIdx.x; v < v_end; v += 256) visit(trow[v], v);
     }
+    // workgroup merge of the base-2 state
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+      const float mn = fmaxf(m, om);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+      m = mn;
+    }
+    if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mm = red[0], ll = red[4];
+      for (int i = 1; i < 4; ++i) {
+        const float mn = fmaxf(mm, red[i]);
+        ll = ll * __builtin_amdgcn_exp2f(mm - mn) + red[4 + i] * __builtin_amdgcn_exp2f(red[i] - mn);
+        mm = mn;
+      }
+      part[(size_t)row * nslices + s] = make_float2(mm, ll);
+    }
+    __syncthreads();
     if (is_bonus) {
-      const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
-      const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-      const float sc = z + gumbel_from_uniform(word_to_uniform(word));
-      if (sc > best.s) best = Cand{sc, (uint32_t)v, z};
+      best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
+      if (threadIdx.x == 0 && best.i != 0xFFFFFFFFu)
+        atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
     }
   }
-  st = block_ml(st, red, red + 4);
-  if (is_bonus) best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
-  if (threadIdx.x == 0) {
-    part[((size_t)b * (G + 1) + kk) * nslices + s] = make_float2(st.m, st.l);
-    if (is_bonus) atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
+}
+
+// lse (natural log) of one target row from its base-2 slice partials; wave-cooperative.
+__device__ __forceinline__ float wave_row_lse(const float2* p, int n, int lane) {
+  float m = -3.0e38f, l = 0.f;
+  for (int s = lane; s < n; s += kWave) {
+    const float mn = fmaxf(m, p[s].x);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + p[s].y * __builtin_amdgcn_exp2f(p[s].x - mn);
+    m = mn;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+    const float mn = fmaxf(m, om);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+    m = mn;
+  }
+  return (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
-__device__ __forceinline__ float row_lse(const float2* p, int n) {
-  ML st{-INFINITY, 0.f};
-  for (int s = 0; s < n; ++s) st = ml_merge(st, ML{p[s].x, p[s].y});
-  return st.m + fast_log(st.l);
-}
-
-// one thread per request
+// one wave per request
 __global__ __launch_bounds__(256) void k_verify_decide(
     const float* __restrict__ T, const int32_t* __restrict__ tokens,
     const float* __restrict__ logp, const int32_t* __restrict__ ell,
@@ -79,20 +196,21 @@ __global__ __launch_bounds__(256) void k_verify_decide(
     int V, int nslices, float invT, uint32_t key0, uint32_t key1,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
     float* __restrict__ pt_tok, int32_t* __restrict__ jrow, float* __restrict__ lse_t_row) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= B) return;
-  const int L = ell[b];
+  const int Lb = ell[b];
+  const int L = Lb < 0 ? 0 : (Lb > G ? G : Lb);   // ell outside [0, gamma] is clamped
   int n = 0, j = 0;
   float lj = 0.f;
   for (int k = 1; k <= G; ++k) {
     if (k > L) {
-      if (pt_tok) pt_tok[(size_t)b * G + (k - 1)] = __builtin_nanf("");
+      if (pt_tok && lane == 0) pt_tok[(size_t)b * G + (k - 1)] = __builtin_nanf("");
       continue;
     }
-    const float lt = row_lse(part + ((size_t)b * (G + 1) + (k - 1)) * nslices, nslices);
-    const int x = tokens[(size_t)b * G + (k - 1)];
+    const float lt = wave_row_lse(part + ((size_t)b * (G + 1) + (k - 1)) * nslices, nslices, lane);
+    const int x = clamp_tok(tokens[(size_t)b * G + (k - 1)], V);
     const float pt = fast_exp(T[((size_t)b * (G + 1) + (k - 1)) * V + x] * invT - lt);
-    if (pt_tok) pt_tok[(size_t)b * G + (k - 1)] = pt;
+    if (pt_tok && lane == 0) pt_tok[(size_t)b * G + (k - 1)] = pt;
     if (j == 0) {
       const U4 w = philox10(0u, (uint32_t)k, (uint32_t)b, 1u, key0, key1);
       const float u = word_to_uniform(w.x);
@@ -106,11 +224,13 @@ __global__ __launch_bounds__(256) void k_verify_decide(
     }
   }
   int32_t* out = out_tokens + (size_t)b * (G + 1);
-  for (int i = 0; i <= G; ++i) out[i] = i < n ? tokens[(size_t)b * G + i] : -1;
-  if (j == 0) out[n] = (int32_t)packed_index(bonus[b]);
-  n_accept[b] = n;
-  jrow[b] = j;
-  lse_t_row[b] = lj;
+  for (int i = lane; i <= G; i += kWave) out[i] = i < n ? tokens[(size_t)b * G + i] : -1;
+  if (lane == 0) {
+    if (j == 0) out[n] = (int32_t)packed_index(bonus[b]);
+    n_accept[b] = n;
+    jrow[b] = j;
+    lse_t_row[b] = lj;
+  }
 }
 
 // Row residual: grid (slices, B), 256 threads.
@@ -121,7 +241,7 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
     const int32_t* __restrict__ tokens, const float* __restrict__ lse_d,
     const int32_t* __restrict__ jrow, const float* __restrict__ lse_t_row, int B, int G, int V,
     int r, int slice_len, float invT, uint32_t key0, uint32_t key1,
-    unsigned long long* __restrict__ res, unsigned long long* __restrict__ fb) {
+    float4* __restrict__ res_part) {
   extern __shared__ float smem[];
   float* w1s = smem;
   float* bias_s = smem + r;
@@ -129,7 +249,7 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
   const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = jrow[b];
   if (j == 0) return;
-  const int prev = (j == 1) ? anchor[b] : tokens[(size_t)b * G + (j - 2)];
+  const int prev = clamp_tok((j == 1) ? anchor[b] : tokens[(size_t)b * G + (j - 2)], V);
   const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
   load_w1_row<WT>(W1, prev, r, w1s);
   __syncthreads();
@@ -159,22 +279,41 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
   }
   b1 = block_cand(b1, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
   b2 = block_cand(b2, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
-  if (tid == 0) {
-    if (b1.i != 0xFFFFFFFFu) atomic_max_u64(&res[b], pack_score(b1.s, b1.i));
-    if (b2.i != 0xFFFFFFFFu) atomic_max_u64(&fb[b], pack_score(b2.s, b2.i));
-  }
+  if (tid == 0)
+    res_part[(size_t)s * B + b] =
+        make_float4(b1.s, __uint_as_float(b1.i), b2.s, __uint_as_float(b2.i));
 }
 
+// One wave per request with a residual row: reduce the residual (and fallback p_t) races
+// over the slice partials in a fixed order; write the token after the accepted prefix.
 __global__ __launch_bounds__(256) void k_verify_final(const int32_t* __restrict__ jrow,
                                                       const int32_t* __restrict__ n_accept,
-                                                      const unsigned long long* __restrict__ res,
-                                                      const unsigned long long* __restrict__ fb,
-                                                      int B, int G,
+                                                      const float4* __restrict__ res_part,
+                                                      int nslices, int B, int G,
                                                       int32_t* __restrict__ out_tokens) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (b >= B || jrow[b] == 0) return;
-  const unsigned long long w = res[b] != 0ull ? res[b] : fb[b];
-  out_tokens[(size_t)b * (G + 1) + n_accept[b]] = (int32_t)packed_index(w);
+  float s1 = -INFINITY, s2 = -INFINITY;
+  uint32_t i1 = 0xFFFFFFFFu, i2 = 0xFFFFFFFFu;
+  for (int s = lane; s < nslices; s += kWave) {
+    const float4 p = res_part[(size_t)s * B + b];
+    const uint32_t pi1 = __float_as_uint(p.y), pi2 = __float_as_uint(p.w);
+    if (p.x > s1 || (p.x == s1 && pi1 < i1)) { s1 = p.x; i1 = pi1; }
+    if (p.z > s2 || (p.z == s2 && pi2 < i2)) { s2 = p.z; i2 = pi2; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float os1 = __shfl_xor(s1, o, kWave), os2 = __shfl_xor(s2, o, kWave);
+    const uint32_t oi1 = (uint32_t)__shfl_xor((int)i1, o, kWave);
+    const uint32_t oi2 = (uint32_t)__shfl_xor((int)i2, o, kWave);
+    if (os1 > s1 || (os1 == s1 && oi1 < i1)) { s1 = os1; i1 = oi1; }
+    if (os2 > s2 || (os2 == s2 && oi2 < i2)) { s2 = os2; i2 = oi2; }
+  }
+  if (lane == 0) {
+    // no positive residual anywhere (rounding): fall back to the p_t race
+    const uint32_t y = i1 != 0xFFFFFFFFu ? i1 : i2;
+    out_tokens[(size_t)b * (G + 1) + n_accept[b]] = (int32_t)y;
+  }
 }
 
 }  // namespace dspark
@@ -185,32 +324,42 @@ namespace {
 
 struct VerifyWs {
   float2* part;
+  int32_t* rows;
+  int32_t* counts;
   unsigned long long* bonus;
-  unsigned long long* res;
-  unsigned long long* fb;
+  float4* res_part;
   int32_t* jrow;
   float* lse_t_row;
   size_t bytes;
 };
 
-VerifyWs verify_ws(const dspark_dims* d, int nslices, void* base) {
+VerifyWs verify_ws(const dspark_dims* d, int nslices, int nres_slices, void* base) {
   Carve c(base);
   VerifyWs w;
   w.part = c.take<float2>((size_t)d->batch * (d->gamma + 1) * nslices);
-  w.bonus = c.take<unsigned long long>((size_t)3 * d->batch);
-  w.res = w.bonus ? w.bonus + d->batch : nullptr;
-  w.fb = w.bonus ? w.bonus + 2 * d->batch : nullptr;
+  w.rows = c.take<int32_t>((size_t)d->batch * (d->gamma + 1));
+  w.counts = c.take<int32_t>(2);
+  w.bonus = c.take<unsigned long long>((size_t)d->batch);
+  w.res_part = c.take<float4>((size_t)nres_slices * d->batch);
   w.jrow = c.take<int32_t>(d->batch);
   w.lse_t_row = c.take<float>(d->batch);
   w.bytes = align_up(c.off, 256);
   return w;
 }
 
+int resid_slices(const dspark_dims* d, bool mfma) {
+  return mfma ? mfma_grid(d->vocab, d->batch, kModeResid) : row_slices(d->vocab, d->batch).count;
+}
+
 }  // namespace
 
+// Target rows are streamed in slices of 8192 entries (32 KB per workgroup item).
+constexpr int kVerifySlice = 8192;
+
 size_t dspark_verify_workspace(const dspark_dims* d) {
-  const RowSlices rs = stream_slices(d->vocab, (long long)d->batch * (d->gamma + 1));
-  return verify_ws(d, rs.count, nullptr).bytes;
+  const int ns = (d->vocab + kVerifySlice - 1) / kVerifySlice;
+  const int nr = std::max(resid_slices(d, true), resid_slices(d, false));
+  return verify_ws(d, ns, nr, nullptr).bytes;
 }
 
 extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, const void* W1,
@@ -229,41 +378,45 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   if (!ws || ws_bytes < dspark_verify_workspace(dm)) return DSPARK_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int B = dm->batch, G = dm->gamma, V = dm->vocab, r = dm->rank;
-  const RowSlices rs = stream_slices(V, (long long)B * (G + 1));
-  VerifyWs w = verify_ws(dm, rs.count, ws);
+  const int nsl = (V + kVerifySlice - 1) / kVerifySlice;
+  const bool mfma = mfma_bias_supported(B, r, wdt);
+  const int nres = resid_slices(dm, mfma);
+  VerifyWs w = verify_ws(dm, nsl, nres, ws);
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
 
-  hipLaunchKernelGGL(k_vfill_u64, dim3((3 * B + 255) / 256), dim3(256), 0, st, w.bonus,
-                     (size_t)3 * B);
-  hipLaunchKernelGGL(k_verify_rows, dim3(rs.count, B, G + 1), dim3(256), 0, st, T, ell, B, G, V,
-                     rs.len, rs.count, invT, key0, key1, w.part, w.bonus);
-  hipLaunchKernelGGL(k_verify_decide, dim3((B + 255) / 256), dim3(256), 0, st, T, tokens, logp,
-                     ell, w.part, w.bonus, B, G, V, rs.count, invT, key0, key1, n_accept,
-                     out_tokens, pt_tok, w.jrow, w.lse_t_row);
-  if (mfma_bias_supported(B, r, wdt)) {
+  hipLaunchKernelGGL(k_vfill_u64, dim3((B + 255) / 256), dim3(256), 0, st, w.bonus, (size_t)B);
+  hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
+                     w.counts);
+  const long long max_items = (long long)B * (G + 1) * nsl;
+  const int grid = (int)std::min<long long>(max_items, 2048);
+  hipLaunchKernelGGL(k_verify_rows, dim3(grid), dim3(256), 0, st, T, ell, w.rows, w.counts, G,
+                     V, kVerifySlice, nsl, invT, key0, key1, w.part, w.bonus);
+  hipLaunchKernelGGL(k_verify_decide, dim3((B + 3) / 4), dim3(256), 0, st, T, tokens, logp, ell,
+                     w.part, w.bonus, B, G, V, nsl, invT, key0, key1, n_accept, out_tokens,
+                     pt_tok, w.jrow, w.lse_t_row);
+  if (mfma) {
     MfmaBiasArgs a{};
     a.mode = kModeResid;
     a.U = U; a.W1 = (const uint16_t*)W1; a.W2t = (const uint16_t*)W2t;
     a.anchor = anchor; a.tokens = tokens; a.T = T; a.lse_d = lse; a.lse_t_row = w.lse_t_row;
-    a.jrow = w.jrow; a.res_best = w.res; a.fb_best = w.fb;
+    a.jrow = w.jrow; a.rpart = w.res_part;
     a.B = B; a.G = G; a.V = V; a.r = r; a.k = 0; a.invT = invT; a.key0 = key0; a.key1 = key1;
     a.ncols = B; a.col0 = 0;
-    if (launch_mfma_bias(a, mfma_grid(V, B), st) != DSPARK_OK) return DSPARK_E_HIP;
+    if (launch_mfma_bias(a, nres, st) != DSPARK_OK) return DSPARK_E_HIP;
   } else {
     const RowSlices rr = row_slices(V, B);
     const size_t sh = sizeof(float) * (r + 256 + 16);
     if (wdt == DSPARK_BF16)
       hipLaunchKernelGGL(k_verify_resid_row<uint16_t>, dim3(rr.count, B), dim3(256), sh, st, U,
                          (const uint16_t*)W1, (const uint16_t*)W2t, T, anchor, tokens, lse,
-                         w.jrow, w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res,
-                         w.fb);
+                         w.jrow, w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_part);
     else
       hipLaunchKernelGGL(k_verify_resid_row<float>, dim3(rr.count, B), dim3(256), sh, st, U,
                          (const float*)W1, (const float*)W2t, T, anchor, tokens, lse, w.jrow,
-                         w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res, w.fb);
+                         w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_part);
   }
-  hipLaunchKernelGGL(k_verify_final, dim3((B + 255) / 256), dim3(256), 0, st, w.jrow, n_accept,
-                     w.res, w.fb, B, G, out_tokens);
+  hipLaunchKernelGGL(k_verify_final, dim3((B + 3) / 4), dim3(256), 0, st, w.jrow, n_accept,
+                     w.res_part, nres, B, G, out_tokens);
   return launch_status();
 }

@@ -25,9 +25,10 @@
  *     return without synchronising.  Arguments are validated on the host first: on any
  *     error a non-zero dspark_status is returned and nothing is enqueued.  Faults inside
  *     kernels surface at the caller's next synchronisation, as usual in HIP.
- *   - Token ids are int32 in [0, V); ids out of range are the caller's error and are not
- *     checked on the device.  Inputs containing NaN give unspecified (but finite-time)
- *     results.
+ *   - Token ids are int32 in [0, V).  Ids out of range are the caller's error; wherever a
+ *     kernel uses an id as an index it is clamped into [0, V), so bad ids never fault.
+ *     Inputs containing NaN give unspecified (but finite-time) results; a draft position
+ *     whose logits are all -inf or NaN reports token -1 and logp NaN.
  *   - Identical inputs give bit-identical outputs (all cross-workgroup reductions have a
  *     fixed order or are order-free).  The calls keep no state between invocations and
  *     may run concurrently on different streams with different workspaces.
