@@ -1,5 +1,21 @@
 // mfma_bias.hip -- batched Markov bias on bf16 MFMA with fused epilogues (see mfma_bias.h).
+//
+// Memory pipeline of one workgroup (NW waves; each wave owns one 32-column block of one
+// 32-row vocab tile per step):
+//   * W2t tiles go HBM -> LDS by DMA (global_load_lds_dwordx4), into a ring of SA stages,
+//     SA-1 steps ahead.  A DMA instruction moves two W2t rows (1 KB); in LDS the two rows
+//     are interleaved by 16-byte chunk and each pair is padded to 1056 bytes, so that the
+//     MFMA A-fragment read of a lane is base + 64*kk (no per-step address arithmetic) and
+//     16 consecutive lanes hit 16 distinct bank groups.
+//   * the base (and target) logit slices are loaded straight into registers in the MFMA
+//     output layout, UD-1 steps ahead; every wave issues the same number of loads each
+//     step (idle lanes read a valid dummy address), so the outstanding-load count that
+//     proves a ring stage has landed is a compile-time constant.
+//   * one barrier per step: after it, stage s is complete for every wave and every wave
+//     is done with stage s-1, which the same step refills.
 #include "mfma_bias.h"
+
+#include <type_traits>
 
 namespace dspark {
 
@@ -7,61 +23,199 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kR = 256;               // Markov rank handled by this path
-constexpr int kKS = kR / 16;          // MFMA k-steps
-constexpr int kRowStride = kR + 8;    // bf16 per LDS row of the gathered W1 (16-byte pad)
+constexpr int kR = 256;                    // Markov rank handled by this path
+constexpr int kKS = kR / 16;               // MFMA k-steps
+constexpr int kPairBytes = 1024 + 32;      // two W2t rows (chunk-interleaved) + pad
+constexpr int kTileBytes = 16 * kPairBytes;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -3.0e38f;   // finite "minus infinity" of the running max
+constexpr float kNegBig = -3.0e38f;        // finite "minus infinity" of the running max
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
+// a ^ b ^ c in one VALU op (gfx950 three-input bit operation, truth table 0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Philox4x32-10 [SALMON] for counters (c0, k, b, s) whose last three words are fixed per
+// lane: the R1 * c2 half of the first round is computed once (PhiloxLane) and the word
+// fed to each call is c0 alone.
+struct PhiloxLane {
+  uint32_t n0;     // round-1 output word 0: hi(R1 * b) ^ k ^ key0
+  uint32_t n1;     // round-1 output word 1: lo(R1 * b)
+  uint32_t x3k1;   // s ^ key1, the other operand of round-1 word 2
+  uint32_t key0, key1;
+};
+
+__device__ __forceinline__ PhiloxLane philox_lane(uint32_t k, uint32_t b, uint32_t s,
+                                                  uint32_t key0, uint32_t key1) {
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * b;
+  PhiloxLane p;
+  p.n0 = (uint32_t)(p1 >> 32) ^ k ^ key0;
+  p.n1 = (uint32_t)p1;
+  p.x3k1 = s ^ key1;
+  p.key0 = key0;
+  p.key1 = key1;
+  return p;
+}
+
+__device__ __forceinline__ U4 philox_call(uint32_t c0, const PhiloxLane& pl) {
+  const uint64_t q0 = (uint64_t)0xD2511F53u * c0;
+  uint32_t x0 = pl.n0, x1 = pl.n1, x2 = (uint32_t)(q0 >> 32) ^ pl.x3k1, x3 = (uint32_t)q0;
+  uint32_t k0 = pl.key0, k1 = pl.key1;
+#pragma unroll
+  for (int round = 1; round < 10; ++round) {
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), x1, k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), x3, k1);
+    x1 = (uint32_t)p1;
+    x3 = (uint32_t)p0;
+    x0 = n0;
+    x2 = n2;
+  }
+  return U4{x0, x1, x2, x3};
+}
+
 // Base-2 Gumbel score offset: -log2(-log2 u) (the common constant -log2(ln 2) is dropped,
-// it shifts every candidate of a race equally).
+// it shifts every candidate of a race equally).  u = (2 (w >> 9) + 1) 2^-24 is formed as
+// the float 1.m with mantissa w >> 9 (one alignbit) minus (1 - 2^-24), which is exact.
 __device__ __forceinline__ float neg_lglg(uint32_t w) {
-  return -lg2(-lg2(word_to_uniform(w)));
+  const float one_m = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+  return -lg2(-lg2(one_m - 0x1.fffffep-1f));
+}
+
+// The W2t ring is filled by LDS DMA issued from inline assembly, and everything that orders
+// it is inline assembly too, so the compiler's own wait-count bookkeeping never sees the
+// DMA: it still counts the ordinary logit loads exactly, and since the DMA only adds to
+// the hardware count, the waits it derives stay sufficient.
+//
+// One global_load_lds_dwordx4: 16 bytes per lane from gbase + voff (saddr form) into LDS
+// at lds + 16 * lane.  M0 carries the LDS address and is restored afterwards.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(gbase)
+      : "memory");
+}
+
+// The same with a per-lane 64-bit source address.
+__device__ __forceinline__ void dma16v(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
+}
+
+// wait until at most N vector-memory operations of this wave are outstanding (loads,
+// including the DMA, complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads() (which would drain every
+// outstanding load).  Each wave waits for its own DMA before it and has consumed its own
+// LDS reads of the previous step; the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// f(step + I, integral_constant<I>, integral_constant<BASE>) for I = I0 .. N-1; BASE >= 0
+// says that step == BASE at compile time, BASE < 0 that it is known at run time only
+template <int I, int N, int BASE, typename F>
+__device__ __forceinline__ void unroll_steps(int step, F& f) {
+  if constexpr (I < N) {
+    f(step + I, std::integral_constant<int, I>{}, std::integral_constant<int, BASE>{});
+    unroll_steps<I + 1, N, BASE>(step, f);
+  }
+}
+
+// the first TRIPS trips of UD steps, with their step numbers known at compile time
+template <int T, int TRIPS, int UD, typename F>
+__device__ __forceinline__ void peel_trips(F& f) {
+  if constexpr (T < TRIPS) {
+    unroll_steps<0, UD, T * UD>(T * UD, f);
+    peel_trips<T + 1, TRIPS, UD>(f);
+  }
 }
 
 template <int NCB, int MODE>
 struct Shape {
-  static constexpr int CBW = NCB >= 4 ? NCB / 4 : 1;     // column blocks per wave
-  static constexpr int NCW = NCB >= 4 ? 4 : NCB;         // distinct column sets
-  static constexpr int TSPLIT = 4 / NCW;                 // tiles per step
+  static constexpr int NCW = NCB;                        // column blocks = waves per tile
+  static constexpr int TSPLIT = NCB >= 4 ? 1 : 4 / NCB;  // tiles per step
+  static constexpr int NW = NCW * TSPLIT;                // waves per workgroup
+  static constexpr int NT = 64 * NW;
   static constexpr int NC = NCB * 32;                    // columns
   static constexpr bool HAS_T = MODE != kModeDraft;
-  static constexpr int kUStride = 36;                    // floats per staged logit row
-  static constexpr int kARows = TSPLIT * 32;             // staged W2t rows per step
-  static constexpr int kURows = TSPLIT * NC;             // staged logit rows per step
-  static constexpr int kAChunks = kARows * (kR / 8);     // 16-byte chunks
-  static constexpr int kUChunks = kURows * 8;
-  static constexpr int kAPer = kAChunks / 256;
-  static constexpr int kUPer = kUChunks / 256;
-  // LDS byte offsets
-  static constexpr size_t kOffA = 0;
-  static constexpr size_t kOffU = kOffA + (size_t)kARows * kRowStride * 2;
-  static constexpr size_t kOffT = kOffU + (size_t)kURows * kUStride * 4;
-  static constexpr size_t kOffMeta = kOffT + (HAS_T ? (size_t)kURows * kUStride * 4 : 0);
+  static constexpr int SA = NCB == 4 ? 4 : (NCB == 8 ? 6 : 2);   // W2t ring stages
+  static constexpr int UD = HAS_T ? 2 : 3;                       // logit register buffers
+  static constexpr int WG_PER_CU = (NCB == 4 || NCB == 2) ? 2 : 1;
+  static constexpr int kStage = TSPLIT * kTileBytes;
+  static constexpr int NA = TSPLIT * 16 / NW;            // DMA instructions per wave per step
+  static constexpr int NU = HAS_T ? 8 : 4;               // logit loads per wave per step
+  // The stage of step s is waited for at step s.  A stage issued inside the loop (at step
+  // s-SA+1) is followed by the loads of the SA-2 steps after that one (every step issues
+  // NA + NU), so once at most that many are outstanding it has landed.
+  static constexpr int kWaitSS = (SA - 2) * (NA + NU);
+  // The gathered W1 rows of the columns are staged in the ring (same pair layout) before
+  // the ring is used, when they fit.
+  static constexpr bool kW1Staged = (size_t)(NC / 2) * kPairBytes <= (size_t)SA * kStage;
+  // Before the loop the stages of steps 0..SA-2 and the logit slices of steps 0..UD-2 are
+  // issued in the order they are needed: stage p, then slice p, for p = 0, 1, ...  The
+  // loads after the stage of such an early step p, up to its wait: the rest of that
+  // sequence and the loads of steps 0..p-1.
+  static constexpr int PRE = SA - 1 > UD - 1 ? SA - 1 : UD - 1;
+  static constexpr int early_after(int p) {
+    int n = p < UD - 1 ? NU : 0;
+    for (int q = p + 1; q < PRE; ++q) n += (q < SA - 1 ? NA : 0) + (q < UD - 1 ? NU : 0);
+    return n + p * (NA + NU);
+  }
+  static constexpr int kPeelTrips = (SA - 1 + UD - 1) / UD;
+  static constexpr int wait_early(int p) {
+    return early_after(p) < kWaitSS ? early_after(p) : kWaitSS;
+  }
+  static constexpr size_t kOffMeta = (size_t)SA * kStage;
   static constexpr size_t kMetaBytes = (size_t)NC * (8 + 8 + 4 + 4 + 4 + 4 + 4);
   static constexpr size_t kRed = (size_t)TSPLIT * NC * 4 * 4;
   static constexpr size_t kLds = kOffMeta + kMetaBytes;
-  static_assert(kAChunks % 256 == 0 && kUChunks % 256 == 0, "chunk split");
-  static_assert(kRed <= kOffMeta, "reduction scratch reuses the staging area");
+  static_assert(TSPLIT * 16 % NW == 0, "DMA split");
+  static_assert(kRed <= kOffMeta, "reduction scratch reuses the ring");
+  static_assert(kLds * WG_PER_CU <= 160 * 1024, "LDS budget");
+  static_assert(kWaitSS < 64, "vmcnt range");
 };
 
-template <int NCB, int MODE>
-__global__ __launch_bounds__(256, (NCB > 4 ? 1 : 2)) void
+template <int NCB> constexpr int kThreads = Shape<NCB, kModeDraft>::NT;
+template <int NCB> constexpr int kWgPerCu = Shape<NCB, kModeDraft>::WG_PER_CU;
+
+// VEC4: V % 4 == 0, so every 4-row run of a logit row is one aligned 16-byte load
+template <int NCB, int MODE, bool VEC4>
+__global__ __launch_bounds__(kThreads<NCB>, kWgPerCu<NCB>) void
 k_mfma_bias(const MfmaBiasArgs a) {
   using S = Shape<NCB, MODE>;
-  constexpr int CBW = S::CBW, NCW = S::NCW, TSPLIT = S::TSPLIT, NC = S::NC;
+  constexpr int NCW = S::NCW, TSPLIT = S::TSPLIT, NC = S::NC, SA = S::SA, UD = S::UD;
+  constexpr int NT = S::NT, NW = S::NW;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* sA = reinterpret_cast<uint16_t*>(smem + S::kOffA);     // [kARows][kRowStride]
-  float* sU = reinterpret_cast<float*>(smem + S::kOffU);           // [kURows][kUStride]
-  float* sT = reinterpret_cast<float*>(smem + S::kOffT);
   long long* col_urow = reinterpret_cast<long long*>(smem + S::kOffMeta);   // [NC]
   long long* col_trow = col_urow + NC;
   int* col_b = reinterpret_cast<int*>(col_trow + NC);
@@ -69,15 +223,41 @@ k_mfma_bias(const MfmaBiasArgs a) {
   int* col_prev = col_k + NC;
   float* col_ld = reinterpret_cast<float*>(col_prev + NC);
   float* col_lt = col_ld + NC;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n32 = lane & 31;
   const int cb0 = wave % NCW, toff = wave / NCW;
   const int G = a.G, V = a.V;
   const float s2 = a.invT * kLog2e;   // logit -> base-2 scale
-  const bool vec4 = (V & 3) == 0;
 
+  // ---- this workgroup's contiguous range of 32-row vocab tiles, TSPLIT per step
+  const int ntiles = (V + 31) >> 5;
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int per = ntiles / nwg, rem = ntiles % nwg;
+  const int t0 = wg * per + min(wg, rem);
+  const int t1 = t0 + per + (wg < rem ? 1 : 0);
+  const int nsteps = (t1 - t0 + TSPLIT - 1) / TSPLIT;
+
+  // ---- W2t ring: DMA of step `step` into stage step % SA.  Lane l of instruction j moves
+  // chunk l>>1 (16 bytes) of stage row 2j + (l&1); rows past V repeat row V-1.  A step past
+  // the last one issues the same instructions on one cached line (its stage is never read
+  // again), which keeps the per-step load count constant.
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+  auto issue_dma = [&](int step) {
+    const int row0 = (t0 + step * TSPLIT) * 32;
+    const uint32_t stage = ring_lds + (uint32_t)((step % SA) * S::kStage);
+    const bool dummy = step >= nsteps;
+    const uint16_t* gbase = dummy ? a.W2t : a.W2t + (size_t)row0 * kR;
+#pragma unroll
+    for (int i = 0; i < S::NA; ++i) {
+      const int j = wave + NW * i;
+      const int row = min(row0 + 2 * j + (lane & 1), V - 1) - row0;   // >= 0: row0 < V
+      const uint32_t voff = dummy ? 0u : (uint32_t)(row * kR * 2 + (lane >> 1) * 16);
+      dma16(gbase, voff, stage + (uint32_t)(j * kPairBytes));
+    }
+  };
   // ---- column metadata: request, position, conditioning token, logit row offsets, lse
-  for (int c = tid; c < NC; c += 256) {
+  for (int c = tid; c < NC; c += NT) {
     int b = -1, k = 0, prev = 0;
     float ld = 0.f, lt = 0.f;
     if (c < a.ncols) {
@@ -113,242 +293,217 @@ k_mfma_bias(const MfmaBiasArgs a) {
     col_urow[c] = b >= 0 ? ((long long)b * G + (k - 1)) * V : -1;
     col_trow[c] = b >= 0 ? ((long long)b * (G + 1) + (k - 1)) * V : -1;
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  // ---- this workgroup's contiguous range of 32-row vocab tiles, TSPLIT per step
-  const int ntiles = (V + 31) >> 5;
-  const int nwg = gridDim.x, wg = blockIdx.x;
-  const int per = ntiles / nwg, rem = ntiles % nwg;
-  const int t0 = wg * per + min(wg, rem);
-  const int t1 = t0 + per + (wg < rem ? 1 : 0);
-  const int nsteps = (t1 - t0 + TSPLIT - 1) / TSPLIT;
-
-  // ---- staging: coalesced global loads of a step's tiles into registers, then LDS
-  u32x4_t RA[S::kAPer];
-  f32x4_t RU[S::kUPer], RT[S::HAS_T ? S::kUPer : 1];
-  auto stage_load = [&](int step) {
+  // ---- this lane's column; its gathered W1 row is the MFMA B operand (idle lanes gather
+  // row 0 and are never reported)
+  const int col = cb0 * 32 + n32;
+  const int cb = col_b[col], ck = col_k[col];
+  const float cld = col_ld[col], clt = col_lt[col];
+  const long long curow = col_urow[col], ctrow = col_trow[col];
+  // ---- logit slices in the MFMA output layout: lane rows 8g + 4h + j of the tile
+  f32x4_t Ub[UD][4], Tb[S::HAS_T ? UD : 1][4];
+  auto load_logits = [&](int step, f32x4_t (&u)[4], f32x4_t (&tt)[4]) {
+    const int t = t0 + step * TSPLIT + toff;
+    const bool live = cb >= 0 && t < t1;       // else one valid dummy address per load
+    if (VEC4) {
+      const int vb = t * 32 + 4 * h;
 #pragma unroll
-    for (int i = 0; i < S::kAPer; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk / (kR / 8), col = chunk % (kR / 8);
-      const int v = min((t0 + step * TSPLIT) * 32 + row, V - 1);   // tile-major rows
-      RA[i] = *reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)v * kR + col * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < S::kUPer; ++i) {
-      const int chunk = tid + 256 * i;
-      const int ur = chunk >> 3, p = chunk & 7;
-      const int tl = ur / NC, c = ur % NC;
-      const int v = (t0 + step * TSPLIT + tl) * 32 + 4 * p;
-      const long long uo = col_urow[c];
-      f32x4_t qu = {0.f, 0.f, 0.f, 0.f}, qt = {0.f, 0.f, 0.f, 0.f};
-      if (uo >= 0) {
-        if (vec4) {
-          if (v < V) {
-            qu = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(a.U + uo + v));
-            if (S::HAS_T)
-              qt = __builtin_nontemporal_load(
-                  reinterpret_cast<const f32x4_t*>(a.T + col_trow[c] + v));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (v + j < V) {
-              qu[j] = a.U[uo + v + j];
-              if (S::HAS_T) qt[j] = a.T[col_trow[c] + v + j];
-            }
+      for (int g = 0; g < 4; ++g) {
+        const int v = min(vb + 8 * g, V - 4);
+        const float* pu = live ? a.U + curow + v : a.U;
+        u[g] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pu));
+        if (S::HAS_T) {
+          const float* pt = live ? a.T + ctrow + v : a.T;
+          tt[g] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pt));
         }
       }
-      RU[i] = qu;
-      if (S::HAS_T) RT[i] = qt;
-    }
-  };
-  auto stage_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < S::kAPer; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk / (kR / 8), col = chunk % (kR / 8);
-      *reinterpret_cast<u32x4_t*>(sA + row * kRowStride + col * 8) = RA[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::kUPer; ++i) {
-      const int chunk = tid + 256 * i;
-      const int ur = chunk >> 3, p = chunk & 7;
-      *reinterpret_cast<f32x4_t*>(sU + ur * S::kUStride + 4 * p) = RU[i];
-      if (S::HAS_T) *reinterpret_cast<f32x4_t*>(sT + ur * S::kUStride + 4 * p) = RT[i];
-    }
-  };
-
-  if (nsteps > 0) stage_load(0);   // first tiles in flight before the dependent gathers
-
-  // ---- this lane's column in each owned block; gathered W1 row = MFMA B operand
-  int cbb[CBW], cbk[CBW];
-  float cbld[CBW], cblt[CBW];
-  uint4 Bop[CBW][kKS];
-#pragma unroll
-  for (int q = 0; q < CBW; ++q) {
-    const int c = (cb0 + 4 * q) * 32 + n32;
-    cbb[q] = col_b[c];
-    cbk[q] = col_k[c];
-    cbld[q] = col_ld[c];
-    cblt[q] = col_lt[c];
-    const uint16_t* wrow = a.W1 + (size_t)col_prev[c] * kR + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < kKS; ++kk)
-      Bop[q][kk] = cbb[q] >= 0 ? *reinterpret_cast<const uint4*>(wrow + kk * 16)
-                               : make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  // per-lane running state of the lane's column in each owned block
-  float st_m[CBW], st_l[CBW], st_s[CBW], st_s2[CBW];
-  uint32_t st_v[CBW], st_v2[CBW];
-#pragma unroll
-  for (int q = 0; q < CBW; ++q) {
-    st_m[q] = kNegBig;
-    st_l[q] = 0.f;
-    st_s[q] = -INFINITY;
-    st_s2[q] = -INFINITY;
-    st_v[q] = 0xFFFFFFFFu;
-    st_v2[q] = 0xFFFFFFFFu;
-  }
-
-  if (nsteps > 0) stage_store();
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const bool more = step + 1 < nsteps;
-    if (more) stage_load(step + 1);            // in flight while this step computes
-    const int t = t0 + step * TSPLIT + toff;
-    const bool active = t < t1;                // wave-uniform
-    const bool full = (t + 1) * 32 <= V;       // every row of this tile is a vocab entry
-    const int vrow = t * 32 + 4 * h;           // first row of this lane's runs
-    const uint16_t* At = sA + (toff * 32 + n32) * kRowStride + 8 * h;
-#pragma unroll
-    for (int q = 0; q < CBW; ++q) {
-      const int b = cbb[q];
-      if (!active) continue;
-      f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                      0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) {
-        const uint4 av = *reinterpret_cast<const uint4*>(At + kk * 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(Bop[q][kk]), acc,
-                                                      0, 0, 0);
-      }
-      if (b < 0) continue;
-      const int k = cbk[q];
-      const int ur = toff * NC + (cb0 + 4 * q) * 32 + n32;   // staged logit row
-      f32x4_t uq[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        uq[g] = *reinterpret_cast<const f32x4_t*>(sU + ur * S::kUStride + 8 * g + 4 * h);
-      // base-2 logits of the 16 rows; rows past V become -inf
-      float z[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z[4 * g + j] = (uq[g][j] + acc[4 * g + j]) * s2;
-      if (!full) {   // wave-uniform: only the last tile of the vocabulary is partial
+      if (__builtin_expect((t + 1) * 32 > V, 0)) {
+        // the vocabulary's last tile: a whole run lies past V (V % 4 == 0); its logits
+        // become -inf, which removes it from the max, the sums and every race
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (vrow + 8 * g + j >= V) z[4 * g + j] = -INFINITY;
+          if (vb + 8 * g >= V) {
+            u[g] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (S::HAS_T) tt[g] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          }
       }
-      if (MODE == kModeDraft) {
-        float mx = z[0];
+    } else {
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, z[i]);
-        const float mnew = fmaxf(st_m[q], mx);
-        float l = st_l[q] * ex2(st_m[q] - mnew);
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) l += ex2(z[i] - mnew);
-        st_m[q] = mnew;
-        st_l[q] = l;
-        float bs = st_s[q];
-        uint32_t bvx = st_v[q];
+        for (int j = 0; j < 4; ++j) {
+          const int v = t * 32 + 8 * g + 4 * h + j;
+          const int vc = min(v, V - 1);
+          u[g][j] = v >= V ? -INFINITY : (live ? a.U[curow + vc] : 0.f);
+          if (S::HAS_T) tt[g][j] = v >= V ? -INFINITY : (live ? a.T[ctrow + vc] : 0.f);
+        }
+    }
+  };
+  u32x4_t Bop[kKS];
+  if constexpr (S::kW1Staged) {
+    // whole 512-byte rows by DMA (full cache lines, unlike 32-byte pieces of 32 rows per
+    // instruction), two rows per instruction in the pair layout, then the fragments from
+    // LDS: B row n32, chunk 2kk + h
+#pragma unroll
+    for (int i = 0; i < NC / 2 / NW; ++i) {
+      const int j = wave + NW * i;
+      const uint16_t* src = a.W1 + (size_t)col_prev[2 * j + (lane & 1)] * kR + (lane >> 1) * 8;
+      dma16v(src, ring_lds + (uint32_t)(j * kPairBytes));
+    }
+    wait_vm<0>();
+    barrier_no_fence();
+    const unsigned char* Bl = smem + (col >> 1) * kPairBytes + (2 * h + (col & 1)) * 16;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) Bop[kk] = *reinterpret_cast<const u32x4_t*>(Bl + kk * 64);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // ring free again
+  } else {
+    const uint16_t* wrow = a.W1 + (size_t)col_prev[col] * kR + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) Bop[kk] = *reinterpret_cast<const u32x4_t*>(wrow + kk * 16);
+  }
+
+  const PhiloxLane pl = philox_lane((uint32_t)ck, (uint32_t)(cb < 0 ? 0 : cb),
+                                    MODE == kModeResid ? 2u : 0u, a.key0, a.key1);
+
+  // the first stages and logit slices, in the order they are needed
+#pragma unroll
+  for (int p = 0; p < S::PRE; ++p) {
+    if (p < SA - 1) issue_dma(p);
+    if (p < UD - 1) load_logits(p, Ub[p], Tb[S::HAS_T ? p : 0]);
+  }
+
+  // per-lane running state of the lane's column
+  float st_m = kNegBig, st_l = 0.f, st_s = -INFINITY, st_s2 = -INFINITY;
+  uint32_t st_v = 0xFFFFFFFFu, st_v2 = 0xFFFFFFFFu;
+
+  // lane's A-fragment base within a stage: row n32 of tile toff, chunk 2kk + h
+  const int a_lane = toff * kTileBytes + (n32 >> 1) * kPairBytes + (2 * h + (n32 & 1)) * 16;
+
+  auto step_body = [&](int step, auto bufc, auto basec) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int BASE = decltype(basec)::value;   // >= 0: step == BASE + BUF
+    constexpr int NXT = (BUF + UD - 1) % UD;
+    // stage `step` complete for this wave, then for all; stage step-1 free for reuse
+    if constexpr (!VEC4) {
+      wait_vm<0>();
+    } else if constexpr (BASE >= 0 && BASE + BUF < SA - 1) {
+      wait_vm<S::wait_early(BASE + BUF)>();
+    } else {
+      wait_vm<S::kWaitSS>();
+    }
+    barrier_no_fence();
+    issue_dma(step + SA - 1);
+    load_logits(step + UD - 1, Ub[NXT], Tb[S::HAS_T ? NXT : 0]);
+
+    const int t = t0 + step * TSPLIT + toff;
+    if (t >= t1) return;                       // wave-uniform (also every step >= nsteps);
+                                               // idle lanes (cb < 0) compute on zeros and
+                                               // are never reported
+    const unsigned char* At = smem + (size_t)(step % SA) * S::kStage + a_lane;
+    f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                    0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      const u32x4_t av = *reinterpret_cast<const u32x4_t*>(At + kk * 64);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(Bop[kk]), acc,
+                                                    0, 0, 0);
+    }
+    const int vrow = t * 32 + 4 * h;           // first row of this lane's runs
+    // element i = 4g + j of the lane is vocab row vrow + 8g + j (rows past V carry -inf
+    // logits); i increases with the row, so a strict '>' keeps the lowest row on ties
+    auto row_of = [&](int i) { return (uint32_t)(vrow + 8 * (i >> 2) + (i & 3)); };
+    float y[16];                               // unscaled draft logit U + bias
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[4 * g + j] = Ub[BUF][g][j] + acc[4 * g + j];
+    if (MODE == kModeDraft) {
+      float mx = y[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, y[i]);
+      const float mnew = fmaxf(st_m, mx * s2);
+      float l = st_l * ex2(st_m - mnew);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) l += ex2(fmaf(y[i], s2, -mnew));
+      st_m = mnew;
+      st_l = l;
+      float bs = st_s;
+      int bi = -1;                             // best element of this step, if it leads
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const U4 w = philox_call((uint32_t)(t * 8 + 2 * g + h), pl);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = fmaf(y[4 * g + j], s2, neg_lglg(wd[j]));
+          const bool better = sc > bs;
+          bs = better ? sc : bs;
+          bi = better ? 4 * g + j : bi;
+        }
+      }
+      st_s = bs;
+      st_v = bi >= 0 ? row_of(bi) : st_v;
+    } else {
+      float zt[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zt[4 * g + j] = Tb[S::HAS_T ? BUF : 0][g][j] * s2;
+      if (MODE == kModeResid) {
+        float bs = st_s, bs2 = st_s2;
+        int bi = -1, bi2 = -1;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const U4 w = philox10((uint32_t)(t * 8 + 2 * g + h), (uint32_t)k, (uint32_t)b, 0u,
-                                a.key0, a.key1);
+          const U4 w = philox_call((uint32_t)(t * 8 + 2 * g + h), pl);
           const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float sc = z[4 * g + j] + neg_lglg(wd[j]);
+            const int i = 4 * g + j;
+            const float gn = neg_lglg(wd[j]);
+            const float rho = ex2(zt[i] - clt) - ex2(fmaf(y[i], s2, -cld));
+            const float sc = rho > 0.f ? lg2(rho) + gn : -INFINITY;
             const bool better = sc > bs;
             bs = better ? sc : bs;
-            bvx = better ? (uint32_t)(vrow + 8 * g + j) : bvx;
+            bi = better ? i : bi;
+            const float sc2 = zt[i] + gn;
+            const bool better2 = sc2 > bs2;
+            bs2 = better2 ? sc2 : bs2;
+            bi2 = better2 ? i : bi2;
           }
         }
-        st_s[q] = bs;
-        st_v[q] = bvx;
+        st_s = bs;
+        st_v = bi >= 0 ? row_of(bi) : st_v;
+        st_s2 = bs2;
+        st_v2 = bi2 >= 0 ? row_of(bi2) : st_v2;
       } else {
-        const float ld = cbld[q], lt = cblt[q];
-        f32x4_t tq[4];
+        float sum = st_l;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          tq[g] = *reinterpret_cast<const f32x4_t*>(sT + ur * S::kUStride + 8 * g + 4 * h);
-        float zt[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) zt[4 * g + j] = tq[g][j] * s2;
-        if (!full) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (vrow + 8 * g + j >= V) zt[4 * g + j] = -INFINITY;
-        }
-        if (MODE == kModeResid) {
-          float bs = st_s[q], bs2 = st_s2[q];
-          uint32_t bvx = st_v[q], bvx2 = st_v2[q];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const U4 w = philox10((uint32_t)(t * 8 + 2 * g + h), (uint32_t)k, (uint32_t)b, 2u,
-                                  a.key0, a.key1);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int i = 4 * g + j;
-              const float gn = neg_lglg(wd[j]);
-              const float rho = ex2(zt[i] - lt) - ex2(z[i] - ld);
-              const float sc = rho > 0.f ? lg2(rho) + gn : -INFINITY;
-              const bool better = sc > bs;
-              bs = better ? sc : bs;
-              bvx = better ? (uint32_t)(vrow + 8 * g + j) : bvx;
-              const float sc2 = zt[i] + gn;
-              const bool better2 = sc2 > bs2;
-              bs2 = better2 ? sc2 : bs2;
-              bvx2 = better2 ? (uint32_t)(vrow + 8 * g + j) : bvx2;
-            }
-          }
-          st_s[q] = bs;
-          st_v[q] = bvx;
-          st_s2[q] = bs2;
-          st_v2[q] = bvx2;
-        } else {
-          float sum = st_l[q];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum += fminf(ex2(z[i] - ld), ex2(zt[i] - lt));
-          st_l[q] = sum;
-        }
+        for (int i = 0; i < 16; ++i)
+          sum += fminf(ex2(fmaf(y[i], s2, -cld)), ex2(zt[i] - clt));
+        st_l = sum;
       }
     }
-    __syncthreads();                // every wave is done reading this step's tiles
-    if (more) {
-      stage_store();
-      __syncthreads();
-    }
-  }
+  };
+
+  // step 0 waits for everything anyway; draining here (with a wait the compiler sees) lets
+  // the loop start with no prologue load pending in its bookkeeping
+  // UD unconditional bodies per trip (steps past the last compute nothing but still issue
+  // their dummy loads), so that every body sees the same load history; the first trips are
+  // peeled, so the compiler's bookkeeping enters the loop in its steady state
+  // (every early step, whose stage was issued before the loop, falls in a peeled trip)
+  peel_trips<0, S::kPeelTrips, UD>(step_body);
+  for (int step = S::kPeelTrips * UD; step < nsteps; step += UD)
+    unroll_steps<0, UD, -1>(step, step_body);
+  __builtin_amdgcn_s_waitcnt(0);   // dummy DMAs of the last steps have landed
+  __syncthreads();                 // every wave is done with the ring; reuse it below
 
   // ---- merge the two lane halves holding the same column, then the TSPLIT waves that
   // covered disjoint tiles of it, in a fixed order: deterministic
-  float* red = reinterpret_cast<float*>(smem);   // [TSPLIT][NC][4] over the staging area
-#pragma unroll
-  for (int q = 0; q < CBW; ++q) {
-    const int cb = cb0 + 4 * q;
-    float m = st_m[q], l = st_l[q], sc = st_s[q], sc2 = st_s2[q];
-    uint32_t v = st_v[q], v2 = st_v2[q];
+  float* red = reinterpret_cast<float*>(smem);   // [TSPLIT][NC][4] over the ring
+  {
+    float m = st_m, l = st_l, sc = st_s, sc2 = st_s2;
+    uint32_t v = st_v, v2 = st_v2;
     const float om = __shfl_xor(m, 32, kWave);
     const float ol = __shfl_xor(l, 32, kWave);
     const float os = __shfl_xor(sc, 32, kWave);
@@ -365,7 +520,7 @@ k_mfma_bias(const MfmaBiasArgs a) {
     if (os > sc || (os == sc && ov < v)) { sc = os; v = ov; }
     if (os2 > sc2 || (os2 == sc2 && ov2 < v2)) { sc2 = os2; v2 = ov2; }
     if (h == 0) {
-      float* e = red + ((size_t)toff * NC + cb * 32 + n32) * 4;
+      float* e = red + ((size_t)toff * NC + col) * 4;
       if (MODE == kModeDraft) {
         e[0] = m; e[1] = l; e[2] = sc; e[3] = __uint_as_float(v);
       } else if (MODE == kModeResid) {
@@ -376,7 +531,7 @@ k_mfma_bias(const MfmaBiasArgs a) {
     }
   }
   __syncthreads();
-  for (int c = tid; c < a.ncols; c += 256) {
+  for (int c = tid; c < a.ncols; c += NT) {
     const int b = col_b[c];
     if (b < 0) continue;
     if (MODE == kModeDraft) {
@@ -410,18 +565,25 @@ k_mfma_bias(const MfmaBiasArgs a) {
   }
 }
 
-template <int NCB, int MODE>
-static dspark_status launch_t(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
-  const size_t sh = Shape<NCB, MODE>::kLds;
+template <int NCB, int MODE, bool VEC4>
+static dspark_status launch_v(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
+  using S = Shape<NCB, MODE>;
+  const size_t sh = S::kLds;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_mfma_bias<NCB, MODE>,
+    if (hipFuncSetAttribute((const void*)k_mfma_bias<NCB, MODE, VEC4>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) != hipSuccess)
       return DSPARK_E_HIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_mfma_bias<NCB, MODE>), dim3(nwg), dim3(256), sh, st, a);
+  hipLaunchKernelGGL((k_mfma_bias<NCB, MODE, VEC4>), dim3(nwg), dim3(S::NT), sh, st, a);
   return launch_status();
+}
+
+template <int NCB, int MODE>
+static dspark_status launch_t(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
+  return (a.V & 3) == 0 ? launch_v<NCB, MODE, true>(a, nwg, st)
+                        : launch_v<NCB, MODE, false>(a, nwg, st);
 }
 
 template <int MODE>
@@ -435,9 +597,10 @@ static dspark_status launch_mode(const MfmaBiasArgs& a, int nwg, hipStream_t st)
 
 int mfma_grid(int V, int ncols, int mode) {
   // one resident wave of workgroups: per-CU occupancy of each variant (registers, LDS)
+  (void)mode;
   const int ntiles = (V + 31) / 32;
   const int ncb = (std::min(ncols, 256) + 31) / 32;
-  const int per_cu = (ncb > 4 || ncb == 1) ? 1 : 2;
+  const int per_cu = (ncb == 2 || (ncb > 2 && ncb <= 4)) ? 2 : 1;
   return std::max(1, std::min(ntiles, per_cu * 256));
 }
 
