@@ -10,9 +10,9 @@ from the round's drafted tokens -- every step re-drafts the identical tokens (sa
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serve128]
 
 Prints one JSON line.  `value` = drafted+verified positions per second = B * gamma / step.
-`roofline` covers the draft (the dominant kernel sequence): algorithmic bytes per call
-(W2t and the base-logit rows, once per position) over the call's average duration,
-measured with HIP events on the launch stream inside the timed region.
+`roofline` covers the dominant kernel, one draft position: its algorithmic bytes (W2t once
+and the B base-logit rows of the position) over its mean launch duration, measured with
+HIP events around each launch on the launch stream in a timed pass of its own.
 `cpu_baseline` times the fp64 oracle on a bounded sample of requests on the host.
 """
 from __future__ import annotations
@@ -148,6 +148,16 @@ def main():
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
         f"draft {draft_ms:.3f} ms")
 
+    # the dominant kernel, one draft position (fused bias MFMA + softmax + Gumbel race):
+    # HIP events around each of its launches on the launch stream, in a pass of its own so
+    # that the events do not perturb the step timing above
+    ds.dspark_profile_start(args.steps * G + 16)
+    for _ in range(args.steps):
+        ds.dspark_draft_markov(U, W1, W2t, anchor, temp, inp.seed, out=(tokens, logp, lse),
+                               ws=ws_d)
+    kern_ms, kern_n = ds.dspark_profile_stop()
+    log(f"draft position kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches")
+
     # algorithmic bytes (what the method must move), from this round's realised ell, n
     ell_h = ell.cpu().numpy().astype(np.int64)
     n_h = nacc.cpu().numpy().astype(np.int64)
@@ -160,7 +170,9 @@ def main():
     step_bytes = draft_bytes + conf_bytes + verify_bytes + tv_bytes
     positions = B * G
     value = positions / (ms_step * 1e-3)
-    achieved = draft_bytes / (draft_ms * 1e-3) / 1e9
+    pos_bytes = w2t_bytes + B * V * 4          # one position: W2t once, B base-logit rows
+    achieved = pos_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name)
 
     rec = {
         "metric": METRIC,
@@ -183,17 +195,19 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "draft: gamma launches of the fused MFMA bias + softmax + Gumbel kernel "
-                      "(+ init and merge), per dspark_draft_markov call",
+            "kernel": "k_mfma_bias<4, draft>: one draft position (bias MFMA + softmax + "
+                      "Gumbel race over W2t and the B base-logit rows)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "bytes_per_launch": draft_bytes,
-            "ms_per_launch": round(draft_ms, 4),
+            "traffic": traffic,
+            "bytes_per_launch": pos_bytes,
+            "ms_per_launch": round(kern_ms, 5),
+            "launches": kern_n,
         },
+        "draft_call_ms": round(draft_ms, 4),
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
         "accepted_mean": round(float(n_h.mean()), 3),
@@ -203,6 +217,27 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch of the draft position kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None when
+    there is none for this workload or the kernel source has changed since it was taken."""
+    import hashlib
+    import re
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"draft_position_{workload_name}_pmc.md")
+    src = os.path.join(here, "draft_verify_sampling_step_amd", "csrc", "mfma_bias.hip")
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic bytes per launch:\s*([0-9]+)", text)
+    if not (m_sha and m_b):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return int(m_b.group(1))
 
 
 def cpu_baseline(inp, budget_s: float):

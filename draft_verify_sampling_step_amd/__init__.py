@@ -77,8 +77,12 @@ def lib() -> ctypes.CDLL:
             L.dspark_rng_uniforms.argtypes = [_U64, ctypes.c_uint32, ctypes.c_uint32,
                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
                                               _P, _P]
+            L.dspark_profile_start.argtypes = [_I]
+            L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(_I)]
             for fn in ("dspark_draft_markov", "dspark_confidence", "dspark_schedule",
-                       "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms"):
+                       "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
+                       "dspark_profile_start", "dspark_profile_stop"):
                 getattr(L, fn).restype = _I
             _lib = L
     return _lib
@@ -267,6 +271,19 @@ def dspark_rng_uniforms(seed: int, b: int, k: int, s: int, v0: int, n: int, devi
     _check(lib().dspark_rng_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, b, k, s, v0, n, _ptr(out),
                                      _stream_handle(stream)))
     return out
+
+
+def dspark_profile_start(max_launches: int = 4096):
+    """Start timing every per-position draft kernel with HIP events (measurement only)."""
+    _check(lib().dspark_profile_start(int(max_launches)))
+
+
+def dspark_profile_stop():
+    """(mean milliseconds, launches) of the draft kernels timed since dspark_profile_start."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    _check(lib().dspark_profile_stop(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------------------------

@@ -1,5 +1,7 @@
-// api.hip -- library-wide entry points: workspace sizes, status names, version, and the
-// generator check hook dspark_rng_uniforms.
+// api.hip -- library-wide entry points: workspace sizes, status names, version, the
+// generator check hook dspark_rng_uniforms and the launch-timing switch.
+#include <vector>
+
 #include "dspark_dev.h"
 #include "dspark_host.h"
 
@@ -20,9 +22,53 @@ __global__ void k_rng_uniforms(uint32_t key0, uint32_t key1, uint32_t b, uint32_
   }
 }
 
+// Launch timing: while enabled, the draft records a HIP event pair around each of its
+// per-position kernels on the caller's stream (measurement only; not thread-safe).
+namespace {
+bool g_prof_on = false;
+int g_prof_n = 0;
+std::vector<hipEvent_t> g_prof_ev;
+}  // namespace
+
+void prof_mark(hipStream_t st) {
+  if (!g_prof_on || g_prof_n >= (int)g_prof_ev.size()) return;
+  (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
+}
+
 }  // namespace dspark
 
 using namespace dspark;
+
+extern "C" dspark_status dspark_profile_start(int max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 16)) return DSPARK_E_VALUE;
+  const size_t need = 2 * (size_t)max_launches;
+  while (g_prof_ev.size() < need) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return DSPARK_E_HIP;
+    g_prof_ev.push_back(e);
+  }
+  g_prof_n = 0;
+  g_prof_on = true;
+  return DSPARK_OK;
+}
+
+extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches) {
+  if (!mean_ms || !launches) return DSPARK_E_NULL;
+  g_prof_on = false;
+  const int pairs = g_prof_n / 2;
+  double total = 0.0;
+  for (int i = 0; i < pairs; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof_ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof_ev[2 * i], g_prof_ev[2 * i + 1]) != hipSuccess)
+      return DSPARK_E_HIP;
+    total += ms;
+  }
+  *launches = pairs;
+  *mean_ms = pairs ? total / pairs : 0.0;
+  g_prof_n = 0;
+  return DSPARK_OK;
+}
 
 extern "C" size_t dspark_workspace_bytes(int op, const dspark_dims* d) {
   switch (op) {

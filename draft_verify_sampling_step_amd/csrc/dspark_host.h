@@ -48,6 +48,9 @@ inline int mfma_workgroups(int V) {
   return tiles < 1024 ? tiles : 1024;
 }
 
+// Records the next launch-timing event on `st` while timing is enabled (api.hip).
+void prof_mark(hipStream_t st);
+
 inline dspark_status launch_status() {
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_E_HIP;
 }

@@ -198,6 +198,19 @@ dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, con
 dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t k, uint32_t s,
                                   uint32_t v0, int64_t n, float* out, void* stream);
 
+/*
+ * Launch timing (measurement support, not part of the method).  Between
+ * dspark_profile_start and dspark_profile_stop every per-position kernel of
+ * dspark_draft_markov is bracketed by a pair of HIP events on the call's stream, for at
+ * most max_launches launches (1..65536; events are created on the first call and kept).
+ * dspark_profile_stop waits for the recorded events and returns the mean duration of the
+ * bracketed launches in milliseconds and their count.  Not thread-safe; meant for one
+ * timing loop at a time.  Errors: DSPARK_E_VALUE (max_launches out of range),
+ * DSPARK_E_NULL, DSPARK_E_HIP (event creation or timing failed).
+ */
+dspark_status dspark_profile_start(int max_launches);
+dspark_status dspark_profile_stop(double* mean_ms, int* launches);
+
 #ifdef __cplusplus
 }
 #endif

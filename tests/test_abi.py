@@ -101,3 +101,11 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(ds, "LIB_PATH", "/nonexistent/libdspark.so")
     with pytest.raises(RuntimeError, match="missing"):
         ds.lib()
+
+
+def test_profile_switch_validation():
+    import ctypes
+    L = ds.lib()
+    assert L.dspark_profile_start(0) == 4            # DSPARK_E_VALUE, no HIP call made
+    assert L.dspark_profile_start(1 << 17) == 4
+    assert L.dspark_profile_stop(None, None) == 1    # DSPARK_E_NULL
