@@ -155,8 +155,9 @@ def main():
     for _ in range(args.steps):
         ds.dspark_draft_markov(U, W1, W2t, anchor, temp, inp.seed, out=(tokens, logp, lse),
                                ws=ws_d)
-    kern_ms, kern_n = ds.dspark_profile_stop()
-    log(f"draft position kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches")
+    kern_ms, kern_n, kern_pos = ds.dspark_profile_stop()
+    log(f"draft sampling kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches of "
+        f"{kern_pos:g} positions each")
 
     # algorithmic bytes (what the method must move), from this round's realised ell, n
     ell_h = ell.cpu().numpy().astype(np.int64)
@@ -171,7 +172,8 @@ def main():
     positions = B * G
     value = positions / (ms_step * 1e-3)
     pos_bytes = w2t_bytes + B * V * 4          # one position: W2t once, B base-logit rows
-    achieved = pos_bytes / (kern_ms * 1e-3) / 1e9
+    launch_bytes = int(round(pos_bytes * kern_pos))
+    achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg.name)
 
     rec = {
@@ -195,15 +197,16 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "k_mfma_bias<4, draft>: one draft position (bias MFMA + softmax + "
-                      "Gumbel race over W2t and the B base-logit rows)",
+            "kernel": "k_mfma_bias<4, draft>: fused bias MFMA + softmax + Gumbel race over "
+                      "W2t and the B base-logit rows, for the draft positions of one launch",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "bytes_per_launch": pos_bytes,
+            "bytes_per_launch": launch_bytes,
+            "positions_per_launch": kern_pos,
             "ms_per_launch": round(kern_ms, 5),
             "launches": kern_n,
         },

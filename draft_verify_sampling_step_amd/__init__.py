@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
                                               _P, _P]
             L.dspark_profile_start.argtypes = [_I]
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
-                                              ctypes.POINTER(_I)]
+                                              ctypes.POINTER(_I),
+                                              ctypes.POINTER(ctypes.c_double)]
             for fn in ("dspark_draft_markov", "dspark_confidence", "dspark_schedule",
                        "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
                        "dspark_profile_start", "dspark_profile_stop"):
@@ -279,11 +280,13 @@ def dspark_profile_start(max_launches: int = 4096):
 
 
 def dspark_profile_stop():
-    """(mean milliseconds, launches) of the draft kernels timed since dspark_profile_start."""
+    """(mean milliseconds, launches, positions per launch) of the draft sampling kernels
+    timed since dspark_profile_start."""
     ms = ctypes.c_double()
     n = ctypes.c_int()
-    _check(lib().dspark_profile_stop(ctypes.byref(ms), ctypes.byref(n)))
-    return ms.value, n.value
+    pos = ctypes.c_double()
+    _check(lib().dspark_profile_stop(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(pos)))
+    return ms.value, n.value, pos.value
 
 
 # ------------------------------------------------------------------------------------

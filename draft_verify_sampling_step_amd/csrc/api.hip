@@ -26,13 +26,24 @@ __global__ void k_rng_uniforms(uint32_t key0, uint32_t key1, uint32_t b, uint32_
 // per-position kernels on the caller's stream (measurement only; not thread-safe).
 namespace {
 bool g_prof_on = false;
-int g_prof_n = 0;
+int g_prof_n = 0;              // events recorded (pairs are complete when even)
+long long g_prof_positions = 0;
 std::vector<hipEvent_t> g_prof_ev;
 }  // namespace
 
-void prof_mark(hipStream_t st) {
-  if (!g_prof_on || g_prof_n >= (int)g_prof_ev.size()) return;
+void prof_begin(hipStream_t st) {
+  if (!g_prof_on || g_prof_n + 2 > (int)g_prof_ev.size()) return;
   (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
+}
+
+void prof_end(hipStream_t st, int positions) {
+  if (!g_prof_on || (g_prof_n & 1) == 0) return;
+  if (positions < 0) {   // the launch was refused: drop its begin event
+    --g_prof_n;
+    return;
+  }
+  (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
+  g_prof_positions += positions;
 }
 
 }  // namespace dspark
@@ -48,12 +59,14 @@ extern "C" dspark_status dspark_profile_start(int max_launches) {
     g_prof_ev.push_back(e);
   }
   g_prof_n = 0;
+  g_prof_positions = 0;
   g_prof_on = true;
   return DSPARK_OK;
 }
 
-extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches) {
-  if (!mean_ms || !launches) return DSPARK_E_NULL;
+extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches,
+                                           double* positions_per_launch) {
+  if (!mean_ms || !launches || !positions_per_launch) return DSPARK_E_NULL;
   g_prof_on = false;
   const int pairs = g_prof_n / 2;
   double total = 0.0;
@@ -66,7 +79,9 @@ extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches) {
   }
   *launches = pairs;
   *mean_ms = pairs ? total / pairs : 0.0;
+  *positions_per_launch = pairs ? (double)g_prof_positions / pairs : 0.0;
   g_prof_n = 0;
+  g_prof_positions = 0;
   return DSPARK_OK;
 }
 

@@ -228,11 +228,11 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
       a.part = pk;
       a.B = B; a.G = G; a.V = V; a.r = r; a.k = k; a.invT = invT; a.key0 = key0; a.key1 = key1;
       a.ncols = B;
-      prof_mark(st);
+      prof_begin(st);
       if (launch_mfma_bias(a, plan.nslices, st) != DSPARK_OK) return DSPARK_E_HIP;
-      prof_mark(st);
+      prof_end(st, 1);
     } else {
-      prof_mark(st);
+      prof_begin(st);
       const size_t sh = sizeof(float) * (r + 256 + 16);
       dim3 grid(plan.nslices, B);
       if (wdt == DSPARK_BF16)
@@ -243,7 +243,7 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
         hipLaunchKernelGGL(k_draft_row<float>, grid, dim3(256), sh, st, U, (const float*)W1,
                            (const float*)W2t, anchor, forced, bprev, bcur, pk, B, G, V, r, k,
                            invT, key0, key1, plan.slice_len);
-      prof_mark(st);
+      prof_end(st, 1);
     }
   }
   if (wdt == DSPARK_BF16)

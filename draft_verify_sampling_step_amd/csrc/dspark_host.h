@@ -48,8 +48,11 @@ inline int mfma_workgroups(int V) {
   return tiles < 1024 ? tiles : 1024;
 }
 
-// Records the next launch-timing event on `st` while timing is enabled (api.hip).
-void prof_mark(hipStream_t st);
+// Launch timing (api.hip): while enabled, prof_begin/prof_end bracket one launch with a
+// pair of events on `st`; `positions` is the number of draft positions the launch covered
+// (a negative count withdraws a begin whose launch was refused).
+void prof_begin(hipStream_t st);
+void prof_end(hipStream_t st, int positions);
 
 inline dspark_status launch_status() {
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_E_HIP;

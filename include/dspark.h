@@ -200,16 +200,18 @@ dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t k, uint32_
 
 /*
  * Launch timing (measurement support, not part of the method).  Between
- * dspark_profile_start and dspark_profile_stop every per-position kernel of
- * dspark_draft_markov is bracketed by a pair of HIP events on the call's stream, for at
- * most max_launches launches (1..65536; events are created on the first call and kept).
- * dspark_profile_stop waits for the recorded events and returns the mean duration of the
- * bracketed launches in milliseconds and their count.  Not thread-safe; meant for one
- * timing loop at a time.  Errors: DSPARK_E_VALUE (max_launches out of range),
+ * dspark_profile_start and dspark_profile_stop every launch of the sampling kernel of
+ * dspark_draft_markov (one launch per draft position) is bracketed by a pair of HIP
+ * events on the call's stream, for at most max_launches launches (1..65536; events are
+ * created on the first call and kept).  dspark_profile_stop waits for the recorded events
+ * and returns the mean duration of the bracketed launches in milliseconds, their count,
+ * and the mean number of draft positions one launch covered.  Not thread-safe; meant for
+ * one timing loop at a time.  Errors: DSPARK_E_VALUE (max_launches out of range),
  * DSPARK_E_NULL, DSPARK_E_HIP (event creation or timing failed).
  */
 dspark_status dspark_profile_start(int max_launches);
-dspark_status dspark_profile_stop(double* mean_ms, int* launches);
+dspark_status dspark_profile_stop(double* mean_ms, int* launches,
+                                  double* positions_per_launch);
 
 #ifdef __cplusplus
 }

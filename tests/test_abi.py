@@ -108,4 +108,4 @@ def test_profile_switch_validation():
     L = ds.lib()
     assert L.dspark_profile_start(0) == 4            # DSPARK_E_VALUE, no HIP call made
     assert L.dspark_profile_start(1 << 17) == 4
-    assert L.dspark_profile_stop(None, None) == 1    # DSPARK_E_NULL
+    assert L.dspark_profile_stop(None, None, None) == 1    # DSPARK_E_NULL
