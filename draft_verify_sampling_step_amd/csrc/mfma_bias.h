@@ -66,4 +66,9 @@ int mfma_grid(int V, int ncols, int mode);
 
 dspark_status launch_mfma_bias(const MfmaBiasArgs& a, int nwg, hipStream_t st);
 
+// Draft mode on 16-column waves (mfma16.hip): 65..256 columns, V % 4 == 0; same grid and
+// partial-slot layout as the 32-column kernel.
+bool draft16_supported(const MfmaBiasArgs& a);
+dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st);
+
 }  // namespace dspark

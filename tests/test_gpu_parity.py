@@ -113,6 +113,12 @@ SMALL = {
                                       wsigma=0.1, temperature=0.7, table="serve15"),
     "mfma_b128": workload.custom(B=128, gamma=3, V=2500, r=256, d=64, bf16=True, wsigma=0.1,
                                  logits="peaked_flat", table="serve"),
+    # 16-column-wave draft kernel with idle columns inside the last waves, ragged last tile
+    "mfma_b100_ragged": workload.custom(B=100, gamma=3, V=3004, r=256, d=64, bf16=True,
+                                        wsigma=0.1, logits="zipf", sigma_mix=True,
+                                        table="serve"),
+    "mfma_b200_t07": workload.custom(B=200, gamma=2, V=1100, r=256, d=48, bf16=True,
+                                     wsigma=0.1, temperature=0.7, table="serve15"),
     "mfma_b256": workload.custom(B=256, gamma=2, V=1600, r=256, d=64, bf16=True, wsigma=0.1,
                                  logits="zipf", table="serve"),
     "mfma_b300": workload.custom(B=300, gamma=2, V=1100, r=256, d=32, bf16=True, wsigma=0.1,
