@@ -197,8 +197,9 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "k_mfma_bias<4, draft>: fused bias MFMA + softmax + Gumbel race over "
-                      "W2t and the B base-logit rows, for the draft positions of one launch",
+            "kernel": "k_draft16<8, 1>: fused bias MFMA (16x16x32 bf16, 16-column waves) + "
+                      "softmax + Gumbel race over W2t and the B base-logit rows, one draft "
+                      "position per launch",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -222,6 +223,10 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+# the dominant kernel's source files, hashed in this order (the counter summary names it)
+KERNEL_SOURCES = ("mfma16.hip", "mfma_common.h")
+
+
 def measured_traffic(workload_name: str):
     """HBM bytes per launch of the draft position kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None when
@@ -230,15 +235,19 @@ def measured_traffic(workload_name: str):
     import re
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"draft_position_{workload_name}_pmc.md")
-    src = os.path.join(here, "draft_verify_sampling_step_amd", "csrc", "mfma_bias.hip")
-    if not (os.path.exists(path) and os.path.exists(src)):
+    csrc = os.path.join(here, "draft_verify_sampling_step_amd", "csrc")
+    srcs = [os.path.join(csrc, f) for f in KERNEL_SOURCES]
+    if not (os.path.exists(path) and all(os.path.exists(f) for f in srcs)):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic bytes per launch:\s*([0-9]+)", text)
     if not (m_sha and m_b):
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m_sha.group(1):
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != m_sha.group(1):
         return None
     return int(m_b.group(1))
 

@@ -35,6 +35,14 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return r;
 }
 
+// The same with a wave-uniform third operand read straight from a scalar register (one
+// scalar operand per VALU instruction is allowed), which saves a copy into a VGPR.
+__device__ __forceinline__ uint32_t xor3s(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
 // Philox4x32-10 [SALMON] for counters (c0, k, b, s) whose last three words are fixed per
 // lane: the R1 * c2 half of the first round is computed once (PhiloxLane) and the word
 // fed to each call is c0 alone.
@@ -101,8 +109,8 @@ __device__ __forceinline__ void philox_calls(const uint32_t (&c0)[N], const Phil
     for (int g = 0; g < N; ++g) {
       const uint64_t p0 = (uint64_t)0xD2511F53u * x0[g];
       const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2[g];
-      const uint32_t n0 = xor3((uint32_t)(p1 >> 32), x1[g], k0);
-      const uint32_t n2 = xor3((uint32_t)(p0 >> 32), x3[g], k1);
+      const uint32_t n0 = xor3s((uint32_t)(p1 >> 32), x1[g], k0);
+      const uint32_t n2 = xor3s((uint32_t)(p0 >> 32), x3[g], k1);
       x1[g] = (uint32_t)p1;
       x3[g] = (uint32_t)p0;
       x0[g] = n0;

@@ -18,6 +18,7 @@
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_bias.h"
+#include "mfma_common.h"
 #include "rowbias.h"
 
 namespace dspark {
@@ -66,15 +67,18 @@ __global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__
   }
 }
 
-// Grid-stride over (row, slice) items: split-vocabulary (max, sum-exp) partials of
-// T/temperature; on row ell_b + 1 also the bonus token's Gumbel race.
-__global__ __launch_bounds__(256) void k_verify_rows(
+// Grid-stride over (row, slice) items.  Rows 1..ell_b: split-vocabulary (max, sum-exp)
+// partials of T/temperature (base 2).  Row ell_b + 1 needs no normaliser (only its bonus
+// token is drawn from it): the Gumbel race over it, merged by a 64-bit atomic max.
+__global__ __launch_bounds__(256, 8) void k_verify_rows(
     const float* __restrict__ T, const int32_t* __restrict__ ell,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, int G, int V,
     int slice_len, int nslices, float invT, uint32_t key0, uint32_t key1,
     float2* __restrict__ part, unsigned long long* __restrict__ bonus) {
   __shared__ float red[16];
   const int nitems = counts[1];
+  const float s2 = invT * 1.4426950408889634f;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     const int row = rows[item / nslices], s = item % nslices;
     const int b = row / (G + 1), k = row % (G + 1) + 1;
@@ -82,87 +86,113 @@ __global__ __launch_bounds__(256) void k_verify_rows(
     const bool is_bonus = (k == (Lb < 0 ? 0 : (Lb > G ? G : Lb)) + 1);
     const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
     const float* trow = T + (size_t)row * V;
-    const float s2 = invT * 1.4426950408889634f;
+    if ((V & 3) == 0 && slice_len == 4 * 256 * 8) {
+      // every thread's eight 16-byte loads are issued before any is consumed; entries past
+      // the slice read as -inf
+      constexpr int kQ = 8;
+      f32x4_t q[kQ];
+#pragma unroll
+      for (int i = 0; i < kQ; ++i) {
+        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
+        q[i] = v < v_end ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(trow + v))
+                         : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      if (!is_bonus) {
+        // max first (a finite floor when every entry is padding), then one exponential per
+        // entry
+        float mq = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kQ; ++i)
+          mq = fmaxf(mq, fmaxf(fmaxf(q[i][0], q[i][1]), fmaxf(q[i][2], q[i][3])));
+        float m = fmaxf(mq * s2, -3.0e38f);
+        float lp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kQ; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lp[j] += ex2(fmaf(q[i][j], s2, -m));
+        float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+          const float mn = fmaxf(m, om);
+          l = l * ex2(m - mn) + ol * ex2(om - mn);
+          m = mn;
+        }
+        if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          float mm = red[0], ll = red[4];
+          for (int i = 1; i < 4; ++i) {
+            const float mn = fmaxf(mm, red[i]);
+            ll = ll * ex2(mm - mn) + red[4 + i] * ex2(red[i] - mn);
+            mm = mn;
+          }
+          part[(size_t)row * nslices + s] = make_float2(mm, ll);
+        }
+        __syncthreads();
+      } else {
+        // four consecutive entries share one Philox call (words 0..3); the calls of a
+        // batch run in lockstep
+        const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)b, 2u, key0, key1);
+        Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+#pragma unroll
+        for (int i0 = 0; i0 < kQ; i0 += 4) {
+          uint32_t c0[4], w[4][4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            c0[i] = (uint32_t)((v_begin + 4 * (threadIdx.x + 256 * (i0 + i))) >> 2);
+          philox_calls<4>(c0, pl, w);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float sc = fmaf(q[i0 + i][j], s2, neg_lglg(w[i][j]));
+              if (sc > best.s) best = Cand{sc, 4 * c0[i] + (uint32_t)j, 0.f};
+            }
+        }
+        best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
+        if (threadIdx.x == 0 && best.i != 0xFFFFFFFFu)
+          atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
+      }
+      continue;
+    }
+    // any other vocabulary size: one entry per thread and step, online state
     float m = -3.0e38f, l = 0.f;
     Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
-    auto visit = [&](float t, int v) {
-      const float z = t * s2;
-      const float mn = fmaxf(m, z);
-      l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
-      m = mn;
+    for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
+      const float z = trow[v] * s2;
       if (is_bonus) {
         const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
         const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-        const float sc =
-            z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
+        const float sc = z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
         if (sc > best.s) best = Cand{sc, (uint32_t)v, 0.f};
+      } else {
+        const float mn = fmaxf(m, z);
+        l = l * ex2(m - mn) + ex2(z - mn);
+        m = mn;
       }
-    };
-    if ((V & 3) == 0) {
-      // all of this thread's 16-byte loads are issued before any is consumed
-      constexpr int kQ = 8;   // float4 per thread per 8192-entry slice
-      typedef float f4 __attribute__((ext_vector_type(4)));
-      f4 q[kQ];
+    }
+    if (!is_bonus) {
 #pragma unroll
-      for (int i = 0; i < kQ; ++i) {
-        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
-        q[i] = v < v_end ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(trow + v))
-                         : f4{0.f, 0.f, 0.f, 0.f};
+      for (int o = 32; o > 0; o >>= 1) {
+        const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+        const float mn = fmaxf(m, om);
+        l = l * ex2(m - mn) + ol * ex2(om - mn);
+        m = mn;
       }
-#pragma unroll
-      for (int i = 0; i < kQ; ++i) {
-        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
-        if (v < v_end) {
-          // four consecutive entries share one Philox call (words 0..3)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float z = q[i][j] * s2;
-            const float mn = fmaxf(m, z);
-            l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
-            m = mn;
-          }
-          if (is_bonus) {
-            const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
-            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float sc = q[i][j] * s2 -
-                               __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(wd[j])));
-              if (sc > best.s) best = Cand{sc, (uint32_t)(v + j), 0.f};
-            }
-          }
+      if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float mm = red[0], ll = red[4];
+        for (int i = 1; i < 4; ++i) {
+          const float mn = fmaxf(mm, red[i]);
+          ll = ll * ex2(mm - mn) + red[4 + i] * ex2(red[i] - mn);
+          mm = mn;
         }
+        part[(size_t)row * nslices + s] = make_float2(mm, ll);
       }
-      for (int v = v_begin + 4 * 256 * kQ + 4 * threadIdx.x; v < v_end; v += 1024) {
-        const f4 t4 = *reinterpret_cast<const f4*>(trow + v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) visit(t4[j], v + j);
-      }
+      __syncthreads();
     } else {
-      for (int v = v_begin + threadIdx.x; v < v_end; v += 256) visit(trow[v], v);
-    }
-    // workgroup merge of the base-2 state
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
-      const float mn = fmaxf(m, om);
-      l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
-      m = mn;
-    }
-    if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float mm = red[0], ll = red[4];
-      for (int i = 1; i < 4; ++i) {
-        const float mn = fmaxf(mm, red[i]);
-        ll = ll * __builtin_amdgcn_exp2f(mm - mn) + red[4 + i] * __builtin_amdgcn_exp2f(red[i] - mn);
-        mm = mn;
-      }
-      part[(size_t)row * nslices + s] = make_float2(mm, ll);
-    }
-    __syncthreads();
-    if (is_bonus) {
       best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
       if (threadIdx.x == 0 && best.i != 0xFFFFFFFFu)
         atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
