@@ -114,6 +114,24 @@ k_mfma_bias(const MfmaBiasArgs a) {
       dma16(gbase, voff, stage + (uint32_t)(j * kPairBytes));
     }
   };
+  // ---- residual mode: the requests with a residual row (usually few) are compacted, in
+  // order, to the front of the columns, so that waves whose column block has none skip the
+  // epilogue (they still issue their share of the loads and meet every barrier)
+  int n_live = NC;
+  if constexpr (MODE == kModeResid) {
+    int* clist = reinterpret_cast<int*>(smem);   // [NC] list, [NC] count, [NC+1..] per wave
+    const bool act = tid < a.ncols && a.jrow[a.col0 + tid] > 0;   // NC <= NT
+    const unsigned long long bal = __ballot(act);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) clist[NC + 1 + wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += clist[NC + 1 + w];
+    if (act) clist[off + below] = tid;
+    if (tid == NT - 1) clist[NC] = off + __popcll(bal);
+    __syncthreads();
+    n_live = clist[NC];
+  }
   // ---- column metadata: request, position, conditioning token, logit row offsets, lse
   for (int c = tid; c < NC; c += NT) {
     int b = -1, k = 0, prev = 0;
@@ -127,9 +145,10 @@ k_mfma_bias(const MfmaBiasArgs a) {
                         : (a.forced ? a.forced[(size_t)b * G + (k - 2)]
                                     : (int)packed_index(a.best_prev[b]));
       } else if (MODE == kModeResid) {
-        const int j = a.jrow[gc];
+        const int gr = c < n_live ? a.col0 + reinterpret_cast<const int*>(smem)[c] : gc;
+        const int j = c < n_live ? a.jrow[gr] : 0;
         if (j > 0) {
-          b = gc;
+          b = gr;
           k = j;
           prev = (j == 1) ? a.anchor[b] : a.tokens[(size_t)b * G + (j - 2)];
           ld = a.lse_d[(size_t)b * G + (j - 1)] * kLog2e;
@@ -157,6 +176,7 @@ k_mfma_bias(const MfmaBiasArgs a) {
   // row 0 and are never reported)
   const int col = cb0 * 32 + n32;
   const int cb = col_b[col], ck = col_k[col];
+  const bool wave_live = MODE != kModeResid || cb0 * 32 < n_live;
   const float cld = col_ld[col], clt = col_lt[col];
   const long long curow = col_urow[col], ctrow = col_trow[col];
   // ---- logit slices in the MFMA output layout: lane rows 8g + 4h + j of the tile
@@ -255,7 +275,7 @@ k_mfma_bias(const MfmaBiasArgs a) {
     load_logits(step + UD - 1, Ub[NXT], Tb[S::HAS_T ? NXT : 0]);
 
     const int t = t0 + step * TSPLIT + toff;
-    if (t >= t1) return;                       // wave-uniform (also every step >= nsteps);
+    if (t >= t1 || !wave_live) return;        // wave-uniform (also every step >= nsteps);
                                                // idle lanes (cb < 0) compute on zeros and
                                                // are never reported
     const unsigned char* At = smem + (size_t)(step % SA) * S::kStage + a_lane;
