@@ -4,10 +4,11 @@
 //
 //  1. prefix survival a_{b,j} = prod_{i<=j} c_{b,i}: one thread per request, fp64,
 //     multiplied left to right (the same rounding sequence as the plain definition);
-//  2. all (b, j) candidates sorted by (a descending, b ascending, j ascending) with a
-//     bitonic network over keys held in registers (pairs within a wave exchange by lane
-//     shuffles, pairs across waves through LDS) -- the key (a, b*gamma + j - 1) is a
-//     total order;
+//  2. all (b, j) candidates put in order by (a descending, b ascending, j ascending) --
+//     the key (a, b*gamma + j - 1) is a total order.  Each request's run of gamma is in
+//     order already (its prefix products never increase when every c <= 1; a run that is
+//     not is sorted by insertion), so adjacent runs are merged level by level in LDS,
+//     every output slot locating its source with a merge-path binary search;
 //  3. the greedy walk: tau accumulates in fp64 in sorted order (a sequential chain, the
 //     plain definition's rounding); the stop tests of 64 candidates at a time run in
 //     parallel on one wave; the walk stops at the first candidate that does not raise
@@ -19,82 +20,33 @@
 
 namespace dspark {
 
-__device__ __forceinline__ bool sched_before(double a1, uint32_t i1, double a2, uint32_t i2) {
-  return a1 > a2 || (a1 == a2 && i1 < i2);
-}
-
-// One candidate key of the sort: (a, index), ordered by sched_before.
+// One candidate of the order: (a, index) with index = b * gamma + j - 1; 16 bytes in LDS.
 struct SKey {
   double a;
   uint32_t i;
+  uint32_t pad;
 };
 
-__device__ __forceinline__ SKey shfl_xor_key(const SKey& k, int m) {
-  SKey o;
-  o.a = __shfl_xor(k.a, m, kWave);
-  o.i = (uint32_t)__shfl_xor((int)k.i, m, kWave);
-  return o;
+// the scheduler's total order: a descending, then index ascending (indices are distinct)
+__device__ __forceinline__ bool sched_before(const SKey& x, const SKey& y) {
+  return x.a > y.a || (x.a == y.a && x.i < y.i);
 }
 
-// Compare-exchange of positions p (mine) and p ^ stride (the partner's key `o`) of a bitonic
-// network: the lower position of a pair keeps the earlier key when the block of `size`
-// sorts up, the later one when it sorts down; the higher position keeps the other.
-__device__ __forceinline__ SKey bitonic_pick(const SKey& mine, const SKey& o, int p, int stride,
-                                             int size) {
-  const bool lower = (p & stride) == 0;
-  const bool up = (p & size) == 0;
-  const bool mine_first = sched_before(mine.a, mine.i, o.a, o.i);
-  const bool keep_first = lower == up;
-  return (mine_first == keep_first) ? mine : o;
-}
-
-// KPT keys per thread (positions KPT * tid + e) of a bitonic sort over NP = 1024 * KPT
-// positions: pairs within a thread are exchanged in registers, pairs within a wave by lane
-// shuffles, and only pairs across waves through LDS.
-template <int KPT>
-__device__ void bitonic_sort_regs(SKey (&k)[KPT], double* xa, uint32_t* xi) {
-  constexpr int NP = 1024 * KPT;
-  const int tid = threadIdx.x;
-  for (int size = 2; size <= NP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < KPT) {
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-          const int pe = e ^ stride;
-          if (pe > e) {
-            const int p = KPT * tid + e;
-            const SKey lo = k[e], hi = k[pe];
-            k[e] = bitonic_pick(lo, hi, p, stride, size);
-            k[pe] = bitonic_pick(hi, lo, p ^ stride, stride, size);
-          }
-        }
-      } else if (stride < KPT * kWave) {
-        const int m = stride / KPT;   // partner lane offset within the wave
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-          const SKey o = shfl_xor_key(k[e], m);
-          k[e] = bitonic_pick(k[e], o, KPT * tid + e, stride, size);
-        }
-      } else {
-        __syncthreads();   // the previous exchange's readers are done
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-          xa[KPT * tid + e] = k[e].a;
-          xi[KPT * tid + e] = k[e].i;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-          const int p = KPT * tid + e;
-          const SKey o{xa[p ^ stride], xi[p ^ stride]};
-          k[e] = bitonic_pick(k[e], o, p, stride, size);
-        }
-      }
-    }
+// Number of elements of A (length la) among the first `diag` elements of the merge of the
+// sorted runs A and B (merge-path search; the order is strict, so the split is unique).
+__device__ __forceinline__ int merge_split(const SKey* A, int la, const SKey* Bv, int lb,
+                                           int diag) {
+  int lo = diag > lb ? diag - lb : 0, hi = diag < la ? diag : la;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sched_before(Bv[diag - 1 - mid], A[mid]))
+      hi = mid;
+    else
+      lo = mid + 1;
   }
+  return lo;
 }
 
-template <int KPT>
 __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
                                                    const double* __restrict__ sps, int B,
                                                    int G, int mode,
@@ -102,41 +54,57 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
                                                    double* __restrict__ theta,
                                                    int32_t* __restrict__ n_total) {
 #pragma clang fp contract(off)
-  constexpr int NP = 1024 * KPT;
   extern __shared__ __align__(16) unsigned char smem[];
-  double* key_a = reinterpret_cast<double*>(smem);               // [NP]
-  uint32_t* key_i = reinterpret_cast<uint32_t*>(key_a + NP);     // [NP]
   const int tid = threadIdx.x, n = B * G;
-  // 1. prefix survival, one thread per request, left to right in fp64
+  SKey* X = reinterpret_cast<SKey*>(smem);   // [n], then [n] for the other merge buffer
+  SKey* Y = X + n;
+  // 1. prefix survival, one thread per request, left to right in fp64.  With every
+  // c <= 1 a request's run is already in order (a non-increasing, index increasing); a run
+  // that is not (some c > 1) is put in order by insertion.
   for (int b = tid; b < B; b += blockDim.x) {
+    SKey* run = X + (size_t)b * G;
     double a = 1.0;
+    bool sorted = true;
     for (int j = 0; j < G; ++j) {
+      const double prev = a;
       a = a * (double)c[(size_t)b * G + j];
-      key_a[b * G + j] = a;
-      key_i[b * G + j] = (uint32_t)(b * G + j);
+      sorted = sorted && !(a > prev);
+      run[j] = SKey{a, (uint32_t)(b * G + j), 0u};
+    }
+    if (!sorted) {
+      for (int j = 1; j < G; ++j) {
+        const SKey key = run[j];
+        int q = j - 1;
+        while (q >= 0 && sched_before(key, run[q])) {
+          run[q + 1] = run[q];
+          --q;
+        }
+        run[q + 1] = key;
+      }
     }
   }
-  for (int i = n + tid; i < NP; i += blockDim.x) {
-    key_a[i] = -1.0;               // padding sorts after every real candidate
-    key_i[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  // 2. bottom-up merge of adjacent runs (length G, 2G, ...) into the full order; every
+  // output slot finds its source by a merge-path search
+  for (int L = G; L < n; L <<= 1) {
+    for (int p = tid; p < n; p += blockDim.x) {
+      const int base = p / (2 * L) * (2 * L);
+      const int la = min(L, n - base), lb = min(L, max(0, n - base - L));
+      const SKey* A = X + base;
+      const SKey* Bv = A + la;
+      const int d = p - base;
+      const int i = merge_split(A, la, Bv, lb, d), j = d - i;
+      Y[p] = (i < la && (j >= lb || sched_before(A[i], Bv[j]))) ? A[i] : Bv[j];
+    }
+    __syncthreads();
+    SKey* t = X;
+    X = Y;
+    Y = t;
   }
-  __syncthreads();
-  // 2. sort into "before" order
-  SKey k[KPT];
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) k[e] = SKey{key_a[KPT * tid + e], key_i[KPT * tid + e]};
-  bitonic_sort_regs<KPT>(k, key_a, key_i);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < KPT; ++e) {
-    key_a[KPT * tid + e] = k[e].a;
-    key_i[KPT * tid + e] = k[e].i;
-  }
-  __syncthreads();
   // greedy walk on wave 0, 64 candidates per chunk.  tau_t follows the sequential fp64
-  // chain tau_{t+1} = tau_t + a_(t) exactly (lane 0 order, broadcast per step); the best
-  // Theta before candidate t is tau_t * sps[B + t] (each admission raises it to exactly
-  // that product), so the stop tests of a chunk are independent and run in parallel.
+  // chain tau_{t+1} = tau_t + a_(t) exactly (lane order, each a_(t) broadcast from its lane);
+  // the best Theta before candidate t is tau_t * sps[B + t] (each admission raises it to
+  // exactly that product), so the stop tests of a chunk are independent and run in parallel.
   __shared__ int stop_s;
   __shared__ double tau_s;
   if (tid < 64) {
@@ -145,11 +113,16 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
     int stop = n;
     for (int base = 0; base < n; base += 64) {
       const int t = base + lane;
-      const double at = t < n ? key_a[t] : 0.0;
+      const double at = t < n ? X[t].a : 0.0;
       const int cnt = min(64, n - base);
       double before = 0.0, after = 0.0, cur = tau;
+      const unsigned long long atb = (unsigned long long)__double_as_longlong(at);
+      const uint32_t at_lo = (uint32_t)atb, at_hi = (uint32_t)(atb >> 32);
       for (int i = 0; i < cnt; ++i) {
-        const double ai = __shfl(at, i, 64);
+        // candidate i's a, read from lane i into scalar registers
+        const uint32_t lo = __builtin_amdgcn_readlane(at_lo, i);
+        const uint32_t hi = __builtin_amdgcn_readlane(at_hi, i);
+        const double ai = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
         before = (lane == i) ? cur : before;
         cur = cur + ai;
         after = (lane == i) ? cur : after;
@@ -180,7 +153,7 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
   __syncthreads();
   // admitted candidates form a prefix of each request's block: ell_b = the largest j
   for (int t = tid; t < stop; t += blockDim.x) {
-    const uint32_t i = key_i[t];
+    const uint32_t i = X[t].i;
     atomicMax(&ell[i / G], (int)(i % G) + 1);
   }
   if (tid == 0) {
@@ -203,24 +176,16 @@ extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, c
   if (!c || !sps || !ell || !theta || !n_total) return DSPARK_E_NULL;
   if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (mode != DSPARK_SCHED_GREEDY && mode != DSPARK_SCHED_FULL) return DSPARK_E_VALUE;
-  const int kpt = B * G <= 1024 ? 1 : (B * G <= 2048 ? 2 : 4);
-  const size_t sh = (size_t)1024 * kpt * (sizeof(double) + sizeof(uint32_t));
+  const size_t sh = (size_t)2 * B * G * sizeof(SKey);
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_schedule<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((size_t)4096 * 12)) != hipSuccess)
+    if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((size_t)2 * kMaxSchedCandidates * sizeof(SKey))) != hipSuccess)
       return DSPARK_E_HIP;
     attr_set = true;
   }
   hipStream_t st = (hipStream_t)stream;
-  if (kpt == 1)
-    hipLaunchKernelGGL(k_schedule<1>, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, ell,
-                       theta, n_total);
-  else if (kpt == 2)
-    hipLaunchKernelGGL(k_schedule<2>, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, ell,
-                       theta, n_total);
-  else
-    hipLaunchKernelGGL(k_schedule<4>, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, ell,
-                       theta, n_total);
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, ell, theta,
+                     n_total);
   return launch_status();
 }
