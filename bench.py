@@ -197,7 +197,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "k_draft16<8, 1>: fused bias MFMA (16x16x32 bf16, 16-column waves) + "
+            "kernel": "k_draft16<8>: fused bias MFMA (16x16x32 bf16, 16-column waves) + "
                       "softmax + Gumbel race over W2t and the B base-logit rows, one draft "
                       "position per launch",
             "bound": "hbm",

@@ -3,8 +3,8 @@
 // Gumbel-max draw.
 //
 // One launch per position; the launch boundary carries the device-wide dependency
-// x_{k-1} -> bias of position k (on MI355X a kernel boundary is several times cheaper
-// than an in-kernel grid barrier).  Each workgroup covers a vocabulary slice for every
+// x_{k-1} -> bias of position k (on MI355X an in-kernel grid barrier, with the next
+// position's independent loads prefetched across it, measured no faster).  Each workgroup covers a vocabulary slice for every
 // request and reports
 //   - its best Gumbel candidate as a packed (score, index) word through a 64-bit atomic
 //     max per request (order-free, so the winner is deterministic), and

@@ -23,21 +23,18 @@
 
 namespace dspark {
 
-__global__ void k_vfill_u64(unsigned long long* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0ull;
-}
-
 // Flattened ragged row list: rows (b, k) with k <= ell_b + 1, in request order.  One
-// workgroup; writes the list, its length and the number of (row, slice) work items.
+// workgroup; writes the list, its length and the number of (row, slice) work items, and
+// clears the bonus-race words.
 __global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__ ell, int B,
                                                      int G, int nslices,
                                                      int32_t* __restrict__ rows,
-                                                     int32_t* __restrict__ counts) {
+                                                     int32_t* __restrict__ counts,
+                                                     unsigned long long* __restrict__ bonus) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
+  for (int b = tid; b < B; b += 256) bonus[b] = 0ull;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 256) {
@@ -415,9 +412,8 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
 
-  hipLaunchKernelGGL(k_vfill_u64, dim3((B + 255) / 256), dim3(256), 0, st, w.bonus, (size_t)B);
   hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
-                     w.counts);
+                     w.counts, w.bonus);
   const long long max_items = (long long)B * (G + 1) * nsl;
   const int grid = (int)std::min<long long>(max_items, 2048);
   hipLaunchKernelGGL(k_verify_rows, dim3(grid), dim3(256), 0, st, T, ell, w.rows, w.counts, G,
