@@ -168,6 +168,22 @@ def main():
     log(f"draft sampling kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches of "
         f"{kern_pos:g} positions each")
 
+    # the production form of the scheduler (top-K admission, K from history): timed alone at
+    # this round's admitted count; one workgroup, latency-bound, so reported in us only
+    k_admit = int(ntot.cpu()[0]) - B
+    topk_out = (torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.float64, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev))
+    ds.dspark_schedule_topk(conf, sps, k_admit, out=topk_out)
+    tk0 = torch.cuda.Event(enable_timing=True)
+    tk1 = torch.cuda.Event(enable_timing=True)
+    tk0.record(stream)
+    for _ in range(args.steps):
+        ds.dspark_schedule_topk(conf, sps, k_admit, out=topk_out)
+    tk1.record(stream)
+    torch.cuda.synchronize()
+    topk_us = tk0.elapsed_time(tk1) * 1e3 / args.steps
+
     # algorithmic bytes (what the method must move), from this round's realised ell, n
     ell_h = ell.cpu().numpy().astype(np.int64)
     n_h = nacc.cpu().numpy().astype(np.int64)
@@ -223,6 +239,7 @@ def main():
         "draft_call_ms": round(draft_ms, 4),
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
+        "schedule_topk_us": round(topk_us, 2),
         "accepted_mean": round(float(n_h.mean()), 3),
         "verify_tokens": int((ell_h + 1).sum()),
     }

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
             L.dspark_confidence.argtypes = [D, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P]
             L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _I, _P, _P,
                                           _P, _P, _SZ, _P]
+            L.dspark_schedule_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                               ctypes.c_int32, _P, _P, _P, _P, _SZ, _P]
             L.dspark_verify.argtypes = [D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _F, _U64,
                                         _P, _P, _P, _P, _SZ, _P]
             L.dspark_accept_rate_tv.argtypes = [D, _P, _P, _P, _I, _P, _P, _P, _P, _F, _P, _P,
@@ -82,7 +84,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(_I),
                                               ctypes.POINTER(ctypes.c_double)]
             for fn in ("dspark_draft_markov", "dspark_confidence", "dspark_schedule",
-                       "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
+                       "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
                        "dspark_profile_start", "dspark_profile_stop"):
                 getattr(L, fn).restype = _I
             _lib = L
@@ -216,6 +218,26 @@ def dspark_schedule(c, sps, mode: int = SCHED_GREEDY, out=None, stream=None):
     ell, theta, n_total = out
     _check(lib().dspark_schedule(B, G, _ptr(c), _ptr(sps), int(mode), _ptr(ell), _ptr(theta),
                                  _ptr(n_total), None, 0, _stream_handle(stream)))
+    return ell, theta, n_total
+
+
+def dspark_schedule_topk(c, sps, k_admit: int, out=None, stream=None):
+    """Dynamic top-K admission: the first k_admit candidates of the scheduler's order.
+    Returns (ell [B] int32, theta [1] f64, n_total [1] int32)."""
+    B, G = c.shape
+    _f32(c, "c")
+    if sps.dtype != torch.float64:
+        raise ValueError("sps must be float64")
+    if sps.numel() < B * (G + 1) + 1:
+        raise ValueError("sps must have B*(gamma+1)+1 entries")
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=c.device),
+               torch.empty(1, dtype=torch.float64, device=c.device),
+               torch.empty(1, dtype=torch.int32, device=c.device))
+    ell, theta, n_total = out
+    _check(lib().dspark_schedule_topk(B, G, _ptr(c), _ptr(sps), int(k_admit), _ptr(ell),
+                                      _ptr(theta), _ptr(n_total), None, 0,
+                                      _stream_handle(stream)))
     return ell, theta, n_total
 
 

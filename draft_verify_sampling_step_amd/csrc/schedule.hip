@@ -47,9 +47,12 @@ __device__ __forceinline__ int merge_split(const SKey* A, int la, const SKey* Bv
   return lo;
 }
 
+// mode of k_schedule beyond the two public ones: admit the first k_admit candidates
+constexpr int kSchedTopK = 2;
+
 __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
                                                    const double* __restrict__ sps, int B,
-                                                   int G, int mode,
+                                                   int G, int mode, int k_admit,
                                                    int32_t* __restrict__ ell,
                                                    double* __restrict__ theta,
                                                    int32_t* __restrict__ n_total) {
@@ -132,6 +135,8 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
         const double th_next = after * sps[B + t + 1];
         const double th_best = before * sps[B + t];
         halt = th_next <= th_best;
+      } else if (mode == kSchedTopK && t < n) {
+        halt = t == k_admit;                   // the first k_admit are in, no more
       }
       const unsigned long long hm = __ballot(halt);
       if (hm) {
@@ -167,6 +172,20 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
 
 using namespace dspark;
 
+namespace {
+// the kernel's dynamic LDS may exceed the default limit: raise it once
+dspark_status set_sched_attr() {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((size_t)2 * kMaxSchedCandidates * sizeof(SKey))) != hipSuccess)
+      return DSPARK_E_HIP;
+    attr_set = true;
+  }
+  return DSPARK_OK;
+}
+}  // namespace
+
 extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, const double* sps,
                                          int mode, int32_t* ell, double* theta,
                                          int32_t* n_total, void* ws, size_t ws_bytes,
@@ -177,15 +196,26 @@ extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, c
   if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (mode != DSPARK_SCHED_GREEDY && mode != DSPARK_SCHED_FULL) return DSPARK_E_VALUE;
   const size_t sh = (size_t)2 * B * G * sizeof(SKey);
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((size_t)2 * kMaxSchedCandidates * sizeof(SKey))) != hipSuccess)
-      return DSPARK_E_HIP;
-    attr_set = true;
-  }
+  if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, ell, theta,
-                     n_total);
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, 0, ell,
+                     theta, n_total);
+  return launch_status();
+}
+
+extern "C" dspark_status dspark_schedule_topk(int32_t B, int32_t G, const float* c,
+                                              const double* sps, int32_t k_admit, int32_t* ell,
+                                              double* theta, int32_t* n_total, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!c || !sps || !ell || !theta || !n_total) return DSPARK_E_NULL;
+  if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
+  if (k_admit < 0) return DSPARK_E_VALUE;
+  const int k = (long long)k_admit > (long long)B * G ? B * G : k_admit;
+  const size_t sh = (size_t)2 * B * G * sizeof(SKey);
+  if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, (hipStream_t)stream, c, sps, B, G,
+                     kSchedTopK, k, ell, theta, n_total);
   return launch_status();
 }

@@ -13,6 +13,7 @@
  *                            over base logits plus a rank-r transition bias  [CSDN Eq. 4; XTL §3-4]
  *   2. dspark_confidence     c_k = sigmoid(w . [h_k ; W1[x_{k-1}]])          [CSDN Eq. 7; XTL §5]
  *   3. dspark_schedule       greedy prefix scheduler maximising tau * SPS(N)  [XTL §6; CSDN]
+ *      dspark_schedule_topk  its production form: top-K admission, K from history [XTL §7]
  *   4. dspark_verify         lossless rejection-sampling verification         [XTL §1; AIMSG 2]
  *   5. dspark_accept_rate_tv analytic accept rate 1 - |p_d - p_t|_1 / 2       [CSDN Eq. 8; XTL §5]
  *
@@ -149,6 +150,26 @@ dspark_status dspark_confidence(const dspark_dims* dims, const void* h, int hdt,
 dspark_status dspark_schedule(int32_t batch, int32_t gamma, const float* c, const double* sps,
                               int mode, int32_t* ell, double* theta, int32_t* n_total,
                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dynamic top-K admission [XTL §7, the production form of the scheduler: candidates are
+ * still ordered by the latest confidences, but the truncation length is predicted from
+ * the confidences of two steps earlier, so the next batch size is known ahead and the
+ * admission depends on history only].
+ *   k_admit  number of draft tokens to admit beyond the B bonus slots (for instance
+ *            n_total - B of a dspark_schedule made two steps earlier); values above
+ *            B * gamma admit everything.  Negative: DSPARK_E_VALUE.
+ * The first k_admit candidates in dspark_schedule's order (a descending, b ascending,
+ * j ascending; a in fp64 as there) are admitted; tau accumulates along them in that order
+ * and Theta = tau * sps[N] with N = B + k_admit.  Since a never increases along a request
+ * (c <= 1), every admission is a prefix: ell_b = the largest admitted j of request b.
+ * c, sps, ell, theta and n_total as for dspark_schedule; needs no workspace (NULL, 0);
+ * B * gamma <= 4096.
+ */
+dspark_status dspark_schedule_topk(int32_t batch, int32_t gamma, const float* c,
+                                   const double* sps, int32_t k_admit, int32_t* ell,
+                                   double* theta, int32_t* n_total, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * Rejection-sampling verification [XTL §1; AIMSG concept 2; accept probability

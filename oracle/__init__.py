@@ -60,6 +60,8 @@ def _load():
         lib.ora_confidence.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P]
         lib.ora_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                      _P, _P, _P]
+        lib.ora_schedule_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                           ctypes.c_int32, _P, _P, _P]
         lib.ora_verify.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_double, ctypes.c_uint64, _P, _P, _P, _P, _P, _P]
         lib.ora_accept_tv.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P,
@@ -187,6 +189,22 @@ def schedule(c, sps, mode=0):
     n_total = np.zeros(1, np.int32)
     lib.ora_schedule(B, G, _ptr(c), _ptr(sps), int(mode), _ptr(ell), _ptr(theta),
                      _ptr(n_total))
+    return ell, float(theta[0]), int(n_total[0])
+
+
+def schedule_topk(c, sps, K):
+    """Dynamic top-K admission: the first K candidates (clamped to [0, B*gamma]) in the
+    greedy scheduler's order.  Returns (ell [B] int32, theta float, n_total int)."""
+    lib = _load()
+    c = _f64(c)
+    B, G = c.shape
+    sps = _f64(sps)
+    assert sps.shape[0] >= B * (G + 1) + 1
+    ell = np.zeros(B, np.int32)
+    theta = np.zeros(1)
+    n_total = np.zeros(1, np.int32)
+    lib.ora_schedule_topk(B, G, _ptr(c), _ptr(sps), int(K), _ptr(ell), _ptr(theta),
+                          _ptr(n_total))
     return ell, float(theta[0]), int(n_total[0])
 
 

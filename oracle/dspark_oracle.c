@@ -29,6 +29,9 @@
  *   ora_confidence ..................... pinned (w=0, unit-vector w special cases)
  *   ora_schedule ....................... pinned (brute force over all prefix lengths,
  *                                        closed-form special cases)
+ *   ora_schedule_topk .................. pinned (brute force over all prefix lengths of a
+ *                                        given total, agreement with ora_schedule at its
+ *                                        own admitted count, Monte-Carlo losslessness)
  *   ora_verify ......................... pinned (Monte-Carlo losslessness against the
  *                                        target law, special cases)
  *   ora_accept_tv ...................... pinned (TV identity, Monte-Carlo acceptance rate)
@@ -262,6 +265,40 @@ void ora_schedule(int32_t B, int32_t gamma, const double* c, const double* sps, 
         ell[cand[t].b] = cand[t].j;
     }
     *theta = best;
+    *n_total = N;
+    free(cand);
+}
+
+/* Dynamic top-K admission [XTL §7: in production the candidates are still ordered by the
+ * latest confidences, but the truncation length is predicted from the confidences of two
+ * steps earlier, so that the next batch size is known ahead and admission depends on
+ * history only].  K is that length: the number of draft tokens admitted beyond the B
+ * bonus slots, supplied by the caller (for instance n_total - B of a schedule made two
+ * steps earlier) and clamped to [0, B*gamma].  The first K candidates in the order of
+ * ora_schedule are admitted; tau, N and Theta accumulate along them exactly as there. */
+void ora_schedule_topk(int32_t B, int32_t gamma, const double* c, const double* sps, int32_t K,
+                       int32_t* ell, double* theta, int32_t* n_total)
+{
+    size_t n = (size_t)B * gamma;
+    size_t take = K < 0 ? 0 : ((size_t)K > n ? n : (size_t)K);
+    ora_cand* cand = (ora_cand*)malloc(sizeof(ora_cand) * (n ? n : 1));
+    for (int b = 0; b < B; ++b) {
+        double a = 1.0;
+        for (int j = 1; j <= gamma; ++j) {
+            a = a * c[(size_t)b * gamma + (j - 1)];
+            cand[(size_t)b * gamma + (j - 1)] = (ora_cand){ a, b, j };
+        }
+        ell[b] = 0;
+    }
+    qsort(cand, n, sizeof(ora_cand), cand_cmp);
+    int32_t N = B;
+    double tau = (double)B;
+    for (size_t t = 0; t < take; ++t) {
+        tau = tau + cand[t].a;
+        N = N + 1;
+        if (cand[t].j > ell[cand[t].b]) ell[cand[t].b] = cand[t].j;
+    }
+    *theta = tau * sps[N];
     *n_total = N;
     free(cand);
 }

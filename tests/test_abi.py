@@ -67,6 +67,16 @@ def test_schedule_argument_validation():
     assert L.dspark_schedule(4, 4, P, P, 2, P, P, P, None, 0, None) == 4
 
 
+def test_schedule_topk_argument_validation():
+    L = ds.lib()
+    assert L.dspark_schedule_topk(4, 4, None, P, 3, P, P, P, None, 0, None) == 1
+    assert L.dspark_schedule_topk(4, 4, P, P, 3, None, P, P, None, 0, None) == 1
+    assert L.dspark_schedule_topk(0, 4, P, P, 3, P, P, P, None, 0, None) == 2
+    assert L.dspark_schedule_topk(4, 65, P, P, 3, P, P, P, None, 0, None) == 2
+    assert L.dspark_schedule_topk(4097, 1, P, P, 3, P, P, P, None, 0, None) == 2
+    assert L.dspark_schedule_topk(4, 4, P, P, -1, P, P, P, None, 0, None) == 4
+
+
 def test_verify_confidence_tv_validation():
     L = ds.lib()
     dm = _dims()

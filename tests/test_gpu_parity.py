@@ -170,6 +170,30 @@ def test_schedule_edge_cases_bit_exact():
         assert host(th_g)[0] == th_o and host(n_g)[0] == n_o
 
 
+def test_schedule_topk_bit_exact():
+    """Top-K admission against the oracle, bit for bit, at the serve128 shape and edges;
+    at the greedy schedule's own admitted count it reproduces that schedule."""
+    rng = np.random.default_rng(6)
+    B, G = 128, 16
+    sps = workload.sps_table(workload.CONFIGS["serve128"])
+    c = rng.uniform(0, 1, size=(B, G)).astype(np.float32)
+    c[::3, :5] = 1.0                    # exact ties in survival
+    c[5, 2] = 0.0
+    cases = [(c, sps, K) for K in (0, 1, 63, 64, 65, 114, 1000, 2047, 2048, 5000)]
+    cases.append((np.full((64, 64), 0.99, np.float32), 1000.0 / (10 + np.arange(64 * 65 + 1)),
+                  4095))
+    cases.append((rng.uniform(size=(1, 4)).astype(np.float32), np.full(6, 3.0), 2))
+    cases.append((rng.uniform(size=(3, 5)).astype(np.float32), np.full(19, 2.0), 7))
+    for c_, sps_, K in cases:
+        ell_o, th_o, n_o = oracle.schedule_topk(c_, sps_, K)
+        ell_g, th_g, n_g = ds.dspark_schedule_topk(dev(c_), dev(np.asarray(sps_, np.float64)), K)
+        assert np.array_equal(host(ell_g), ell_o), (c_.shape, K)
+        assert host(th_g)[0] == th_o and host(n_g)[0] == n_o, (c_.shape, K)
+    ell_g, th_g, n_g = ds.dspark_schedule(dev(c), dev(sps), 0)
+    ell_k, th_k, n_k = ds.dspark_schedule_topk(dev(c), dev(sps), int(host(n_g)[0]) - B)
+    assert np.array_equal(host(ell_g), host(ell_k)) and host(th_g)[0] == host(th_k)[0]
+
+
 # ------------------------------------------------------------------------------------
 # full-size workloads, sampled requests
 # ------------------------------------------------------------------------------------

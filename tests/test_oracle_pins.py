@@ -256,6 +256,75 @@ def test_schedule_tie_order_request_then_position():
     assert list(ell) == [2] and theta == 3.0
 
 
+def _tau(c, ell):
+    """tau(ell) = B + sum_b sum_{j<=ell_b} prod_{i<=j} c_bi (expected output tokens)."""
+    B = c.shape[0]
+    tau = float(B)
+    for b in range(B):
+        a = 1.0
+        for j in range(ell[b]):
+            a *= c[b, j]
+            tau += a
+    return tau
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_schedule_topk_is_the_best_admission_of_its_size(seed):
+    """For a fixed number K of admitted tokens (fixed N = B + K), the admitted set with
+    the most expected output tokens is the top-K by survival [XTL §6/§7]: brute force
+    over every ell with sum(ell) = K reaches the same tau, at the same ell when unique."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 4))
+    G = int(rng.integers(1, 5))
+    c = rng.uniform(0.05, 1.0, size=(B, G)).astype(np.float32)
+    c64 = c.astype(np.float64)
+    sps = 1000.0 / (10.0 + np.arange(B * (G + 1) + 1))
+    for K in range(B * G + 1):
+        ell, theta, n_total = oracle.schedule_topk(c, sps, K)
+        assert n_total == B + K and int(ell.sum()) == K
+        cands = [e for e in itertools.product(range(G + 1), repeat=B) if sum(e) == K]
+        taus = np.array([_tau(c64, e) for e in cands])
+        best = taus.max()
+        assert abs(_tau(c64, ell) - best) <= 1e-12 * best
+        assert abs(theta - best * sps[B + K]) <= 1e-12 * theta
+        if (taus >= best * (1 - 1e-12)).sum() == 1:
+            assert tuple(ell) == cands[int(taus.argmax())]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_topk_at_the_greedy_count_is_the_greedy_schedule(seed):
+    """The greedy schedule admits the first n_total - B candidates of the same order, so
+    top-K with that K must reproduce its ell, Theta and N bit for bit."""
+    rng = np.random.default_rng(200 + seed)
+    B, G = int(rng.integers(2, 40)), int(rng.integers(1, 17))
+    c = rng.uniform(0.0, 1.0, size=(B, G)).astype(np.float32)
+    c[rng.random((B, G)) < 0.1] = 1.0     # exact ties in survival
+    N = np.arange(B * (G + 1) + 1, dtype=np.float64)
+    sps = 1000.0 / (12.0 + 0.02 * N + 1e-5 * N * N)
+    ell_g, theta_g, n_g = oracle.schedule(c, sps, 0)
+    ell_k, theta_k, n_k = oracle.schedule_topk(c, sps, n_g - B)
+    assert np.array_equal(ell_g, ell_k) and theta_g == theta_k and n_g == n_k
+
+
+def test_schedule_topk_edges_and_monotonicity():
+    rng = np.random.default_rng(7)
+    B, G = 6, 5
+    c = rng.uniform(0.1, 0.95, size=(B, G)).astype(np.float32)
+    sps = 1000.0 / (10.0 + np.arange(B * (G + 1) + 1))
+    ell, theta, n = oracle.schedule_topk(c, sps, 0)
+    assert np.all(ell == 0) and n == B and theta == B * sps[B]
+    full = oracle.schedule(c, sps, 1)
+    for K in (B * G, B * G + 7):
+        ell, theta, n = oracle.schedule_topk(c, sps, K)
+        assert np.all(ell == G) and n == B * (G + 1) and theta == full[1]
+    assert np.all(oracle.schedule_topk(c, sps, -3)[0] == 0)
+    prev = np.zeros(B, np.int32)
+    for K in range(B * G + 1):
+        ell = oracle.schedule_topk(c, sps, K)[0]
+        assert np.all(ell >= prev) and int((ell - prev).sum()) == (1 if K else 0)
+        prev = ell
+
+
 # ------------------------------------------------------------------------------------
 # verification
 # ------------------------------------------------------------------------------------
@@ -349,10 +418,11 @@ def _chi2_p(hist, law):
     return stats.chisquare(obs, exp).pvalue
 
 
-@pytest.mark.parametrize("rule", ["full", "fixed_mix", "scheduler"])
+@pytest.mark.parametrize("rule", ["full", "fixed_mix", "scheduler", "topk_delayed"])
 def test_verify_is_lossless_monte_carlo(rule):
     """The emitted tokens, completed with the target chain, follow the target law."""
-    rng = np.random.default_rng({"full": 1, "fixed_mix": 2, "scheduler": 3}[rule])
+    rng = np.random.default_rng({"full": 1, "fixed_mix": 2, "scheduler": 3,
+                                 "topk_delayed": 4}[rule])
     B, G, V, r = 200000, 3, 4, 2
 
     def ell_rule(tok, d, T):
@@ -367,7 +437,13 @@ def test_verify_is_lossless_monte_carlo(rule):
         c = oracle.confidence(h, np.eye(V, r) * 3.0, w, np.full(B, 1), tok).astype(np.float32)
         N = np.arange(B * (G + 1) + 1, dtype=np.float64)
         sps = 1000.0 / (10.0 + 3.0 * N / B + 1.0 * (N / B) ** 2)
-        return oracle.schedule(c, sps, 0)[0]
+        if rule == "scheduler":
+            return oracle.schedule(c, sps, 0)[0]
+        # dynamic top-K [XTL §7]: K from an earlier, independent batch's schedule (the
+        # history), the admitted set from the current confidences
+        c_old = rng.uniform(0.0, 1.0, size=(B, G)).astype(np.float32)
+        K = oracle.schedule(c_old, sps, 0)[2] - B
+        return oracle.schedule_topk(c, sps, K)[0]
 
     hist, law, v = _lossless_round(rng, B, G, V, r, ell_rule, seed=77 + len(rule))
     assert _chi2_p(hist, law) > 1e-4
