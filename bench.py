@@ -184,6 +184,22 @@ def main():
     torch.cuda.synchronize()
     topk_us = tk0.elapsed_time(tk1) * 1e3 / args.steps
 
+    # sequential temperature scaling of the confidence head on a held-out set of this draft
+    # length (synthetic, 131072 blocks, 256-value grid, 15 bins): fp64 sigmoid evaluations
+    # dominate, n * grid * gamma of them
+    cal = workload.calibration_inputs(131072, G, seed=args.seed)
+    cal_logit, cal_acc = ds.to_device(cal.logit), ds.to_device(cal.n_accept)
+    cal_grid = torch.tensor(np.geomspace(0.4, 5.0, 256), dtype=torch.float64, device=dev)
+    ds.dspark_sts_calibrate(cal_logit, cal_acc, cal_grid, 15)
+    sc0 = torch.cuda.Event(enable_timing=True)
+    sc1 = torch.cuda.Event(enable_timing=True)
+    sc0.record(stream)
+    for _ in range(3):
+        ds.dspark_sts_calibrate(cal_logit, cal_acc, cal_grid, 15)
+    sc1.record(stream)
+    torch.cuda.synchronize()
+    sts_ms = sc0.elapsed_time(sc1) / 3
+
     # algorithmic bytes (what the method must move), from this round's realised ell, n
     ell_h = ell.cpu().numpy().astype(np.int64)
     n_h = nacc.cpu().numpy().astype(np.int64)
@@ -240,6 +256,8 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
         "schedule_topk_us": round(topk_us, 2),
+        "sts_calibrate_ms": round(sts_ms, 4),
+        "sts_sigmoids_per_s": round(131072 * 256 * G / (sts_ms * 1e-3), 1),
         "accepted_mean": round(float(n_h.mean()), 3),
         "verify_tokens": int((ell_h + 1).sum()),
     }

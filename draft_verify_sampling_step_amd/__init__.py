@@ -70,6 +70,13 @@ def lib() -> ctypes.CDLL:
             L.dspark_confidence.argtypes = [D, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P]
             L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _I, _P, _P,
                                           _P, _P, _SZ, _P]
+            L.dspark_confidence_calibrated.argtypes = [D, _P, _I, _P, _I, _P, _I, _P, _P, _P,
+                                                       _P, _P]
+            L.dspark_sts_workspace_bytes.argtypes = [ctypes.c_int32] * 3
+            L.dspark_sts_workspace_bytes.restype = _SZ
+            L.dspark_sts_calibrate.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                               ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                               _SZ, _P]
             L.dspark_schedule_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P,
                                                ctypes.c_int32, _P, _P, _P, _P, _SZ, _P]
             L.dspark_verify.argtypes = [D, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _F, _U64,
@@ -83,7 +90,8 @@ def lib() -> ctypes.CDLL:
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(_I),
                                               ctypes.POINTER(ctypes.c_double)]
-            for fn in ("dspark_draft_markov", "dspark_confidence", "dspark_schedule",
+            for fn in ("dspark_draft_markov", "dspark_confidence",
+                       "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
                        "dspark_profile_start", "dspark_profile_stop"):
                 getattr(L, fn).restype = _I
@@ -201,6 +209,45 @@ def dspark_confidence(h, W1, w, anchor, tokens, out=None, stream=None):
                                    _ptr(w), _wdtype(w), _ptr(anchor), _ptr(tokens), _ptr(c),
                                    _stream_handle(stream)))
     return c
+
+
+def dspark_confidence_calibrated(h, W1, w, anchor, tokens, temps, out=None, stream=None):
+    """c [B][gamma] f32 = sigmoid(w . [h_k ; W1[x_{k-1}]] / temps[k-1]), temps [gamma] f64."""
+    B, G, d = h.shape
+    V, r = W1.shape
+    _i32(anchor, "anchor")
+    _i32(tokens, "tokens")
+    if temps.dtype != torch.float64 or temps.numel() < G:
+        raise ValueError("temps must be float64 with gamma entries")
+    c = out if out is not None else torch.empty((B, G), dtype=torch.float32, device=h.device)
+    dm = Dims(B, G, V, r, d)
+    _check(lib().dspark_confidence_calibrated(ctypes.byref(dm), _ptr(h), _wdtype(h), _ptr(W1),
+                                              _wdtype(W1), _ptr(w), _wdtype(w), _ptr(anchor),
+                                              _ptr(tokens), _ptr(temps), _ptr(c),
+                                              _stream_handle(stream)))
+    return c
+
+
+def dspark_sts_calibrate(logit, n_accept, temps, n_bins: int = 15, out=None, ws=None,
+                         stream=None):
+    """Sequential temperature scaling: logit [n][gamma] f32, n_accept [n] int32, temps [n_t]
+    f64 grid.  Returns (t [gamma] f64, ece [gamma] f64)."""
+    n, G = logit.shape
+    _f32(logit, "logit")
+    _i32(n_accept, "n_accept")
+    if temps.dtype != torch.float64:
+        raise ValueError("temps must be float64")
+    n_t = temps.numel()
+    if out is None:
+        out = (torch.empty(G, dtype=torch.float64, device=logit.device),
+               torch.empty(G, dtype=torch.float64, device=logit.device))
+    t_out, ece_out = out
+    need = int(lib().dspark_sts_workspace_bytes(n, n_t, int(n_bins)))
+    w = _workspace(logit.device, need, ws)
+    _check(lib().dspark_sts_calibrate(n, G, _ptr(logit), _ptr(n_accept), _ptr(temps), n_t,
+                                      int(n_bins), _ptr(t_out), _ptr(ece_out), _ptr(w),
+                                      w.numel(), _stream_handle(stream)))
+    return t_out, ece_out
 
 
 def dspark_schedule(c, sps, mode: int = SCHED_GREEDY, out=None, stream=None):

@@ -1,5 +1,6 @@
 // confidence.hip -- confidence head [CSDN Eq. 7; XTL §5]:
-//   c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]),  x_0 = anchor, no bias term.
+//   c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]),  x_0 = anchor, no bias term;
+// calibrated form (sequential temperature scaling, [XTL §5]): c_k = sigmoid(logit_k / t_k).
 // One wave per (request, position): a wave-reduced dot product of length d + r with
 // coalesced 16-byte loads where the element type allows.
 #include "dspark_dev.h"
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(256) void k_confidence(const TH* __restrict__ h,
                                                     const TWV* __restrict__ w,
                                                     const int32_t* __restrict__ anchor,
                                                     const int32_t* __restrict__ tokens,
+                                                    const double* __restrict__ temps,
                                                     float* __restrict__ c, int B, int G, int d,
                                                     int r, int V) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -57,16 +59,17 @@ __global__ __launch_bounds__(256) void k_confidence(const TH* __restrict__ h,
   float acc = lane_dot<TWV, TH>(w, h + (size_t)wid * d, d, lane);
   acc += lane_dot<TWV, TW1>(w + d, W1 + (size_t)prev * r, r, lane);
   acc = wave_sum(acc);
+  if (temps) acc = (float)((double)acc / temps[k - 1]);
   if (lane == 0) c[wid] = 1.0f / (1.0f + expf(-acc));
 }
 
 template <typename TH, typename TW1, typename TWV>
 static void launch_conf(const dspark_dims* dm, const void* h, const void* W1, const void* w,
-                        const int32_t* anchor, const int32_t* tokens, float* c,
-                        hipStream_t st) {
+                        const int32_t* anchor, const int32_t* tokens, const double* temps,
+                        float* c, hipStream_t st) {
   const int n = dm->batch * dm->gamma;
   hipLaunchKernelGGL((k_confidence<TH, TW1, TWV>), dim3((n + 3) / 4), dim3(256), 0, st,
-                     (const TH*)h, (const TW1*)W1, (const TWV*)w, anchor, tokens, c,
+                     (const TH*)h, (const TW1*)W1, (const TWV*)w, anchor, tokens, temps, c,
                      dm->batch, dm->gamma, dm->hidden, dm->rank, dm->vocab);
 }
 
@@ -74,25 +77,48 @@ static void launch_conf(const dspark_dims* dm, const void* h, const void* W1, co
 
 using namespace dspark;
 
-extern "C" dspark_status dspark_confidence(const dspark_dims* dm, const void* h, int hdt,
-                                           const void* W1, int wdt, const void* w, int wvdt,
-                                           const int32_t* anchor, const int32_t* tokens,
-                                           float* c, void* stream) {
+namespace {
+
+dspark_status confidence_impl(const dspark_dims* dm, const void* h, int hdt, const void* W1,
+                              int wdt, const void* w, int wvdt, const int32_t* anchor,
+                              const int32_t* tokens, const double* temps, float* c,
+                              void* stream) {
   if (!dm || !W1 || !w || !anchor || !tokens || !c) return DSPARK_E_NULL;
   if (!dims_ok(dm)) return DSPARK_E_SHAPE;
   if (dm->hidden > 0 && !h) return DSPARK_E_NULL;
   if (!dtype_ok(hdt) || !dtype_ok(wdt) || !dtype_ok(wvdt)) return DSPARK_E_DTYPE;
   hipStream_t st = (hipStream_t)stream;
   const int code = (hdt << 2) | (wdt << 1) | wvdt;
+  const double* tp = temps;
   switch (code) {
-    case 0: launch_conf<float, float, float>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 1: launch_conf<float, float, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 2: launch_conf<float, uint16_t, float>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 3: launch_conf<float, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 4: launch_conf<uint16_t, float, float>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 5: launch_conf<uint16_t, float, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
-    case 6: launch_conf<uint16_t, uint16_t, float>(dm, h, W1, w, anchor, tokens, c, st); break;
-    default: launch_conf<uint16_t, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, c, st); break;
+    case 0: launch_conf<float, float, float>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 1: launch_conf<float, float, uint16_t>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 2: launch_conf<float, uint16_t, float>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 3: launch_conf<float, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 4: launch_conf<uint16_t, float, float>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 5: launch_conf<uint16_t, float, uint16_t>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    case 6: launch_conf<uint16_t, uint16_t, float>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
+    default: launch_conf<uint16_t, uint16_t, uint16_t>(dm, h, W1, w, anchor, tokens, tp, c, st); break;
   }
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" dspark_status dspark_confidence(const dspark_dims* dm, const void* h, int hdt,
+                                           const void* W1, int wdt, const void* w, int wvdt,
+                                           const int32_t* anchor, const int32_t* tokens,
+                                           float* c, void* stream) {
+  return confidence_impl(dm, h, hdt, W1, wdt, w, wvdt, anchor, tokens, nullptr, c, stream);
+}
+
+extern "C" dspark_status dspark_confidence_calibrated(const dspark_dims* dm, const void* h,
+                                                      int hdt, const void* W1, int wdt,
+                                                      const void* w, int wvdt,
+                                                      const int32_t* anchor,
+                                                      const int32_t* tokens,
+                                                      const double* temps, float* c,
+                                                      void* stream) {
+  if (!temps) return DSPARK_E_NULL;
+  return confidence_impl(dm, h, hdt, W1, wdt, w, wvdt, anchor, tokens, temps, c, stream);
 }

@@ -13,6 +13,9 @@ namespace dspark {
 
 constexpr int kRowTile = 256;        // vocab rows per tile in the row (GEMV) kernels
 constexpr int kMaxSchedCandidates = 4096;
+// Calibration samples per call: the integer bin sums (p in 2^-40 units, labels shifted by
+// 40 bits) then stay below 2^62.
+constexpr int kMaxStsSamples = 1 << 22;
 
 inline bool dims_ok(const dspark_dims* d) {
   return d && d->batch >= 1 && d->batch <= 65535 && d->gamma >= 1 && d->gamma <= 64 &&

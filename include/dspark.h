@@ -12,6 +12,8 @@
  *   1. dspark_draft_markov   Markov-head draft: gamma sequential softmax + sampling steps
  *                            over base logits plus a rank-r transition bias  [CSDN Eq. 4; XTL §3-4]
  *   2. dspark_confidence     c_k = sigmoid(w . [h_k ; W1[x_{k-1}]])          [CSDN Eq. 7; XTL §5]
+ *      dspark_sts_calibrate  per-position temperatures for it, fitted on held-out data, and
+ *      dspark_confidence_calibrated, the head with them applied          [XTL §5; AIMSG]
  *   3. dspark_schedule       greedy prefix scheduler maximising tau * SPS(N)  [XTL §6; CSDN]
  *      dspark_schedule_topk  its production form: top-K admission, K from history [XTL §7]
  *   4. dspark_verify         lossless rejection-sampling verification         [XTL §1; AIMSG 2]
@@ -129,6 +131,47 @@ dspark_status dspark_confidence(const dspark_dims* dims, const void* h, int hdt,
                                 const void* W1, int wdt, const void* w, int wvdt,
                                 const int32_t* anchor, const int32_t* tokens, float* c,
                                 void* stream);
+
+/*
+ * The calibrated confidence head [XTL §5, sequential temperature scaling]:
+ *   c[b][k-1] = 1 / (1 + exp(-logit_{b,k} / temps[k-1]))
+ * with logit_{b,k} the argument of the sigmoid of dspark_confidence (computed the same
+ * way) and temps [gamma] fp64 > 0 per-position temperatures, for instance those of
+ * dspark_sts_calibrate.  temps NULL: DSPARK_E_NULL.  Other arguments as there.
+ */
+dspark_status dspark_confidence_calibrated(const dspark_dims* dims, const void* h, int hdt,
+                                           const void* W1, int wdt, const void* w, int wvdt,
+                                           const int32_t* anchor, const int32_t* tokens,
+                                           const double* temps, float* c, void* stream);
+
+/*
+ * Sequential temperature scaling [XTL §5: the scheduler needs confidences whose values
+ * match acceptance rates, so the product of confidences is calibrated on held-out data
+ * from left to right; AIMSG, on STS: per position a 1-D grid search over the temperature,
+ * minimising the expected calibration error (ECE) of the cumulative product against the
+ * empirical prefix acceptance; scaling by a temperature keeps the confidences' order].
+ *   n         held-out drafted blocks, 1 <= n <= 2^22.
+ *   logit     [n][gamma] fp32 confidence logits (c = sigmoid(logit)).
+ *   n_accept  [n] int32 accepted prefix length of each block; the label of position k is
+ *             y_k = [n_accept >= k].
+ *   temps     [n_t] fp64 candidate temperatures (> 0), 1 <= n_t <= 65535.
+ *   n_bins    equal-width ECE bins on [0, 1], 1..256; p lies in bin
+ *             min(floor(p * n_bins), n_bins - 1).
+ *   t_out     out [gamma] fp64 chosen temperature per position.
+ *   ece_out   out [gamma] fp64 ECE of the cumulative product at the chosen temperatures.
+ * For k = 1..gamma, with t_1..t_{k-1} chosen:
+ *   p_{s,k}(t) = prod_{i<k} sigmoid(logit_{s,i} / t_i) * sigmoid(logit_{s,k} / t)   (fp64)
+ *   ECE_k(t)   = sum over bins of (|bin| / n) |mean p - mean y_k| = sum |sum p - sum y| / n
+ *   t_k        = the grid value with the smallest ECE_k (the first on exact ties).
+ * The bin sums are accumulated as integers (p in units of 2^-40), so the result does not
+ * depend on the order of accumulation.  Workspace: dspark_sts_workspace_bytes(n, n_t,
+ * n_bins) bytes.
+ */
+size_t dspark_sts_workspace_bytes(int32_t n, int32_t n_t, int32_t n_bins);
+dspark_status dspark_sts_calibrate(int32_t n, int32_t gamma, const float* logit,
+                                   const int32_t* n_accept, const double* temps, int32_t n_t,
+                                   int32_t n_bins, double* t_out, double* ece_out, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * Hardware-aware prefix scheduler [XTL §6; CSDN throughput objective and the quotes of

@@ -57,11 +57,13 @@ def _load():
             ctypes.c_int64, _P]
         lib.ora_draft.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P,
                                   ctypes.c_double, ctypes.c_uint64, _P, _P, _P, _P, _P]
-        lib.ora_confidence.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P]
+        lib.ora_confidence.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P, _P]
         lib.ora_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32,
                                      _P, _P, _P]
         lib.ora_schedule_topk.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P,
                                            ctypes.c_int32, _P, _P, _P]
+        lib.ora_sts_calibrate.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                          ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
         lib.ora_verify.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_double, ctypes.c_uint64, _P, _P, _P, _P, _P, _P]
         lib.ora_accept_tv.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P,
@@ -154,8 +156,9 @@ def draft(U, W1, W2t, anchor, temperature, seed, forced=None, gid=None, want_pro
     return out
 
 
-def confidence(h, W1, w, anchor, tokens):
-    """c[b][k-1] = sigmoid(w . [h_k ; W1[x_{k-1}]]) in fp64."""
+def confidence(h, W1, w, anchor, tokens, temps=None):
+    """c[b][k-1] = sigmoid(w . [h_k ; W1[x_{k-1}]]) in fp64; with temps [gamma] the
+    calibrated head sigmoid(logit / temps[k-1])."""
     lib = _load()
     h = _f64(h)
     B, G, d = h.shape
@@ -167,8 +170,10 @@ def confidence(h, W1, w, anchor, tokens):
     tokens = _i32(tokens)
     c = np.zeros((B, G))
     dm = _dims(B, G, W1.shape[0], r, d)
+    t = None if temps is None else _f64(temps)
+    assert t is None or t.shape == (G,)
     lib.ora_confidence(ctypes.byref(dm), _ptr(h), _ptr(W1), _ptr(w), _ptr(anchor),
-                       _ptr(tokens), _ptr(c))
+                       _ptr(tokens), _ptr(t), _ptr(c))
     return c
 
 
@@ -206,6 +211,26 @@ def schedule_topk(c, sps, K):
     lib.ora_schedule_topk(B, G, _ptr(c), _ptr(sps), int(K), _ptr(ell), _ptr(theta),
                           _ptr(n_total))
     return ell, float(theta[0]), int(n_total[0])
+
+
+def sts_calibrate(logit, n_accept, temps, n_bins=15):
+    """Sequential temperature scaling of the confidence head.
+
+    logit [n][gamma] confidence logits (fp32 values are widened exactly), n_accept [n]
+    accepted prefix lengths, temps the grid, n_bins equal-width ECE bins.
+    Returns (t [gamma], ece [gamma], gap [gamma]): the chosen temperature per position,
+    the ECE of the cumulative product there, and the margin to the runner-up."""
+    lib = _load()
+    logit = _f64(logit)
+    n, G = logit.shape
+    n_accept = np.ascontiguousarray(n_accept, np.int32)
+    temps = _f64(temps)
+    t = np.zeros(G)
+    ece = np.zeros(G)
+    gap = np.zeros(G)
+    lib.ora_sts_calibrate(n, G, _ptr(logit), _ptr(n_accept), _ptr(temps), temps.shape[0],
+                          int(n_bins), _ptr(t), _ptr(ece), _ptr(gap))
+    return t, ece, gap
 
 
 def verify(U, W1, W2t, anchor, tokens, T, ell, temperature, seed, gid=None):

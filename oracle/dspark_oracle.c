@@ -32,6 +32,8 @@
  *   ora_schedule_topk .................. pinned (brute force over all prefix lengths of a
  *                                        given total, agreement with ora_schedule at its
  *                                        own admitted count, Monte-Carlo losslessness)
+ *   ora_sts_calibrate .................. pinned (recovery of known per-position
+ *                                        temperatures, hand-computed ECE, one-value grids)
  *   ora_verify ......................... pinned (Monte-Carlo losslessness against the
  *                                        target law, special cases)
  *   ora_accept_tv ...................... pinned (TV identity, Monte-Carlo acceptance rate)
@@ -194,8 +196,11 @@ void ora_draft(const ora_dims* dm, const double* U, const double* W1, const doub
 /* Confidence head [CSDN Eq. 7; XTL §5]: c_k = sigmoid(w . [h_k ; W1[x_{k-1}]]).          */
 /* ------------------------------------------------------------------------------------ */
 /* w has d + r entries in the concatenation order [h ; W1 row]; there is no bias term. */
+/* With temps (may be NULL) the head is the calibrated one [XTL §5, sequential temperature
+ * scaling]: c = 1 / (1 + exp(-logit / temps[k-1])). */
 void ora_confidence(const ora_dims* dm, const double* h, const double* W1, const double* w,
-                    const int32_t* anchor, const int32_t* tokens, double* c)
+                    const int32_t* anchor, const int32_t* tokens, const double* temps,
+                    double* c)
 {
     const int B = dm->batch, G = dm->gamma, d = dm->hidden, r = dm->rank;
     for (int b = 0; b < B; ++b) {
@@ -205,6 +210,7 @@ void ora_confidence(const ora_dims* dm, const double* h, const double* W1, const
             double logit = 0.0;
             for (int j = 0; j < d; ++j) logit += w[j] * hk[j];
             for (int i = 0; i < r; ++i) logit += w[d + i] * e[i];
+            if (temps) logit = logit / temps[k - 1];
             c[(size_t)b * G + (k - 1)] = 1.0 / (1.0 + exp(-logit));
         }
     }
@@ -301,6 +307,72 @@ void ora_schedule_topk(int32_t B, int32_t gamma, const double* c, const double* 
     *theta = tau * sps[N];
     *n_total = N;
     free(cand);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Sequential temperature scaling of the confidence head [XTL §5: the scheduler needs     */
+/* confidences whose values match acceptance rates, not only their order, so the product  */
+/* of confidences is calibrated on held-out data from left to right; AIMSG, on STS: a     */
+/* 1-D grid search per position over the cumulative product, minimising the expected      */
+/* calibration error against the empirical prefix acceptance; temperature scaling keeps   */
+/* the order of the confidences].                                                        */
+/* ------------------------------------------------------------------------------------ */
+/* n held-out drafted blocks: logit[s][k-1] is the confidence logit of position k
+ * (c = 1 / (1 + exp(-logit))), n_accept[s] the accepted prefix length, so the label of
+ * position k is y_{s,k} = [n_accept[s] >= k].  temps[0..n_t) is the grid, n_bins the
+ * number of equal-width bins on [0, 1] (p falls in bin min(floor(p n_bins), n_bins - 1)).
+ * For k = 1..gamma in order, with t_1..t_{k-1} already chosen:
+ *   p_{s,k}(t) = prod_{i<k} c_{s,i}(t_i) * c_{s,k}(t),   c_{s,i}(t) = 1/(1+exp(-logit/t))
+ *   ECE_k(t)   = sum over bins m of (|m| / n) * | mean_{s in m} p - mean_{s in m} y_k |
+ *   t_k        = the grid value with the smallest ECE_k (the first one on exact ties).
+ * Outputs t_out[k-1], ece_out[k-1] = ECE_k(t_k) and, if gap is not NULL, gap[k-1] = the
+ * second-smallest ECE_k over the grid minus the smallest (+inf for a one-value grid). */
+void ora_sts_calibrate(int32_t n, int32_t gamma, const double* logit, const int32_t* n_accept,
+                       const double* temps, int32_t n_t, int32_t n_bins, double* t_out,
+                       double* ece_out, double* gap)
+{
+    double* q = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* sp = (double*)malloc(sizeof(double) * (size_t)n_bins);
+    double* sy = (double*)malloc(sizeof(double) * (size_t)n_bins);
+    double* cnt = (double*)malloc(sizeof(double) * (size_t)n_bins);
+    for (int s = 0; s < n; ++s) q[s] = 1.0;
+    for (int k = 1; k <= gamma; ++k) {
+        double best = INFINITY, second = INFINITY;
+        int best_i = 0;
+        for (int ti = 0; ti < n_t; ++ti) {
+            const double t = temps[ti];
+            for (int m = 0; m < n_bins; ++m) sp[m] = sy[m] = cnt[m] = 0.0;
+            for (int s = 0; s < n; ++s) {
+                const double c = 1.0 / (1.0 + exp(-logit[(size_t)s * gamma + (k - 1)] / t));
+                const double p = q[s] * c;
+                int m = (int)floor(p * n_bins);
+                if (m >= n_bins) m = n_bins - 1;
+                if (m < 0) m = 0;
+                sp[m] += p;
+                sy[m] += n_accept[s] >= k ? 1.0 : 0.0;
+                cnt[m] += 1.0;
+            }
+            double ece = 0.0;
+            for (int m = 0; m < n_bins; ++m)
+                if (cnt[m] > 0.0) ece += (cnt[m] / n) * fabs(sp[m] / cnt[m] - sy[m] / cnt[m]);
+            if (ece < best) {
+                second = best;
+                best = ece;
+                best_i = ti;
+            } else if (ece < second) {
+                second = ece;
+            }
+        }
+        t_out[k - 1] = temps[best_i];
+        ece_out[k - 1] = best;
+        if (gap) gap[k - 1] = second - best;
+        for (int s = 0; s < n; ++s)
+            q[s] = q[s] * (1.0 / (1.0 + exp(-logit[(size_t)s * gamma + (k - 1)] / t_out[k - 1])));
+    }
+    free(q);
+    free(sp);
+    free(sy);
+    free(cnt);
 }
 
 /* ------------------------------------------------------------------------------------ */

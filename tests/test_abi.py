@@ -77,6 +77,25 @@ def test_schedule_topk_argument_validation():
     assert L.dspark_schedule_topk(4, 4, P, P, -1, P, P, P, None, 0, None) == 4
 
 
+def test_sts_and_calibrated_confidence_validation():
+    L = ds.lib()
+    ws = 1 << 30
+    assert L.dspark_sts_calibrate(100, 4, None, P, P, 8, 15, P, P, P, ws, None) == 1
+    assert L.dspark_sts_calibrate(100, 4, P, P, P, 8, 15, P, None, P, ws, None) == 1
+    assert L.dspark_sts_calibrate(0, 4, P, P, P, 8, 15, P, P, P, ws, None) == 2
+    assert L.dspark_sts_calibrate((1 << 22) + 1, 4, P, P, P, 8, 15, P, P, P, ws, None) == 2
+    assert L.dspark_sts_calibrate(100, 65, P, P, P, 8, 15, P, P, P, ws, None) == 2
+    assert L.dspark_sts_calibrate(100, 4, P, P, P, 0, 15, P, P, P, ws, None) == 2
+    assert L.dspark_sts_calibrate(100, 4, P, P, P, 8, 257, P, P, P, ws, None) == 2
+    need = L.dspark_sts_workspace_bytes(100, 8, 15)
+    assert need >= 100 * 8 + 8 * 15 * 3 * 8
+    assert L.dspark_sts_calibrate(100, 4, P, P, P, 8, 15, P, P, P, need - 1, None) == 5
+    assert L.dspark_sts_calibrate(100, 4, P, P, P, 8, 15, P, P, None, need, None) == 5
+    dm = _dims()
+    assert L.dspark_confidence_calibrated(ctypes.byref(dm), P, 0, P, 0, P, 0, P, P, None, P,
+                                          None) == 1
+
+
 def test_verify_confidence_tv_validation():
     L = ds.lib()
     dm = _dims()

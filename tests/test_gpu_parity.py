@@ -194,6 +194,34 @@ def test_schedule_topk_bit_exact():
     assert np.array_equal(host(ell_g), host(ell_k)) and host(th_g)[0] == host(th_k)[0]
 
 
+@pytest.mark.parametrize("n,G,n_t,n_bins,seed", [
+    (50000, 6, 64, 15, 1),
+    (3001, 3, 7, 10, 2),          # a ragged last chunk, a short grid
+    (65536, 16, 256, 15, 3),      # the serve128 draft length, a fine grid
+])
+def test_sts_calibration_matches_oracle(n, G, n_t, n_bins, seed):
+    """Chosen temperatures exactly (the seeds keep every runner-up ECE at least 1e-9 away)
+    and ECE within 1e-9 (the GPU sums p in 2^-40 units)."""
+    cal = workload.calibration_inputs(n, G, seed=seed)
+    grid = np.geomspace(0.4, 5.0, n_t)
+    t_o, ece_o, gap_o = oracle.sts_calibrate(cal.logit, cal.n_accept, grid, n_bins)
+    assert np.all(gap_o >= 1e-9), gap_o
+    t_g, ece_g = ds.dspark_sts_calibrate(dev(cal.logit), dev(cal.n_accept), dev(grid), n_bins)
+    assert np.array_equal(host(t_g), t_o)
+    assert_abs(host(ece_g), ece_o, "sts ece", 1e-9)
+
+
+def test_calibrated_confidence_matches_oracle():
+    cfg = SMALL["bf16_rows_b16"]
+    inp = workload.generate(cfg, 1)
+    D = DeviceInputs(inp)
+    tokens = np.random.default_rng(3).integers(0, cfg.V, size=(cfg.B, cfg.gamma)).astype(np.int32)
+    temps = np.geomspace(0.6, 2.4, cfg.gamma)
+    c_o = oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tokens, temps)
+    c_g = ds.dspark_confidence_calibrated(D.h, D.W1, D.w, D.anchor, dev(tokens), dev(temps))
+    assert_rel(host(c_g), c_o, "calibrated confidence")
+
+
 # ------------------------------------------------------------------------------------
 # full-size workloads, sampled requests
 # ------------------------------------------------------------------------------------

@@ -326,6 +326,64 @@ def test_schedule_topk_edges_and_monotonicity():
 
 
 # ------------------------------------------------------------------------------------
+# sequential temperature scaling of the confidence head
+# ------------------------------------------------------------------------------------
+def test_sts_recovers_known_temperatures():
+    """Labels drawn so that sigmoid(logit / t*_k) is the true conditional acceptance: the
+    left-to-right search must find t*_k (within the grid's spacing and the sampling noise)
+    and leave the cumulative products calibrated, where the raw head (t = 1) is not."""
+    cal = workload.calibration_inputs(200000, 6, seed=1)
+    grid = np.geomspace(0.5, 4.0, 64)          # neighbouring values 3.4% apart
+    t, ece, gap = oracle.sts_calibrate(cal.logit, cal.n_accept, grid, 15)
+    step = np.log(grid[1] / grid[0])
+    assert np.all(np.abs(np.log(t / cal.t_true)) <= 2.5 * step), (t, cal.t_true)
+    assert np.all(ece < 0.006)
+    _, ece_raw, _ = oracle.sts_calibrate(cal.logit, cal.n_accept, np.array([1.0]), 15)
+    assert np.all(ece_raw > 3 * ece)
+
+
+def test_sts_calibrated_head_keeps_temperature_one():
+    cal = workload.calibration_inputs(200000, 4, seed=2, t_true=np.ones(4))
+    grid = np.geomspace(0.5, 2.0, 41)
+    t, _, _ = oracle.sts_calibrate(cal.logit, cal.n_accept, grid, 15)
+    assert np.all(np.abs(np.log(t)) <= 2.5 * np.log(grid[1] / grid[0]))
+
+
+def test_calibrated_confidence_is_the_scaled_logit():
+    """sigmoid(logit / t) from the calibrated head equals the plain head's c pushed back
+    through the logit: c' = sigmoid(log(c / (1 - c)) / t)."""
+    inp = workload.generate(workload.CONFIGS["tiny"], 2)
+    tokens = np.random.default_rng(1).integers(0, 1024, size=(4, 4)).astype(np.int32)
+    temps = np.array([0.5, 1.0, 1.7, 3.0])
+    c = oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tokens)
+    ct = oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tokens, temps)
+    assert np.allclose(ct, special.expit(special.logit(c) / temps), rtol=1e-12, atol=0)
+    assert np.array_equal(oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tokens,
+                                            np.ones(4)), c)
+
+
+def test_sts_ece_by_hand():
+    """Four samples, one position, t = 1: c = sigmoid(logit) put p at 0.1, 0.15 (bin 1 of
+    10), 0.5 (bin 5) and 0.9 (bin 9); labels 0, 1, 1, 1.
+    ECE = (2/4)|0.125 - 0.5| + (1/4)|0.5 - 1| + (1/4)|0.9 - 1| = 0.1875 + 0.125 + 0.025."""
+    p = np.array([0.1, 0.15, 0.5, 0.9])
+    logit = np.log(p / (1 - p))[:, None]
+    t, ece, gap = oracle.sts_calibrate(logit, np.array([0, 1, 1, 1]), np.array([1.0]), 10)
+    assert t[0] == 1.0 and np.isinf(gap[0])
+    assert ece[0] == pytest.approx(0.3375, abs=1e-15)
+
+
+def test_sts_one_value_grid_and_first_on_ties():
+    """A one-value grid returns that value at every position, with the ECE of the plain
+    products; a grid listing the same value twice chooses the first (a zero gap)."""
+    cal = workload.calibration_inputs(5000, 3, seed=3)
+    t, ece, _ = oracle.sts_calibrate(cal.logit, cal.n_accept, np.array([1.7]), 12)
+    assert np.all(t == 1.7)
+    t2, ece2, gap2 = oracle.sts_calibrate(cal.logit, cal.n_accept, np.array([1.7, 1.7]), 12)
+    assert np.array_equal(t2, t) and np.array_equal(ece2, ece) and np.all(gap2 == 0.0)
+
+
+# ------------------------------------------------------------------------------------
 # verification
 # ------------------------------------------------------------------------------------
 def test_verify_identical_target_accepts_everything():

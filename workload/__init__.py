@@ -236,3 +236,31 @@ def synthesize_target(inp: RoundInputs, tokens: np.ndarray, rows: Optional[np.nd
         noise = rng.standard_normal(size=(G + 1, V), dtype=np.float32)
         T[i] = base + bias + inp.sigma[b][:, None] * noise
     return T
+
+
+# ------------------------------------------------------------------------------------
+# held-out data for calibrating the confidence head
+# ------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class CalibrationInputs:
+    logit: np.ndarray      # [n][gamma] float32 confidence logits of an over-confident head
+    n_accept: np.ndarray   # [n] int32 accepted prefix lengths
+    t_true: np.ndarray     # [gamma] float64 temperature that makes the head calibrated
+
+
+def calibration_inputs(n: int, gamma: int, seed: int = 0,
+                       t_true: Optional[np.ndarray] = None) -> CalibrationInputs:
+    """n held-out drafted blocks.  The logit of position k is N(2 - 0.1 k, 2^2); the
+    position is accepted, given the earlier ones were, with probability
+    sigmoid(logit / t_true[k-1]) (by default t_true[k-1] = 1.3 + 0.05 k: a head that is
+    over-confident by that temperature); n_accept is the length of the accepted prefix."""
+    rng = np.random.Generator(np.random.PCG64([0xCA11B8, seed, n, gamma]))
+    k = np.arange(1, gamma + 1)
+    if t_true is None:
+        t_true = 1.3 + 0.05 * k
+    t_true = np.asarray(t_true, np.float64)
+    logit = (rng.normal(size=(n, gamma)) * 2.0 + (2.0 - 0.1 * k)).astype(np.float32)
+    p_acc = 1.0 / (1.0 + np.exp(-logit.astype(np.float64) / t_true))
+    ok = rng.random((n, gamma)) < p_acc
+    alive = np.cumprod(ok, axis=1)
+    return CalibrationInputs(logit, alive.sum(axis=1).astype(np.int32), t_true)
