@@ -64,6 +64,9 @@ def _load():
                                            ctypes.c_int32, _P, _P, _P]
         lib.ora_sts_calibrate.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                           ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+        lib.ora_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                       _P, _P, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_double, _P, _P, _P, _P]
         lib.ora_verify.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_double, ctypes.c_uint64, _P, _P, _P, _P, _P, _P]
         lib.ora_accept_tv.argtypes = [ctypes.POINTER(_Dims), _P, _P, _P, _P, _P, _P,
@@ -231,6 +234,29 @@ def sts_calibrate(logit, n_accept, temps, n_bins=15):
     lib.ora_sts_calibrate(n, G, _ptr(logit), _ptr(n_accept), _ptr(temps), temps.shape[0],
                           int(n_bins), _ptr(t), _ptr(ece), _ptr(gap))
     return t, ece, gap
+
+
+def draft_loss(zd, zt, labels, conf_logit, alphas=(0.1, 0.9, 1.0), grads=True):
+    """Distribution-matching training loss and its gradients.
+
+    zd, zt [B][gamma][V] draft and target logits, labels [B][gamma] true next tokens,
+    conf_logit [B][gamma].  Returns dict(loss, terms [B][gamma][3] (ce, l1, bce),
+    grad_zd [B][gamma][V], grad_conf [B][gamma]) (gradients None when grads is False)."""
+    lib = _load()
+    zd = _f64(zd)
+    B, G, V = zd.shape
+    zt = _f64(zt)
+    assert zt.shape == zd.shape
+    labels = _i32(labels)
+    conf_logit = _f64(conf_logit)
+    loss = np.zeros(1)
+    terms = np.zeros((B, G, 3))
+    gz = np.zeros((B, G, V)) if grads else None
+    gc = np.zeros((B, G)) if grads else None
+    a_ce, a_l1, a_cf = (float(x) for x in alphas)
+    lib.ora_draft_loss(B, G, V, _ptr(zd), _ptr(zt), _ptr(labels), _ptr(conf_logit), a_ce, a_l1,
+                       a_cf, _ptr(loss), _ptr(terms), _ptr(gz), _ptr(gc))
+    return {"loss": float(loss[0]), "terms": terms, "grad_zd": gz, "grad_conf": gc}
 
 
 def verify(U, W1, W2t, anchor, tokens, T, ell, temperature, seed, gid=None):

@@ -34,6 +34,8 @@
  *                                        own admitted count, Monte-Carlo losslessness)
  *   ora_sts_calibrate .................. pinned (recovery of known per-position
  *                                        temperatures, hand-computed ECE, one-value grids)
+ *   ora_draft_loss ..................... pinned (central finite differences of the loss,
+ *                                        p_d = p_t and one-hot special cases)
  *   ora_verify ......................... pinned (Monte-Carlo losslessness against the
  *                                        target law, special cases)
  *   ora_accept_tv ...................... pinned (TV identity, Monte-Carlo acceptance rate)
@@ -373,6 +375,94 @@ void ora_sts_calibrate(int32_t n, int32_t gamma, const double* logit, const int3
     free(sp);
     free(sy);
     free(cnt);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Distribution-matching training loss of the draft and confidence heads [XTL §9: a       */
+/* cross-entropy term on the true next token, an L1 (total-variation) term between the    */
+/* draft and target distributions, a binary cross-entropy term training the confidence    */
+/* head on the soft accept rate 1 - |p_d - p_t|_1 / 2, position weights exp(-(k-1)/gamma);*/
+/* XTL §8: the open configuration weights them 0.1, 0.9 and 1.0].                         */
+/* ------------------------------------------------------------------------------------ */
+/* Rows (b, k), k = 1..gamma, of draft logits zd and target logits zt ([B][gamma][V]):
+ *   p_d = softmax(zd), p_t = softmax(zt)
+ *   ce  = -log p_d(y)                       y = labels[b][k-1], the true next token
+ *   l1  = sum_v |p_d(v) - p_t(v)|           (twice the total-variation distance)
+ *   a   = 1 - l1 / 2                        the soft accept rate (a fixed target)
+ *   bce = -(a log c + (1 - a) log(1 - c)),  c = sigmoid(conf_logit[b][k-1]),
+ *         evaluated as log(1 + exp(l)) - a l
+ *   w_k = exp(-(k-1)/gamma),  W = B * sum_k w_k
+ *   loss = sum_{b,k} w_k (alpha_ce ce + alpha_l1 l1 + alpha_conf bce) / W
+ * Gradients (a and p_t held fixed):
+ *   dloss/dzd[j]  = w_k/W (alpha_ce (p_d(j) - [j = y]) + alpha_l1 p_d(j) (s_j - S)),
+ *                   s_j = sign(p_d(j) - p_t(j)) (0 at equality), S = sum_v s_v p_d(v)
+ *   dloss/dconf_logit = w_k/W alpha_conf (c - a)
+ * terms[row][0..2] = (ce, l1, bce) when terms is not NULL. */
+void ora_draft_loss(int32_t B, int32_t gamma, int32_t V, const double* zd, const double* zt,
+                    const int32_t* labels, const double* conf_logit, double alpha_ce,
+                    double alpha_l1, double alpha_conf, double* loss, double* terms,
+                    double* grad_zd, double* grad_conf)
+{
+    double* pd = (double*)malloc(sizeof(double) * (size_t)V);
+    double* pt = (double*)malloc(sizeof(double) * (size_t)V);
+    double wsum = 0.0;
+    for (int k = 1; k <= gamma; ++k) wsum += exp(-(double)(k - 1) / gamma);
+    const double W = B * wsum;
+    double total = 0.0;
+    for (int b = 0; b < B; ++b) {
+        for (int k = 1; k <= gamma; ++k) {
+            const size_t row = (size_t)b * gamma + (k - 1);
+            const double* xd = zd + row * V;
+            const double* xt = zt + row * V;
+            double md = xd[0], mt = xt[0];
+            for (int v = 1; v < V; ++v) {
+                if (xd[v] > md) md = xd[v];
+                if (xt[v] > mt) mt = xt[v];
+            }
+            double sd = 0.0, st = 0.0;
+            for (int v = 0; v < V; ++v) {
+                sd += exp(xd[v] - md);
+                st += exp(xt[v] - mt);
+            }
+            const double lse_d = md + log(sd), lse_t = mt + log(st);
+            double l1 = 0.0, S = 0.0;
+            for (int v = 0; v < V; ++v) {
+                pd[v] = exp(xd[v] - lse_d);
+                pt[v] = exp(xt[v] - lse_t);
+                const double diff = pd[v] - pt[v];
+                l1 += fabs(diff);
+                S += (diff > 0.0 ? 1.0 : (diff < 0.0 ? -1.0 : 0.0)) * pd[v];
+            }
+            int y = labels[row];
+            if (y < 0) y = 0;
+            if (y >= V) y = V - 1;
+            const double ce = lse_d - xd[y];
+            const double a = 1.0 - 0.5 * l1;
+            const double l = conf_logit[row];
+            const double softplus = l > 0.0 ? l + log1p(exp(-l)) : log1p(exp(l));
+            const double bce = softplus - a * l;
+            const double c = 1.0 / (1.0 + exp(-l));
+            const double wk = exp(-(double)(k - 1) / gamma) / W;
+            total += wk * (alpha_ce * ce + alpha_l1 * l1 + alpha_conf * bce);
+            if (terms) {
+                terms[row * 3 + 0] = ce;
+                terms[row * 3 + 1] = l1;
+                terms[row * 3 + 2] = bce;
+            }
+            if (grad_zd) {
+                for (int v = 0; v < V; ++v) {
+                    const double diff = pd[v] - pt[v];
+                    const double sv = diff > 0.0 ? 1.0 : (diff < 0.0 ? -1.0 : 0.0);
+                    grad_zd[row * V + v] =
+                        wk * (alpha_ce * (pd[v] - (v == y ? 1.0 : 0.0)) + alpha_l1 * pd[v] * (sv - S));
+                }
+            }
+            if (grad_conf) grad_conf[row] = wk * alpha_conf * (c - a);
+        }
+    }
+    *loss = total;
+    free(pd);
+    free(pt);
 }
 
 /* ------------------------------------------------------------------------------------ */

@@ -570,3 +570,137 @@ def test_tv_is_one_for_identical_and_zero_for_disjoint():
     T = np.full((2, 3, 64), -1e4, np.float32); T[:, :, 32:] = 0
     alpha, _ = oracle.accept_tv(U, inp.W1, W2t, inp.anchor, tok, T, 1.0)
     assert np.all(alpha < 1e-300)
+
+
+# ------------------------------------------------------------------------------------
+# distribution-matching training loss
+# ------------------------------------------------------------------------------------
+ALPHAS = (0.1, 0.9, 1.0)
+
+
+def test_draft_loss_by_hand():
+    """B=1, gamma=2, V=2 worked by hand.
+    Row k=1: p_d = (1/2, 1/2), p_t = (3/4, 1/4), y = 0, confidence logit 0:
+      l1 = 1/2, a = 3/4, ce = ln 2, bce = ln 2; signs (-1, +1), S = 0;
+      per-unit-weight gradient 0.1 (p_d - e_0) + 0.9 p_d (s - S) = (-1/2, 1/2),
+      confidence gradient c - a = -1/4.
+    Row k=2: p_d = (3/4, 1/4), p_t = (1/2, 1/2), y = 1, confidence logit ln 3 (c = 3/4):
+      l1 = 1/2, a = 3/4, ce = ln 4, bce = ln 4 - (3/4) ln 3; signs (+1, -1), S = 1/2;
+      gradient 0.1 (3/4, -3/4) + 0.9 (3/8, -3/8) = (0.4125, -0.4125), confidence 0.
+    Weights 1 and e^{-1/2}, normalised by their sum."""
+    ln2, ln3, ln4 = np.log(2.0), np.log(3.0), np.log(4.0)
+    zd = np.array([[[0.0, 0.0], [ln3, 0.0]]])
+    zt = np.array([[[ln3, 0.0], [0.0, 0.0]]])
+    labels = np.array([[0, 1]])
+    cl = np.array([[0.0, ln3]])
+    r = oracle.draft_loss(zd, zt, labels, cl, ALPHAS)
+    w2 = np.exp(-0.5)
+    W = 1.0 + w2
+    t1 = 0.1 * ln2 + 0.9 * 0.5 + ln2
+    t2 = 0.1 * ln4 + 0.9 * 0.5 + (ln4 - 0.75 * ln3)
+    assert r["loss"] == pytest.approx((t1 + w2 * t2) / W, rel=1e-14)
+    np.testing.assert_allclose(r["terms"][0], [[ln2, 0.5, ln2], [ln4, 0.5, ln4 - 0.75 * ln3]],
+                               rtol=1e-14)
+    np.testing.assert_allclose(r["grad_zd"][0], [[-0.5 / W, 0.5 / W],
+                                                 [0.4125 * w2 / W, -0.4125 * w2 / W]],
+                               rtol=1e-13)
+    np.testing.assert_allclose(r["grad_conf"][0], [-0.25 / W, 0.0], atol=1e-15)
+
+
+def _loss_case(seed, B=2, G=3, V=7):
+    rng = np.random.default_rng(seed)
+    zt = rng.normal(size=(B, G, V)) * 2.0
+    zd = zt + rng.normal(size=(B, G, V)) * 0.7
+    labels = rng.integers(0, V, size=(B, G))
+    cl = rng.normal(size=(B, G)) * 1.5
+    return zd, zt, labels, cl
+
+
+@pytest.mark.parametrize("alphas", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.1, 0.9, 0.0)])
+def test_draft_loss_gradient_finite_differences(alphas):
+    """Central differences of the loss in every draft logit (the confidence term off, so
+    that the soft label, held fixed by the gradient, plays no part)."""
+    zd, zt, labels, cl = _loss_case(11)
+    g = oracle.draft_loss(zd, zt, labels, cl, alphas)["grad_zd"]
+    h = 1e-6
+    fd = np.zeros_like(zd)
+    for idx in np.ndindex(zd.shape):
+        zp = zd.copy()
+        zm = zd.copy()
+        zp[idx] += h
+        zm[idx] -= h
+        fd[idx] = (oracle.draft_loss(zp, zt, labels, cl, alphas, grads=False)["loss"] -
+                   oracle.draft_loss(zm, zt, labels, cl, alphas, grads=False)["loss"]) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-9)
+
+
+def test_draft_loss_confidence_gradient_finite_differences():
+    zd, zt, labels, cl = _loss_case(12)
+    g = oracle.draft_loss(zd, zt, labels, cl, ALPHAS)["grad_conf"]
+    h = 1e-6
+    for idx in np.ndindex(cl.shape):
+        cp = cl.copy()
+        cm = cl.copy()
+        cp[idx] += h
+        cm[idx] -= h
+        fd = (oracle.draft_loss(zd, zt, labels, cp, ALPHAS, grads=False)["loss"] -
+              oracle.draft_loss(zd, zt, labels, cm, ALPHAS, grads=False)["loss"]) / (2 * h)
+        assert g[idx] == pytest.approx(fd, rel=1e-6, abs=1e-10)
+
+
+def test_draft_loss_soft_label_is_held_fixed():
+    """The confidence term trains only the confidence head: the draft-logit gradient does
+    not depend on its weight, and is the softmax Jacobian applied to the other terms."""
+    zd, zt, labels, cl = _loss_case(13)
+    g1 = oracle.draft_loss(zd, zt, labels, cl, (0.1, 0.9, 1.0))["grad_zd"]
+    g0 = oracle.draft_loss(zd, zt, labels, cl, (0.1, 0.9, 0.0))["grad_zd"]
+    np.testing.assert_array_equal(g1, g0)
+    # softmax invariance: every row of the gradient sums to zero
+    assert np.abs(g1.sum(axis=2)).max() < 1e-15
+
+
+def test_draft_loss_cross_entropy_is_the_library_one():
+    """With only the cross-entropy term on, the loss is the position-weighted mean of
+    -log_softmax at the labels (scipy), and the gradient is softmax minus one-hot."""
+    zd, zt, labels, cl = _loss_case(14, B=3, G=4, V=9)
+    r = oracle.draft_loss(zd, zt, labels, cl, (1.0, 0.0, 0.0))
+    ls = special.log_softmax(zd, axis=2)
+    ce = -np.take_along_axis(ls, labels[..., None], axis=2)[..., 0]
+    w = np.exp(-np.arange(4) / 4.0)
+    assert r["loss"] == pytest.approx((ce * w).sum() / (3 * w.sum()), rel=1e-13)
+    np.testing.assert_allclose(r["terms"][..., 0], ce, rtol=1e-13)
+    onehot = np.eye(9)[labels]
+    np.testing.assert_allclose(r["grad_zd"], (np.exp(ls) - onehot) * w[None, :, None] /
+                               (3 * w.sum()), rtol=1e-12, atol=1e-16)
+
+
+def test_draft_loss_identical_distributions():
+    """p_d = p_t (draft logits shifted per row): no L1 term, soft label 1, so the
+    confidence term is -log sigmoid(l) (scipy's log_expit) and its gradient c - 1."""
+    _, zt, labels, cl = _loss_case(15)
+    zd = zt + np.arange(6).reshape(2, 3, 1) * 0.37
+    r = oracle.draft_loss(zd, zt, labels, cl, ALPHAS)
+    assert np.abs(r["terms"][..., 1]).max() < 1e-14
+    np.testing.assert_allclose(r["terms"][..., 2], -special.log_expit(cl), rtol=1e-13)
+    w = np.exp(-np.arange(3) / 3.0)
+    np.testing.assert_allclose(r["grad_conf"], (special.expit(cl) - 1.0) * w / (2 * w.sum()),
+                               rtol=1e-12)
+    # identical logits: every difference is exactly zero, its sign taken as 0, so the L1
+    # term adds nothing to the gradient
+    g_l1 = oracle.draft_loss(zt.copy(), zt, labels, cl, (0.0, 1.0, 0.0))["grad_zd"]
+    assert np.abs(g_l1).max() == 0.0
+
+
+def test_draft_loss_disjoint_distributions():
+    """Draft and target put their mass on different tokens: L1 -> 2, soft label -> 0, so
+    the confidence term is softplus(l) = -log(1 - sigmoid(l))."""
+    V = 6
+    zd = np.full((1, 1, V), -60.0)
+    zt = np.full((1, 1, V), -60.0)
+    zd[0, 0, 1] = 0.0
+    zt[0, 0, 4] = 0.0
+    cl = np.array([[0.8]])
+    r = oracle.draft_loss(zd, zt, np.array([[4]]), cl, ALPHAS)
+    assert r["terms"][0, 0, 1] == pytest.approx(2.0, abs=1e-15)
+    assert r["terms"][0, 0, 2] == pytest.approx(-special.log_expit(-0.8), rel=1e-12)
+    assert r["terms"][0, 0, 0] == pytest.approx(60.0, rel=1e-12)
