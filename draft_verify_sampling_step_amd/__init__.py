@@ -86,13 +86,19 @@ def lib() -> ctypes.CDLL:
             L.dspark_rng_uniforms.argtypes = [_U64, ctypes.c_uint32, ctypes.c_uint32,
                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
                                               _P, _P]
+            L.dspark_loss_workspace_bytes.argtypes = [ctypes.c_int32] * 3
+            L.dspark_loss_workspace_bytes.restype = _SZ
+            L.dspark_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            _P, _P, _P, _P, ctypes.c_double, ctypes.c_double,
+                                            ctypes.c_double, _P, _P, _P, _P, _P, _SZ, _P]
             L.dspark_profile_start.argtypes = [_I]
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(_I),
                                               ctypes.POINTER(ctypes.c_double)]
             for fn in ("dspark_draft_markov", "dspark_confidence",
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
-                       "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv", "dspark_rng_uniforms",
+                       "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
+                       "dspark_draft_loss", "dspark_rng_uniforms",
                        "dspark_profile_start", "dspark_profile_stop"):
                 getattr(L, fn).restype = _I
             _lib = L
@@ -248,6 +254,37 @@ def dspark_sts_calibrate(logit, n_accept, temps, n_bins: int = 15, out=None, ws=
                                       int(n_bins), _ptr(t_out), _ptr(ece_out), _ptr(w),
                                       w.numel(), _stream_handle(stream)))
     return t_out, ece_out
+
+
+def dspark_draft_loss(zd, zt, labels, conf_logit, alphas=(0.1, 0.9, 1.0), grads=True,
+                      terms=True, out=None, ws=None, stream=None):
+    """Distribution-matching training loss: zd, zt [B][gamma][V] f32, labels [B][gamma]
+    int32, conf_logit [B][gamma] f32.  Returns (loss [1] f64, terms [B][gamma][3] f32 or
+    None, grad_zd [B][gamma][V] f32 or None, grad_conf [B][gamma] f32 or None)."""
+    B, G, V = zd.shape
+    _f32(zd, "zd")
+    _f32(zt, "zt")
+    _i32(labels, "labels")
+    _f32(conf_logit, "conf_logit")
+    if tuple(zt.shape) != (B, G, V) or tuple(labels.shape) != (B, G) or \
+            tuple(conf_logit.shape) != (B, G):
+        raise ValueError("zt must match zd; labels and conf_logit must be [B][gamma]")
+    dev = zd.device
+    if out is None:
+        out = (torch.empty(1, dtype=torch.float64, device=dev),
+               torch.empty(B, G, 3, dtype=torch.float32, device=dev) if terms else None,
+               torch.empty(B, G, V, dtype=torch.float32, device=dev) if grads else None,
+               torch.empty(B, G, dtype=torch.float32, device=dev) if grads else None)
+    loss, t, gz, gc = out
+    need = int(lib().dspark_loss_workspace_bytes(B, G, V))
+    if need == 0:
+        raise DsparkError("dspark_loss_workspace_bytes: shape out of range")
+    w = _workspace(dev, need, ws)
+    a_ce, a_l1, a_cf = (float(x) for x in alphas)
+    _check(lib().dspark_draft_loss(B, G, V, _ptr(zd), _ptr(zt), _ptr(labels), _ptr(conf_logit),
+                                   a_ce, a_l1, a_cf, _ptr(loss), _ptr(t), _ptr(gz), _ptr(gc),
+                                   _ptr(w), w.numel(), _stream_handle(stream)))
+    return loss, t, gz, gc
 
 
 def dspark_schedule(c, sps, mode: int = SCHED_GREEDY, out=None, stream=None):

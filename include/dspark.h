@@ -18,6 +18,9 @@
  *      dspark_schedule_topk  its production form: top-K admission, K from history [XTL §7]
  *   4. dspark_verify         lossless rejection-sampling verification         [XTL §1; AIMSG 2]
  *   5. dspark_accept_rate_tv analytic accept rate 1 - |p_d - p_t|_1 / 2       [CSDN Eq. 8; XTL §5]
+ * and, on the training side of the same heads:
+ *   6. dspark_draft_loss     distribution-matching loss (CE + L1 + confidence BCE, position
+ *                            weights) and its gradients                   [XTL §9, §5, §8]
  *
  * Conventions shared by every call:
  *   - Tensor arguments are DEVICE pointers to row-major contiguous arrays owned by the
@@ -254,6 +257,44 @@ dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, con
                                     const int32_t* tokens, const float* lse, const float* T,
                                     float temperature, float* alpha, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/*
+ * Distribution-matching training loss of the draft and confidence heads, forward and
+ * backward [XTL §9: a cross-entropy term on the true next token, an L1 (total-variation)
+ * term between the draft and target distributions, a binary cross-entropy term training
+ * the confidence head on the soft accept rate, position weights exp(-(k-1)/gamma); XTL §5:
+ * the soft label 1 - |p_d - p_t|_1 / 2 from the two softmaxes; XTL §8: the open
+ * configuration weighs the terms 0.1, 0.9 and 1.0].  For each row (b, k), k = 1..gamma:
+ *   p_d = softmax(zd[b][k-1]), p_t = softmax(zt[b][k-1]), y = labels[b][k-1]
+ *   ce  = -log p_d(y),  l1 = sum_v |p_d(v) - p_t(v)|,  a = 1 - l1 / 2 (a fixed target)
+ *   bce = log(1 + exp(l)) - a l,  l = conf_logit[b][k-1],  c = sigmoid(l)
+ *   loss = sum_{b,k} w_k (alpha_ce ce + alpha_l1 l1 + alpha_conf bce) / (B sum_k w_k),
+ *          w_k = exp(-(k-1)/gamma)
+ *   grad_zd[j]  = w_k / (B sum w) (alpha_ce (p_d(j) - [j = y]) + alpha_l1 p_d(j) (s_j - S)),
+ *                 s_j = sign(p_d(j) - p_t(j)) (0 at equality), S = sum_v s_v p_d(v)
+ *   grad_conf   = w_k / (B sum w) alpha_conf (c - a)
+ * The soft label is held fixed: the confidence term sends no gradient into zd.
+ *   zd, zt      [B][gamma][V] fp32 draft and target logits, 1 <= V <= 2^22.
+ *   labels      [B][gamma] int32 true next tokens (clamped into [0, V) where used).
+ *   conf_logit  [B][gamma] fp32 confidence-head logits.
+ *   alpha_*     finite term weights (else DSPARK_E_VALUE).
+ *   loss        out [1] fp64; NaN if the workgroups of a row failed to meet (see below).
+ *   terms       out [B][gamma][3] fp32 (ce, l1, bce) per row, or NULL.
+ *   grad_zd     out [B][gamma][V] fp32, or NULL (forward only).
+ *   grad_conf   out [B][gamma] fp32, or NULL.
+ * One cooperative launch: the vocabulary of a row is split over up to 1024 workgroups that
+ * exchange partial sums through the workspace and wait for each other with bounded polls;
+ * DSPARK_E_HIP if the device cannot run the grid resident at once.  Rows run in a fixed
+ * order and every sum has a fixed order, so results are bit-reproducible.  Workspace:
+ * dspark_loss_workspace_bytes(B, gamma, V) bytes.
+ */
+size_t dspark_loss_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab);
+dspark_status dspark_draft_loss(int32_t batch, int32_t gamma, int32_t vocab, const float* zd,
+                                const float* zt, const int32_t* labels,
+                                const float* conf_logit, double alpha_ce, double alpha_l1,
+                                double alpha_conf, double* loss, float* terms,
+                                float* grad_zd, float* grad_conf, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * The uniforms of the random-number definition above, for checking the generator:

@@ -96,6 +96,26 @@ def test_sts_and_calibrated_confidence_validation():
                                           None) == 1
 
 
+def test_draft_loss_validation():
+    L = ds.lib()
+    ws = 1 << 30
+    f = L.dspark_draft_loss
+    assert f(2, 4, 100, None, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, ws, None) == 1
+    assert f(2, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, None, None, P, P, P, ws, None) == 1
+    assert f(0, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, ws, None) == 2
+    assert f(2, 65, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, ws, None) == 2
+    assert f(2, 4, (1 << 22) + 1, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, ws, None) == 2
+    assert f(2, 4, 100, P, P, P, P, float("nan"), 0.9, 1.0, P, None, P, P, P, ws, None) == 4
+    assert f(2, 4, 100, P, P, P, P, 0.1, float("inf"), 1.0, P, None, P, P, P, ws, None) == 4
+    need = L.dspark_loss_workspace_bytes(2, 4, 100)
+    assert need >= 8 * (6 + 1) * 8 + 8 * 2 * 4
+    assert L.dspark_loss_workspace_bytes(2, 4, 0) == 0
+    assert f(2, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, need - 1, None) == 5
+    assert f(2, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, None, need, None) == 5
+    # the vocabulary is split into ceil(V / 4096) chunks of partials per row
+    assert L.dspark_loss_workspace_bytes(128, 16, 151936) >= 2048 * 38 * 6 * 8
+
+
 def test_verify_confidence_tv_validation():
     L = ds.lib()
     dm = _dims()

@@ -239,6 +239,43 @@ def synthesize_target(inp: RoundInputs, tokens: np.ndarray, rows: Optional[np.nd
 
 
 # ------------------------------------------------------------------------------------
+# a training batch of the draft and confidence heads
+# ------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class TrainingInputs:
+    zd: np.ndarray         # [B][gamma][V] float32 draft logits
+    zt: np.ndarray         # [B][gamma][V] float32 target logits
+    labels: np.ndarray     # [B][gamma] int32 true next tokens
+    conf_logit: np.ndarray  # [B][gamma] float32 confidence-head logits
+
+
+def training_inputs(cfg: Config, seed: int = 0, B: Optional[int] = None) -> TrainingInputs:
+    """One training batch of B (default cfg.B) blocks of gamma positions.
+    Target logits: the configuration's base-logit family.  Draft logits: the target's plus
+    N(0, s_k^2) with s_k = 2 (sigma0 + sigma1 k), so the draft drifts from the target with
+    depth.  Labels: the target's argmax with probability 0.7, else a uniform token.
+    Confidence logits: N(1, 1.5^2)."""
+    B = cfg.B if B is None else int(B)
+    G, V = cfg.gamma, cfg.V
+    rng = _rng(seed, cfg, 7)
+    R = B * G
+    zt = _base_logits(rng, cfg, R, np.arange(R))
+    zd = np.empty_like(zt)
+    s_k = 2.0 * (cfg.sigma0 + cfg.sigma1 * np.arange(1, G + 1))
+    for i in range(0, R, 256):
+        n = min(256, R - i)
+        noise = rng.standard_normal(size=(n, V), dtype=np.float32)
+        noise *= s_k[(np.arange(i, i + n) % G)].astype(np.float32)[:, None]
+        zd[i:i + n] = zt[i:i + n] + noise
+    top = np.argmax(zt, axis=1)
+    uni = rng.integers(0, V, size=R)
+    labels = np.where(rng.random(R) < 0.7, top, uni).astype(np.int32)
+    conf = (rng.normal(size=R) * 1.5 + 1.0).astype(np.float32)
+    return TrainingInputs(zd.reshape(B, G, V), zt.reshape(B, G, V), labels.reshape(B, G),
+                          conf.reshape(B, G))
+
+
+# ------------------------------------------------------------------------------------
 # held-out data for calibrating the confidence head
 # ------------------------------------------------------------------------------------
 @dataclasses.dataclass
