@@ -168,6 +168,17 @@ def main():
     log(f"draft sampling kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches of "
         f"{kern_pos:g} positions each")
 
+    # verification alone (rows pass, decisions, residual pass, final), same inputs as a step
+    vf0 = torch.cuda.Event(enable_timing=True)
+    vf1 = torch.cuda.Event(enable_timing=True)
+    vf0.record(stream)
+    for _ in range(args.steps):
+        ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, inp.seed,
+                         out=(nacc, outtok, None), ws=ws_v)
+    vf1.record(stream)
+    torch.cuda.synchronize()
+    verify_ms = vf0.elapsed_time(vf1) / args.steps
+
     # the production form of the scheduler (top-K admission, K from history): timed alone at
     # this round's admitted count; one workgroup, latency-bound, so reported in us only
     k_admit = int(ntot.cpu()[0]) - B
@@ -253,6 +264,8 @@ def main():
             "launches": kern_n,
         },
         "draft_call_ms": round(draft_ms, 4),
+        "verify_call_ms": round(verify_ms, 4),
+        "verify_hbm_frac": round(verify_bytes / (verify_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
         "schedule_topk_us": round(topk_us, 2),
