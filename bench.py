@@ -211,6 +211,32 @@ def main():
     torch.cuda.synchronize()
     sts_ms = sc0.elapsed_time(sc1) / 3
 
+    # training side: the distribution-matching loss, forward and backward, over a batch of
+    # this shape (B blocks of gamma positions, draft and target logits over V); HBM-bound at
+    # 12 bytes per logit (read draft and target, write the gradient)
+    log("training loss: generating a batch")
+    tr = workload.training_inputs(cfg, args.seed)
+    zd_t, zt_t = ds.to_device(tr.zd), ds.to_device(tr.zt)
+    lab_t, cl_t = ds.to_device(tr.labels), ds.to_device(tr.conf_logit)
+    del tr
+    loss_out = (torch.empty(1, dtype=torch.float64, device=dev),
+                torch.empty(B, G, 3, dtype=torch.float32, device=dev),
+                torch.empty_like(zd_t), torch.empty(B, G, dtype=torch.float32, device=dev))
+    for _ in range(2):
+        ds.dspark_draft_loss(zd_t, zt_t, lab_t, cl_t, out=loss_out)
+    lo0 = torch.cuda.Event(enable_timing=True)
+    lo1 = torch.cuda.Event(enable_timing=True)
+    lo0.record(stream)
+    for _ in range(5):
+        ds.dspark_draft_loss(zd_t, zt_t, lab_t, cl_t, out=loss_out)
+    lo1.record(stream)
+    torch.cuda.synchronize()
+    loss_ms = lo0.elapsed_time(lo1) / 5
+    loss_val = float(loss_out[0].cpu()[0])
+    loss_bytes = B * G * V * 12
+    del zd_t, zt_t, loss_out
+    torch.cuda.empty_cache()
+
     # algorithmic bytes (what the method must move), from this round's realised ell, n
     ell_h = ell.cpu().numpy().astype(np.int64)
     n_h = nacc.cpu().numpy().astype(np.int64)
@@ -271,6 +297,9 @@ def main():
         "schedule_topk_us": round(topk_us, 2),
         "sts_calibrate_ms": round(sts_ms, 4),
         "sts_sigmoids_per_s": round(131072 * 256 * G / (sts_ms * 1e-3), 1),
+        "loss_call_ms": round(loss_ms, 4),
+        "loss_hbm_frac": round(loss_bytes / (loss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "loss_value": round(loss_val, 6),
         "accepted_mean": round(float(n_h.mean()), 3),
         "verify_tokens": int((ell_h + 1).sum()),
     }

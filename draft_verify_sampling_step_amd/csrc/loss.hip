@@ -41,11 +41,17 @@
 
 namespace dspark {
 
-constexpr int kLossComputeWaves = 4;
-constexpr int kLossThreads = (kLossComputeWaves + 1) * kWave;   // + the control wave
-constexpr int kLossPer = 16;                                     // entries per lane per row
-constexpr int kLossChunk = kLossComputeWaves * kWave * kLossPer;  // 4096 entries
+constexpr int kLossWaves = 4;                             // every wave holds entries
+constexpr int kLossThreads = kLossWaves * kWave;          // 256: one wave per SIMD
+constexpr int kLossPer = 16;                              // entries per lane per row
+constexpr int kLossChunk = kLossThreads * kLossPer;       // 4096 entries
 constexpr int kLossMaxVocab = 1 << 22;
+// Arrival counters sit 128 bytes apart: the pollers of rows in flight at once never share
+// a line.
+constexpr int kCntStride = 32;
+// Polls of a counter between two looks at the fault word (every poller reading one shared
+// word each time would make it a hot spot).
+constexpr uint32_t kFaultCheckPolls = 64;
 
 struct LossArgs {
   const float* zd;
@@ -58,7 +64,7 @@ struct LossArgs {
   double* rowloss;      // [R] weighted row contributions
   double* part1;        // [R][C][4] (max_d, sum_d, max_t, sum_t)
   double* part2;        // [R][C][2] (l1, S)
-  uint32_t* cnt;        // [R][2] arrivals per row and exchange
+  uint32_t* cnt;        // [R + P][kCntStride]: arrivals per exchange (word 0 used)
   uint32_t* fault;
   int R, G, V, C, L, P;
   double a_ce, a_l1, a_conf, inv_W;
@@ -67,7 +73,7 @@ struct LossArgs {
 
 __device__ __forceinline__ void raw_barrier() {
   // LDS writes complete, then a barrier without the release fence of __syncthreads()
-  // (that fence would wait for the register prefetch as well)
+  // (that fence would wait for the LDS prefetch as well)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -78,34 +84,44 @@ __device__ __forceinline__ void st_dev(double* p, double v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Control wave: publish this workgroup's partials (n doubles, held by lanes 0..n-1), arrive
-// on the row's counter, wait for all C arrivals.  Lane 0 does the stores, the releasing
-// increment and the polling; the whole wave then takes the acquire.  Returns false when the
-// wait gave up.
-__device__ __forceinline__ bool exchange(const LossArgs& a, double* slot, int n, double v,
-                                         uint32_t* counter, int lane) {
-  double vals[4];
+// Wave 0: publish this workgroup's partials -- lanes 0..na-1 hold the values of slot_a,
+// lanes na..na+nb-1 those of slot_b -- arrive on the exchange's counter and wait for all C
+// arrivals.  Lane 0 does the stores, the increment and the polling.  Every access to the
+// exchanged words is a device-scope atomic (they bypass the non-coherent caches), so the
+// ordering needs no cache-wide fence: the partials' stores are complete (s_waitcnt) before
+// the increment is issued, and the partials are loaded only after the poll has seen every
+// increment.  (A release/acquire fence pair would write back and invalidate the whole L2
+// at every exchange.)  Returns false when the wait gave up.
+__device__ __forceinline__ bool exchange(const LossArgs& a, double* slot_a, int na,
+                                         double* slot_b, int nb, double v, uint32_t* counter,
+                                         int lane) {
+  double vals[6];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vals[i] = __shfl(v, i, kWave);
+  for (int i = 0; i < 6; ++i) vals[i] = __shfl(v, i, kWave);
   bool ok = true;
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i < n) st_dev(slot + i, vals[i]);
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 6; ++i) {
+      if (i < na) st_dev(slot_a + i, vals[i]);
+      else if (i < na + nb) st_dev(slot_b + (i - na), vals[i]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t polls = 0;
     while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
            (uint32_t)a.C) {
-      if (++polls > a.spin_limit ||
-          __hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+      ++polls;
+      if (polls > a.spin_limit ||
+          (polls % kFaultCheckPolls == 0 &&
+           __hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
         __hip_atomic_store(a.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = false;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(2);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  asm volatile("" ::: "memory");   // the partials' loads stay after the poll
   return __shfl(ok ? 1 : 0, 0, kWave) != 0;
 }
 
@@ -123,31 +139,60 @@ __device__ __forceinline__ double wave_max_d(double v) {
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // Entry e of a lane's slice: chunk-relative offset 4*lane' + 1024*(e/4) + e%4, lane' the
-// lane index over the four compute waves.  Quad e/4 of the four compute waves is one
-// contiguous 4 KiB piece of the chunk, 1 KiB per wave.
+// lane index in the workgroup.  Quad e/4 of the four waves is one contiguous 4 KiB piece of
+// the chunk, 1 KiB per wave.  The LDS stage mirrors the chunk: draft logits at float 0,
+// target logits at float kLossChunk, each entry where its owner lane reads it back.
 __device__ __forceinline__ int slice_off(int ct, int e) { return 4 * ct + 1024 * (e >> 2) + (e & 3); }
 
-// Start the direct global-to-LDS loads of row r's chunk (draft logits at stage, target
-// logits at stage + 16 KiB), each lane's quads landing where that same lane reads them back.
-// A lane past the chunk's end loads its last quad (len is a positive multiple of 4); the
-// entries it does not own are masked where they are used.
-__device__ __forceinline__ void dma_row(const LossArgs& a, int r, int c, int ct, int wave,
-                                        uint32_t stage) {
+// Start staging row r's chunk into LDS.  16-byte rows: direct global-to-LDS loads, which the
+// compiler's wait counting does not see (nothing waits for them until wait_stage).  A lane
+// past the chunk's end loads its last quad (len is a positive multiple of 4) or entry; the
+// entries it does not own are masked where they are used.  Other rows: plain loads written
+// to the stage.
+// A lane's loop-invariant offsets are recomputed from its index at each use (the asm hides
+// the index from the optimiser) rather than held in registers across the row loop.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <bool VEC>
+__device__ __forceinline__ void stage_row(const LossArgs& a, int r, int c, int ct_, int wave,
+                                          uint32_t stage_lds, float* stage) {
+  const int ct = fresh(ct_);
   const int c0 = c * a.L;
   const int len = min(a.L, a.V - c0);
   const size_t base = (size_t)r * a.V + c0;
-  const float* pd = a.zd + base;
-  const float* pt = a.zt + base;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the stage are done
+  const float* pd = a.zd + base;   // uniform chunk bases: the loads take a scalar base
+  const float* pt = a.zt + base;   // and a 32-bit lane offset
+  if constexpr (VEC) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the stage are done
 #pragma unroll
-  for (int q = 0; q < kLossPer / 4; ++q) {
-    const int o = 4 * ct + 1024 * q;
-    const uint32_t voff = 4u * (uint32_t)(o < len ? o : len - 4);
-    // wave-uniform LDS address (M0)
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + 4u * (uint32_t)(1024 * q + 256 * wave));
-    dma16(pd, voff, dst);
-    dma16(pt, voff, dst + 4u * kLossChunk);
+    for (int q = 0; q < kLossPer / 4; ++q) {
+      const int o = 4 * ct + 1024 * q;
+      const uint32_t voff = 4u * (uint32_t)(o < len ? o : len - 4);
+      // wave-uniform LDS address (M0), formed in scalar registers
+      const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)ct >> 6);
+      const uint32_t dst = stage_lds + 4u * (1024u * q + 256u * wv);
+      dma16(pd, voff, dst);
+      dma16(pt, voff, dst + 4u * kLossChunk);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kLossPer; ++e) {
+      const int o = slice_off(ct, e);
+      const uint32_t oc = (uint32_t)(o < len ? o : len - 1);
+      const float vd = pd[oc], vt = pt[oc];
+      stage[o] = vd;
+      stage[kLossChunk + o] = vt;
+    }
   }
+}
+
+// this lane's staged entries are in LDS
+template <bool VEC>
+__device__ __forceinline__ void wait_stage() {
+  if constexpr (VEC) wait_vm<0>();
 }
 
 // the lane's entries of the staged chunk into registers
@@ -161,25 +206,10 @@ __device__ __forceinline__ void read_stage(const float* stage, int ct, float* d,
   }
 }
 
-// the lane's entries of row r straight from global memory (rows whose logits are not
-// 16-byte aligned)
-__device__ __forceinline__ void load_direct(const LossArgs& a, int r, int c, int ct, float* d,
-                                            float* t) {
-  const int c0 = c * a.L;
-  const int len = min(a.L, a.V - c0);
-  const size_t base = (size_t)r * a.V + c0;
-#pragma unroll
-  for (int e = 0; e < kLossPer; ++e) {
-    const int o = slice_off(ct, e);
-    const uint32_t oc = (uint32_t)(o < len ? o : len - 1);
-    d[e] = a.zd[base + oc];
-    t[e] = a.zt[base + oc];
-  }
-}
-
 template <bool VEC>
-__device__ __forceinline__ void store_grad(const LossArgs& a, int r, int c, int ct,
+__device__ __forceinline__ void store_grad(const LossArgs& a, int r, int c, int ct_,
                                            const float* g) {
+  const int ct = fresh(ct_);
   const int c0 = c * a.L;
   const int len = min(a.L, a.V - c0);
   float* out = a.grad + (size_t)r * a.V + c0;
@@ -203,216 +233,312 @@ __device__ __forceinline__ void store_grad(const LossArgs& a, int r, int c, int 
 // Entry e of the lane's slice lies inside the chunk (bit e of the lane's mask).
 __device__ __forceinline__ bool live(uint32_t mask, int e) { return (mask >> e) & 1u; }
 
-// (max, sum of exp(x - max)) of one lane's live entries; none live, or all -inf, gives
-// (-inf, 0)
-__device__ __forceinline__ ML lane_ml(const float* x, uint32_t mask) {
-  float m = -INFINITY;
+// Per-lane (max, sum of exp(x - max)) of both logit sets of the staged chunk, reading LDS
+// twice rather than holding a second row in registers; none live or all -inf: (-inf, 0).
+__device__ __forceinline__ void stage_ml(const float* stage, int ct, uint32_t mask, ML& md,
+                                         ML& mt) {
+  float xd = -INFINITY, xt = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < kLossPer; ++e) m = fmaxf(m, live(mask, e) ? x[e] : -INFINITY);
-  if (m == -INFINITY) return ML{-INFINITY, 0.f};
-  float s = 0.f;
+  for (int q = 0; q < kLossPer / 4; ++q) {
+    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + 1024 * q);
+    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + 1024 * q);
 #pragma unroll
-  for (int e = 0; e < kLossPer; ++e) s += live(mask, e) ? fast_exp(x[e] - m) : 0.f;
-  return ML{m, s};
+    for (int i = 0; i < 4; ++i) {
+      const bool on = live(mask, 4 * q + i);
+      xd = fmaxf(xd, on ? vd[i] : -INFINITY);
+      xt = fmaxf(xt, on ? vt[i] : -INFINITY);
+    }
+  }
+  const float bd = xd == -INFINITY ? 0.f : xd, bt = xt == -INFINITY ? 0.f : xt;
+  float sd = 0.f, st = 0.f;
+#pragma unroll
+  for (int q = 0; q < kLossPer / 4; ++q) {
+    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + 1024 * q);
+    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + 1024 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool on = live(mask, 4 * q + i);
+      sd += on ? fast_exp(vd[i] - bd) : 0.f;
+      st += on ? fast_exp(vt[i] - bt) : 0.f;
+    }
+  }
+  md = ML{xd, sd};
+  mt = ML{xt, st};
 }
 
 struct LossShared {
-  float w1[kLossComputeWaves][4];   // per compute wave: (m_d, s_d, m_t, s_t)
-  float w2[kLossComputeWaves][2];   // per compute wave: (l1, S)
-  float r1[4];                      // row: (max_d, log sum_d, max_t, log sum_t)
-  float r2[3];                      // row: (S, w alpha_ce, w alpha_l1)
-  int y;                            // row: the label, clamped into the vocabulary
-  double lse_d;                     // row: log-sum-exp of the draft logits (fp64)
+  float w1[kLossWaves][4];   // per wave: (m_d, s_d, m_t, s_t) of the staged row
+  float w2[kLossWaves][2];   // per wave: (l1, S) of the current row
+  float r1[4];               // staged row: (max_d, log sum_d, max_t, log sum_t)
+  float r2[3];               // current row: (S, w alpha_ce, w alpha_l1)
+  int y;                     // current row: the label, clamped into the vocabulary
   int stop;
 };
 
-// One row of the stream; the compute waves hold its slice in d, t.  Returns false when the
-// stream must stop.
-template <bool VEC>
-__device__ __forceinline__ bool loss_row(const LossArgs& a, LossShared& sh, int r, int c,
-                                         uint32_t mask, const float* d, const float* t) {
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const bool control = wave == kLossComputeWaves;
-  const int ct = tid;   // lane index over the compute waves (control: unused)
-
-  // ---- sweep 1: per-chunk softmax normalisers
-  if (!control) {
-    const ML md = wave_ml(lane_ml(d, mask));
-    const ML mt = wave_ml(lane_ml(t, mask));
-    if (lane == 0) {
-      sh.w1[wave][0] = md.m; sh.w1[wave][1] = md.l;
-      sh.w1[wave][2] = mt.m; sh.w1[wave][3] = mt.l;
+// wave 0: the four waves' (max, sum) pairs of one logit set combined in fp64 (lanes 0..3
+// of the caller give (m_d, s_d, m_t, s_t); others 0)
+__device__ __forceinline__ double combine_waves1(const LossShared& sh, int lane) {
+  double v = 0.0;
+  if (lane < 4) {
+    const int off = lane & 2;   // 0: draft, 2: target
+    double m = -INFINITY;
+    for (int w = 0; w < kLossWaves; ++w) m = fmax(m, (double)sh.w1[w][off]);
+    if (lane & 1) {
+      if (m != -INFINITY)
+        for (int w = 0; w < kLossWaves; ++w)
+          v += (double)sh.w1[w][off + 1] * (double)fast_exp(sh.w1[w][off] - (float)m);
+    } else {
+      v = m;
     }
   }
-  raw_barrier();
-  if (control) {
-    // combine the four waves (fp64), publish, wait, combine the C chunks (fp64)
-    double v = 0.0;
-    if (lane < 4) {
-      const int off = (lane & 2);   // 0: draft, 2: target
-      double m = -INFINITY;
-      for (int w = 0; w < kLossComputeWaves; ++w) m = fmax(m, (double)sh.w1[w][off]);
-      if (lane & 1) {
-        double s = 0.0;
-        if (m != -INFINITY)
-          for (int w = 0; w < kLossComputeWaves; ++w)
-            s += (double)sh.w1[w][off + 1] * (double)fast_exp(sh.w1[w][off] - (float)m);
-        v = s;
-      } else {
-        v = m;
-      }
-    }
-    double* slot = a.part1 + ((size_t)r * a.C + c) * 4;
-    const bool ok = exchange(a, slot, 4, v, a.cnt + 2 * (size_t)r, lane);
-    if (ok) {
-      double m_d = -INFINITY, m_t = -INFINITY;
-      for (int cc = lane; cc < a.C; cc += kWave) {
-        const double* p = a.part1 + ((size_t)r * a.C + cc) * 4;
-        m_d = fmax(m_d, ld_dev(p));
-        m_t = fmax(m_t, ld_dev(p + 2));
-      }
-      m_d = wave_max_d(m_d);
-      m_t = wave_max_d(m_t);
-      double s_d = 0.0, s_t = 0.0;
-      for (int cc = lane; cc < a.C; cc += kWave) {
-        const double* p = a.part1 + ((size_t)r * a.C + cc) * 4;
-        const double pm_d = ld_dev(p), ps_d = ld_dev(p + 1);
-        const double pm_t = ld_dev(p + 2), ps_t = ld_dev(p + 3);
-        if (ps_d > 0.0) s_d += ps_d * (double)fast_exp((float)(pm_d - m_d));
-        if (ps_t > 0.0) s_t += ps_t * (double)fast_exp((float)(pm_t - m_t));
-      }
-      s_d = wave_sum_d(s_d);
-      s_t = wave_sum_d(s_t);
-      if (lane == 0) {
-        const float ls_d = fast_log((float)s_d), ls_t = fast_log((float)s_t);
-        sh.r1[0] = (float)m_d; sh.r1[1] = ls_d;
-        sh.r1[2] = (float)m_t; sh.r1[3] = ls_t;
-        sh.lse_d = m_d + (double)ls_d;
-        sh.stop = 0;
-      }
-    } else if (lane == 0) {
-      sh.stop = 1;
-    }
-  }
-  raw_barrier();
-  if (sh.stop) return false;
-
-  // ---- sweep 2: l1 and S partials
-  const float Md = sh.r1[0], Ld = sh.r1[1], Mt = sh.r1[2], Lt = sh.r1[3];
-  if (!control) {
-    float l1 = 0.f, S = 0.f;
-#pragma unroll
-    for (int e = 0; e < kLossPer; ++e) {
-      const float pd = fast_exp((d[e] - Md) - Ld);
-      const float pt = fast_exp((t[e] - Mt) - Lt);
-      const float df = live(mask, e) ? pd - pt : 0.f;
-      l1 += fabsf(df);
-      S += df > 0.f ? pd : (df < 0.f ? -pd : 0.f);
-    }
-    l1 = wave_sum(l1);
-    S = wave_sum(S);
-    if (lane == 0) { sh.w2[wave][0] = l1; sh.w2[wave][1] = S; }
-  }
-  raw_barrier();
-  if (control) {
-    double v = 0.0;
-    if (lane < 2)
-      for (int w = 0; w < kLossComputeWaves; ++w) v += (double)sh.w2[w][lane];
-    double* slot = a.part2 + ((size_t)r * a.C + c) * 2;
-    const bool ok = exchange(a, slot, 2, v, a.cnt + 2 * (size_t)r + 1, lane);
-    if (ok) {
-      double l1 = 0.0, S = 0.0;
-      for (int cc = lane; cc < a.C; cc += kWave) {
-        const double* p = a.part2 + ((size_t)r * a.C + cc) * 2;
-        l1 += ld_dev(p);
-        S += ld_dev(p + 1);
-      }
-      l1 = wave_sum_d(l1);
-      S = wave_sum_d(S);
-      const int k = r % a.G;
-      const double wk = (double)fast_exp(-(float)k / (float)a.G) * a.inv_W;
-      if (lane == 0) {
-        sh.r2[0] = (float)S;
-        sh.r2[1] = (float)(wk * a.a_ce);
-        sh.r2[2] = (float)(wk * a.a_l1);
-        sh.y = clamp_tok(a.labels[r], a.V);
-        sh.stop = 0;
-      }
-      if (c == 0 && lane == 0) {
-        // the row's scalar terms (chunk 0's control wave)
-        const int y = clamp_tok(a.labels[r], a.V);
-        const double ce = sh.lse_d - (double)a.zd[(size_t)r * a.V + y];
-        const double at = 1.0 - 0.5 * l1;
-        // log(1 + e^l) and sigmoid(l) in fp32 through e = exp(-|l|) in (0, 1]
-        const float lf = a.conf[r];
-        const float e = fast_exp(-fabsf(lf));
-        const double l = (double)lf;
-        const double softplus = (double)fmaxf(lf, 0.f) + (double)log1pf(e);
-        const double bce = softplus - at * l;
-        const double cs = lf >= 0.f ? 1.0 / (1.0 + (double)e) : (double)e / (1.0 + (double)e);
-        a.rowloss[r] = wk * (a.a_ce * ce + a.a_l1 * l1 + a.a_conf * bce);
-        if (a.terms) {
-          a.terms[3 * (size_t)r] = (float)ce;
-          a.terms[3 * (size_t)r + 1] = (float)l1;
-          a.terms[3 * (size_t)r + 2] = (float)bce;
-        }
-        if (a.grad_conf) a.grad_conf[r] = (float)(wk * a.a_conf * (cs - at));
-      }
-    } else if (lane == 0) {
-      sh.stop = 1;
-    }
-  }
-  raw_barrier();
-  if (sh.stop) return false;
-
-  // ---- sweep 3: the gradient of the draft logits
-  if (!control && a.grad) {
-    const float S = sh.r2[0], fa = sh.r2[1], fb = sh.r2[2];
-    const int y = sh.y - c * a.L;   // chunk-relative label
-    float g[kLossPer];
-#pragma unroll
-    for (int e = 0; e < kLossPer; ++e) {
-      const float pd = fast_exp((d[e] - Md) - Ld);
-      const float pt = fast_exp((t[e] - Mt) - Lt);
-      const float df = pd - pt;
-      const float s = df > 0.f ? 1.f : (df < 0.f ? -1.f : 0.f);
-      const float oh = slice_off(ct, e) == y ? 1.f : 0.f;
-      g[e] = fa * (pd - oh) + fb * pd * (s - S);
-    }
-    store_grad<VEC>(a, r, c, ct, g);
-  }
-  return true;
+  return v;
 }
 
+// Values the kernel only reads, loaded through the scalar unit (uniform addresses): they
+// land in scalar registers and their waits never involve the vector-memory counter.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
+__device__ __forceinline__ float ld_uniform(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)(uintptr_t)p;
+}
+
+// Row scalars that do not depend on the exchange, fetched before it.
+struct RowScalars {
+  int y;        // label, clamped into the vocabulary
+  float zy;     // draft logit at the label
+  float lf;     // confidence logit
+};
+
+__device__ __forceinline__ RowScalars row_scalars(const LossArgs& a, int r) {
+  RowScalars rs;
+  rs.y = clamp_tok(ld_uniform(a.labels + r), a.V);
+  rs.zy = ld_uniform(a.zd + (size_t)r * a.V + rs.y);
+  rs.lf = ld_uniform(a.conf + r);
+  return rs;
+}
+
+// wave 0, after the prologue's exchange: row r's normalisers from its C chunk partials
+// -> sh.r1 (lane 0 writes); returns lse of the draft logits in fp64
+__device__ __forceinline__ double combine_part1(const LossArgs& a, LossShared& sh, int r,
+                                                int lane) {
+  // per lane: online (max, sum) over its chunks; all loads of a pass issued together
+  double m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
+  for (int cc = lane; cc < a.C; cc += kWave) {
+    const double* p = a.part1 + ((size_t)r * a.C + cc) * 4;
+    const double pm_d = ld_dev(p), ps_d = ld_dev(p + 1), pm_t = ld_dev(p + 2), ps_t = ld_dev(p + 3);
+    if (ps_d > 0.0) {
+      const double m = fmax(m_d, pm_d);
+      s_d = s_d * (double)fast_exp((float)(m_d - m)) + ps_d * (double)fast_exp((float)(pm_d - m));
+      m_d = m;
+    }
+    if (ps_t > 0.0) {
+      const double m = fmax(m_t, pm_t);
+      s_t = s_t * (double)fast_exp((float)(m_t - m)) + ps_t * (double)fast_exp((float)(pm_t - m));
+      m_t = m;
+    }
+  }
+  const double M_d = wave_max_d(m_d), M_t = wave_max_d(m_t);
+  s_d = s_d > 0.0 ? s_d * (double)fast_exp((float)(m_d - M_d)) : 0.0;
+  s_t = s_t > 0.0 ? s_t * (double)fast_exp((float)(m_t - M_t)) : 0.0;
+  s_d = wave_sum_d(s_d);
+  s_t = wave_sum_d(s_t);
+  const float ls_d = fast_log((float)s_d), ls_t = fast_log((float)s_t);
+  if (lane == 0) {
+    sh.r1[0] = (float)M_d; sh.r1[1] = ls_d;
+    sh.r1[2] = (float)M_t; sh.r1[3] = ls_t;
+  }
+  return M_d + (double)ls_d;
+}
+
+// wave 0, after a loop exchange: row r's l1 and S and (has_next) row rn's normalisers from
+// the C chunk partials, all loaded in one round trip; the row's scalar outputs (chunk 0's
+// workgroup) and the gradient coefficients -> sh.r2, sh.y; rn's normalisers -> sh.r1.
+// lse_d: in, row r's; out, row rn's.
+__device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, int r, int rn,
+                                             bool has_next, int c, double& lse_d,
+                                             const RowScalars& rs, int lane) {
+  double l1 = 0.0, S = 0.0, m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
+  for (int cc = lane; cc < a.C; cc += kWave) {
+    const double* p2 = a.part2 + ((size_t)r * a.C + cc) * 2;
+    const double* p1 = a.part1 + ((size_t)(has_next ? rn : r) * a.C + cc) * 4;
+    const double q0 = ld_dev(p2), q1 = ld_dev(p2 + 1);
+    double pm_d = -INFINITY, ps_d = 0.0, pm_t = -INFINITY, ps_t = 0.0;
+    if (has_next) {
+      pm_d = ld_dev(p1); ps_d = ld_dev(p1 + 1); pm_t = ld_dev(p1 + 2); ps_t = ld_dev(p1 + 3);
+    }
+    l1 += q0;
+    S += q1;
+    if (ps_d > 0.0) {
+      const double m = fmax(m_d, pm_d);
+      s_d = s_d * (double)fast_exp((float)(m_d - m)) + ps_d * (double)fast_exp((float)(pm_d - m));
+      m_d = m;
+    }
+    if (ps_t > 0.0) {
+      const double m = fmax(m_t, pm_t);
+      s_t = s_t * (double)fast_exp((float)(m_t - m)) + ps_t * (double)fast_exp((float)(pm_t - m));
+      m_t = m;
+    }
+  }
+  l1 = wave_sum_d(l1);
+  S = wave_sum_d(S);
+  if (lane == 0) {
+    const int k = r % a.G;
+    const double wk = (double)fast_exp(-(float)k / (float)a.G) * a.inv_W;
+    sh.r2[0] = (float)S;
+    sh.r2[1] = (float)(wk * a.a_ce);
+    sh.r2[2] = (float)(wk * a.a_l1);
+    sh.y = rs.y;
+    if (c == 0) {
+      const double ce = lse_d - (double)rs.zy;
+      const double at = 1.0 - 0.5 * l1;
+      // log(1 + e^l) and sigmoid(l) in fp32 through e = exp(-|l|) in (0, 1]
+      const float lf = rs.lf;
+      const float e = fast_exp(-fabsf(lf));
+      const double l = (double)lf;
+      const double softplus = (double)fmaxf(lf, 0.f) + (double)log1pf(e);
+      const double bce = softplus - at * l;
+      const double cs = lf >= 0.f ? 1.0 / (1.0 + (double)e) : (double)e / (1.0 + (double)e);
+      a.rowloss[r] = wk * (a.a_ce * ce + a.a_l1 * l1 + a.a_conf * bce);
+      if (a.terms) {
+        a.terms[3 * (size_t)r] = (float)ce;
+        a.terms[3 * (size_t)r + 1] = (float)l1;
+        a.terms[3 * (size_t)r + 2] = (float)bce;
+      }
+      if (a.grad_conf) a.grad_conf[r] = (float)(wk * a.a_conf * (cs - at));
+    }
+  }
+  if (has_next) {
+    const double M_d = wave_max_d(m_d), M_t = wave_max_d(m_t);
+    s_d = s_d > 0.0 ? s_d * (double)fast_exp((float)(m_d - M_d)) : 0.0;
+    s_t = s_t > 0.0 ? s_t * (double)fast_exp((float)(m_t - M_t)) : 0.0;
+    s_d = wave_sum_d(s_d);
+    s_t = wave_sum_d(s_t);
+    const float ls_d = fast_log((float)s_d), ls_t = fast_log((float)s_t);
+    if (lane == 0) {
+      sh.r1[0] = (float)M_d; sh.r1[1] = ls_d;
+      sh.r1[2] = (float)M_t; sh.r1[3] = ls_t;
+    }
+    lse_d = M_d + (double)ls_d;
+  }
+}
+
+// A stream of C workgroups (chunk c of rows p, p + P, ...).  Per row r, with the next row
+// rn = r + P already staged in LDS:
+//   1. every wave: l1 and S partials of r (its registers); (max, sum) partials of rn (the
+//      stage);
+//   2. wave 0: one exchange carries both -- the stream meets once per row;
+//   3. every wave: the gradient of r; rn moves from the stage to the registers and the row
+//      after it starts streaming into the stage.
 template <bool VEC>
-__global__ __launch_bounds__(kLossThreads) void k_draft_loss(LossArgs a) {
+__global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
   __shared__ LossShared sh;
-  __shared__ __align__(16) float stage[VEC ? 2 * kLossChunk : 1];   // the next row's chunk
+  __shared__ __align__(16) float stage[2 * kLossChunk];
   const int p = blockIdx.x / a.C, c = blockIdx.x % a.C;
   if (p >= a.P) return;
-  const int tid = threadIdx.x, wave = tid / kWave;
-  const bool compute = wave < kLossComputeWaves;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const bool lead = wave == 0;
   const uint32_t stage_lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage;
   // which of the lane's entries lie inside its chunk (the same for every row)
   const int len = min(a.L, a.V - c * a.L);
   uint32_t mask = 0;
 #pragma unroll
   for (int e = 0; e < kLossPer; ++e) mask |= (slice_off(tid, e) < len ? 1u : 0u) << e;
+  uint32_t* const cnt_end = a.cnt + (size_t)(a.R + p) * kCntStride;
   float d[kLossPer], t[kLossPer];
-  if constexpr (VEC) {
-    if (compute) dma_row(a, p, c, tid, wave, stage_lds);
+  double lse_cur = 0.0;   // wave 0: lse of the current row's draft logits
+
+  // prologue: row p's normalisers
+  stage_row<VEC>(a, p, c, tid, wave, stage_lds, stage);
+  wait_stage<VEC>();
+  {
+    ML md, mt;
+    stage_ml(stage, tid, mask, md, mt);
+    md = wave_ml(md);
+    mt = wave_ml(mt);
+    if (lane == 0) {
+      sh.w1[wave][0] = md.m; sh.w1[wave][1] = md.l;
+      sh.w1[wave][2] = mt.m; sh.w1[wave][3] = mt.l;
+    }
   }
-  for (int r = p; r < a.R; r += a.P) {
-    if (compute) {
-      if constexpr (VEC) {
-        wait_vm<0>();                    // this lane's share of row r has landed
-        read_stage(stage, tid, d, t);
-        if (r + a.P < a.R) dma_row(a, r + a.P, c, tid, wave, stage_lds);
-      } else {
-        load_direct(a, r, c, tid, d, t);
+  read_stage(stage, tid, d, t);
+  if (p + a.P < a.R) stage_row<VEC>(a, p + a.P, c, tid, wave, stage_lds, stage);
+  raw_barrier();
+  if (lead) {
+    const double v = combine_waves1(sh, lane);
+    const bool ok = exchange(a, a.part1 + ((size_t)p * a.C + c) * 4, 4, nullptr, 0, v,
+                             a.cnt + (size_t)p * kCntStride, lane);
+    if (ok) lse_cur = combine_part1(a, sh, p, lane);
+    if (lane == 0) sh.stop = ok ? 0 : 1;
+  }
+  raw_barrier();
+
+  for (int r = p; r < a.R && !sh.stop; r += a.P) {
+    const int rn = r + a.P;
+    const bool has_next = rn < a.R;
+    // 1. partials
+    const float Md = sh.r1[0], Ld = sh.r1[1], Mt = sh.r1[2], Lt = sh.r1[3];
+    {
+      float l1 = 0.f, S = 0.f;
+#pragma unroll
+      for (int e = 0; e < kLossPer; ++e) {
+        const float pd = fast_exp((d[e] - Md) - Ld);
+        const float pt = fast_exp((t[e] - Mt) - Lt);
+        const float df = live(mask, e) ? pd - pt : 0.f;
+        l1 += fabsf(df);
+        S += df > 0.f ? pd : (df < 0.f ? -pd : 0.f);
+      }
+      l1 = wave_sum(l1);
+      S = wave_sum(S);
+      if (lane == 0) { sh.w2[wave][0] = l1; sh.w2[wave][1] = S; }
+    }
+    const RowScalars rs = row_scalars(a, r);   // scalar loads, in flight during the sweeps
+    if (has_next) {
+      wait_stage<VEC>();
+      ML md, mt;
+      stage_ml(stage, tid, mask, md, mt);
+      md = wave_ml(md);
+      mt = wave_ml(mt);
+      if (lane == 0) {
+        sh.w1[wave][0] = md.m; sh.w1[wave][1] = md.l;
+        sh.w1[wave][2] = mt.m; sh.w1[wave][3] = mt.l;
       }
     }
-    if (!loss_row<VEC>(a, sh, r, c, mask, d, t)) break;
+    raw_barrier();
+    // 2. the stream's exchange
+    if (lead) {
+      double v = has_next ? combine_waves1(sh, lane - 2 < 0 ? 63 : lane - 2) : 0.0;
+      if (lane < 2)
+        for (int w = 0; w < kLossWaves; ++w) v += (double)sh.w2[w][lane];
+      const bool ok =
+          exchange(a, a.part2 + ((size_t)r * a.C + c) * 2, 2,
+                   a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v,
+                   has_next ? a.cnt + (size_t)rn * kCntStride : cnt_end, lane);
+      if (ok) combine_step(a, sh, r, rn, has_next, c, lse_cur, rs, lane);
+      if (lane == 0) sh.stop = ok ? 0 : 1;
+    }
+    raw_barrier();
+    if (sh.stop) break;
+    // 3. the gradient of row r; the next row into registers, the one after it into LDS
+    if (a.grad) {
+      const float S = sh.r2[0], fa = sh.r2[1], fb = sh.r2[2];
+      const int y = sh.y - c * a.L;   // chunk-relative label
+      float g[kLossPer];
+#pragma unroll
+      for (int e = 0; e < kLossPer; ++e) {
+        const float pd = fast_exp((d[e] - Md) - Ld);
+        const float pt = fast_exp((t[e] - Mt) - Lt);
+        const float df = pd - pt;
+        const float sg = df > 0.f ? 1.f : (df < 0.f ? -1.f : 0.f);
+        const float oh = slice_off(tid, e) == y ? 1.f : 0.f;
+        g[e] = fa * (pd - oh) + fb * pd * (sg - S);
+      }
+      store_grad<VEC>(a, r, c, tid, g);
+    }
+    if (has_next) {
+      read_stage(stage, tid, d, t);
+      if (rn + a.P < a.R) stage_row<VEC>(a, rn + a.P, c, tid, wave, stage_lds, stage);
+    }
   }
   if constexpr (VEC) wait_vm<0>();   // nothing in flight into LDS when the workgroup ends
 }
@@ -464,7 +590,7 @@ LossWs loss_ws(int R, int V, void* base) {
   w.part1 = c.take<double>((size_t)R * C * 4);
   w.part2 = c.take<double>((size_t)R * C * 2);
   w.rowloss = c.take<double>((size_t)R);
-  w.cnt = c.take<uint32_t>((size_t)R * 2);
+  w.cnt = c.take<uint32_t>(((size_t)R + 1024) * kCntStride);
   w.fault = c.take<uint32_t>(1);
   w.bytes = align_up(c.off, 256);
   return w;
@@ -525,14 +651,14 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
   a.C = loss_chunks(V);
   a.L = (V + 4 * a.C - 1) / (4 * a.C) * 4;
   if (cap < a.C) return DSPARK_E_HIP;   // no cooperative launch, or a row does not fit
-  a.P = std::min(R, cap / a.C);
+  a.P = std::min(std::min(R, cap / a.C), 1024);   // the end-of-stream counters hold 1024
   double wsum = 0.0;
   for (int k = 0; k < G; ++k) wsum += std::exp(-(double)k / G);
   a.inv_W = 1.0 / ((double)B * wsum);
   a.a_ce = alpha_ce; a.a_l1 = alpha_l1; a.a_conf = alpha_conf;
   a.spin_limit = 1u << 22;
   hipStream_t st = (hipStream_t)stream;
-  const size_t ncnt = (size_t)R * 2;
+  const size_t ncnt = ((size_t)R + 1024) * kCntStride;
   hipLaunchKernelGGL(k_loss_init, dim3((unsigned)std::min<size_t>(256, (ncnt + 255) / 256)),
                      dim3(256), 0, st, w.cnt, ncnt, w.fault);
   if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
