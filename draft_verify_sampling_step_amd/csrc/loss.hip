@@ -17,20 +17,20 @@
 // The softmax normalisers, l1 and S are sums over the whole row, and the gradient needs all
 // of them, so a row is three dependent sweeps.  Rows of 150k fp32 logits do not fit one
 // compute unit, and re-reading them twice from HBM would more than double the traffic.
-// Instead one cooperative launch keeps every logit in registers from its single read to the
+// Instead one cooperative launch keeps every logit on chip from its single read to the
 // gradient write:
 //   * a row's vocabulary is cut into C chunks of at most 4096 entries; a "stream" of C
 //     workgroups (chunk c of rows p, p + P, p + 2P, ...) works through its rows together,
 //     P streams at once, every workgroup resident (cooperative launch);
-//   * each workgroup has four compute waves (16 entries of each row per lane, in registers)
-//     and one control wave; while a row is processed the next row's chunk streams into LDS
-//     by direct global-to-LDS loads, which the compiler's wait counting does not see, so
-//     nothing in the row's three sweeps waits for them;
-//   * the control wave alone talks to the other workgroups of its stream: it publishes the
-//     workgroup's partials with device-scope stores, counts arrivals on a per-row counter,
-//     polls it, and combines the C partials in fp64.  Keeping all polling and atomics on
-//     that wave means the compute waves never wait on a counter load, so their prefetch
-//     stays in flight; they meet the control wave at plain (fence-free) barriers.
+//   * a workgroup is four waves (one per SIMD, so four workgroups pack evenly on a compute
+//     unit), 16 entries of the current row per lane in registers; the next row's chunk
+//     streams into LDS by direct global-to-LDS loads, which the compiler's wait counting
+//     does not see, so nothing waits for them before they are needed;
+//   * the stream meets once per row: one exchange carries the current row's L1 and S
+//     partials together with the next row's (max, sum) partials, which the waves compute
+//     from the LDS copy; wave 0 publishes them with device-scope atomic stores, counts
+//     arrivals on a per-exchange counter, polls it, and combines the C partials in fp64 in
+//     one round trip of loads.  No cache-wide fence is involved;
 //   * every wait is bounded: a poll that runs past its limit raises a fault word, the
 //     stream stops, and the loss is written as NaN.
 // HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 32 bytes of
