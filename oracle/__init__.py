@@ -64,6 +64,8 @@ def _load():
                                            ctypes.c_int32, _P, _P, _P]
         lib.ora_sts_calibrate.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                           ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+        lib.ora_markov_target.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          _P, _P, _P, ctypes.c_double, ctypes.c_uint64, _P]
         lib.ora_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                        _P, _P, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_double, _P, _P, _P, _P]
@@ -234,6 +236,21 @@ def sts_calibrate(logit, n_accept, temps, n_bins=15):
     lib.ora_sts_calibrate(n, G, _ptr(logit), _ptr(n_accept), _ptr(temps), temps.shape[0],
                           int(n_bins), _ptr(t), _ptr(ece), _ptr(gap))
     return t, ece, gap
+
+
+def markov_target(U, anchor, tokens, sigma, seed):
+    """Stand-in target of a closed loop (not a step of the method): T [B][gamma+1][V] with
+    T[b][j] = U[b][min(j, gamma-1)] + sigma sqrt(3) (2 u(seed, prev, 0, 3, v) - 1), prev the
+    token before position j+1 (anchor[b] for j = 0, else tokens[b][j-1])."""
+    lib = _load()
+    U = _f64(U)
+    B, G, V = U.shape
+    anchor = _i32(anchor)
+    tokens = _i32(tokens)
+    T = np.empty((B, G + 1, V))
+    lib.ora_markov_target(B, G, V, _ptr(U), _ptr(anchor), _ptr(tokens), float(sigma),
+                          ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(T))
+    return T
 
 
 def draft_loss(zd, zt, labels, conf_logit, alphas=(0.1, 0.9, 1.0), grads=True):

@@ -34,6 +34,10 @@
  *                                        own admitted count, Monte-Carlo losslessness)
  *   ora_sts_calibrate .................. pinned (recovery of known per-position
  *                                        temperatures, hand-computed ECE, one-value grids)
+ *   ora_markov_target .................. pinned (depends on the previous token only,
+ *                                        moments of the uniform transition term); the
+ *                                        closed loop's stand-in target, not a step of
+ *                                        the method
  *   ora_draft_loss ..................... pinned (central finite differences of the loss,
  *                                        p_d = p_t and one-hot special cases)
  *   ora_verify ......................... pinned (Monte-Carlo losslessness against the
@@ -375,6 +379,36 @@ void ora_sts_calibrate(int32_t n, int32_t gamma, const double* logit, const int3
     free(sp);
     free(sy);
     free(cnt);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Stand-in target for a closed loop of rounds (not a step of the method).  A synthetic   */
+/* Markov target: the logits of position k = j + 1 (j = 0..gamma) of request b are the   */
+/* draft's base logits plus a transition term that depends only on the previous token:   */
+/*   T[b][j][v] = U[b][min(j, gamma-1)][v] + sigma sqrt(3) (2 u - 1),                     */
+/*   u = u(seed, prev, 0, 3, v),  prev = anchor[b] (j = 0) or tokens[b][j-1],             */
+/* with the random-number definition above (stream s = 3 reserved for it): a zero-mean    */
+/* uniform term of variance sigma^2 per (previous token, next token) pair.               */
+/* ------------------------------------------------------------------------------------ */
+void ora_markov_target(int32_t B, int32_t gamma, int32_t V, const double* U,
+                       const int32_t* anchor, const int32_t* tokens, double sigma,
+                       uint64_t seed, double* T)
+{
+    const double scale = sigma * sqrt(3.0);
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j <= gamma; ++j) {
+            int prev = j == 0 ? anchor[b] : tokens[(size_t)b * gamma + (j - 1)];
+            if (prev < 0) prev = 0;
+            if (prev >= V) prev = V - 1;
+            const int row = j < gamma ? j : gamma - 1;
+            const double* base = U + ((size_t)b * gamma + row) * V;
+            double* out = T + ((size_t)b * (gamma + 1) + j) * V;
+            for (int v = 0; v < V; ++v) {
+                const double u = ora_uniform(seed, (uint32_t)prev, 0u, 3u, (uint32_t)v);
+                out[v] = base[v] + scale * (2.0 * u - 1.0);
+            }
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------------------ */

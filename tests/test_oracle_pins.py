@@ -704,3 +704,41 @@ def test_draft_loss_disjoint_distributions():
     assert r["terms"][0, 0, 1] == pytest.approx(2.0, abs=1e-15)
     assert r["terms"][0, 0, 2] == pytest.approx(-special.log_expit(-0.8), rel=1e-12)
     assert r["terms"][0, 0, 0] == pytest.approx(60.0, rel=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# stand-in target of the closed loop
+# ------------------------------------------------------------------------------------
+def test_markov_target_rows_and_previous_token():
+    """sigma = 0: the target rows are the base rows, the last one repeated for position
+    gamma + 1.  sigma > 0: the transition term depends on the previous token alone."""
+    B, G, V = 2, 3, 64
+    U = np.arange(B * G, dtype=np.float64).reshape(B, G, 1) * np.ones((1, 1, V))
+    anchor = np.array([5, 9])
+    tokens = np.array([[9, 5, 5], [7, 9, 5]])
+    T0 = oracle.markov_target(U, anchor, tokens, 0.0, 1)
+    np.testing.assert_array_equal(T0[:, :G], U)
+    np.testing.assert_array_equal(T0[:, G], U[:, G - 1])
+    T = oracle.markov_target(U, anchor, tokens, 0.8, 1)
+    term = T - np.concatenate([U, U[:, G - 1:]], axis=1)
+    prev = np.concatenate([anchor[:, None], tokens], axis=1)   # prev of positions 1..G+1
+    for tok in (5, 9):
+        rows = [term[b, j] for b in range(B) for j in range(G + 1) if prev[b, j] == tok]
+        assert len(rows) >= 3
+        for r_ in rows[1:]:
+            np.testing.assert_allclose(r_, rows[0], rtol=0, atol=1e-14)   # base + term - base
+    assert not np.array_equal(term[0, 0], term[0, 1])          # prev 5 vs prev 9
+    assert np.abs(term).max() <= 0.8 * np.sqrt(3.0)
+
+
+def test_markov_target_term_moments():
+    """The transition term is uniform on [-sigma sqrt 3, sigma sqrt 3]: mean 0, variance
+    sigma^2 (65536 draws: 6-sigma bounds)."""
+    V = 65536
+    U = np.zeros((1, 1, V))
+    T = oracle.markov_target(U, np.array([17]), np.zeros((1, 1), np.int64), 1.3, 99)
+    x = T[0, 0]
+    assert abs(x.mean()) < 6 * 1.3 / np.sqrt(V)
+    assert abs(x.var() / 1.3 ** 2 - 1.0) < 6 * np.sqrt(0.8 / V)
+    h, _ = np.histogram(x, bins=16, range=(-1.3 * np.sqrt(3), 1.3 * np.sqrt(3)))
+    assert stats.chisquare(h).pvalue > 1e-4
