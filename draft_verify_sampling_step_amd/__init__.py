@@ -91,6 +91,11 @@ def lib() -> ctypes.CDLL:
             L.dspark_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             _P, _P, _P, _P, ctypes.c_double, ctypes.c_double,
                                             ctypes.c_double, _P, _P, _P, _P, _P, _SZ, _P]
+            L.dspark_loop_workspace_bytes.argtypes = [D]
+            L.dspark_loop_workspace_bytes.restype = _SZ
+            L.dspark_closed_loop.argtypes = [D, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _F,
+                                             _U64, _F, _U64, ctypes.c_int32, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, _SZ, _P]
             L.dspark_profile_start.argtypes = [_I]
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(_I),
@@ -98,7 +103,7 @@ def lib() -> ctypes.CDLL:
             for fn in ("dspark_draft_markov", "dspark_confidence",
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
-                       "dspark_draft_loss", "dspark_rng_uniforms",
+                       "dspark_draft_loss", "dspark_closed_loop", "dspark_rng_uniforms",
                        "dspark_profile_start", "dspark_profile_stop"):
                 getattr(L, fn).restype = _I
             _lib = L
@@ -254,6 +259,48 @@ def dspark_sts_calibrate(logit, n_accept, temps, n_bins: int = 15, out=None, ws=
                                       int(n_bins), _ptr(t_out), _ptr(ece_out), _ptr(w),
                                       w.numel(), _stream_handle(stream)))
     return t_out, ece_out
+
+
+def dspark_closed_loop(U, W1, W2t, h, w, anchor, sps, rounds: int, temperature: float,
+                       seed: int, sched_mode: int = SCHED_GREEDY, target_sigma: float = 0.5,
+                       target_seed: int = 0, pt_tok: bool = True, out=None, ws=None,
+                       stream=None):
+    """`rounds` chained rounds with the synthetic Markov target.  Returns a dict of device
+    tensors, one slice per round: anchors [R][B], tokens [R][B][gamma], c [R][B][gamma],
+    ell [R][B], theta [R], n_total [R], n_accept [R][B], out_tokens [R][B][gamma+1],
+    pt_tok [R][B][gamma] (or None)."""
+    B, G, V = U.shape
+    r = W1.shape[1]
+    d = h.shape[2]
+    _f32(U, "U")
+    _i32(anchor, "anchor")
+    if sps.dtype != torch.float64:
+        raise ValueError("sps must be float64")
+    R = int(rounds)
+    dev = U.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"anchors": torch.empty(R, B, **i32), "tokens": torch.empty(R, B, G, **i32),
+               "c": torch.empty(R, B, G, dtype=torch.float32, device=dev),
+               "ell": torch.empty(R, B, **i32),
+               "theta": torch.empty(R, dtype=torch.float64, device=dev),
+               "n_total": torch.empty(R, **i32), "n_accept": torch.empty(R, B, **i32),
+               "out_tokens": torch.empty(R, B, G + 1, **i32),
+               "pt_tok": torch.empty(R, B, G, dtype=torch.float32, device=dev) if pt_tok else None}
+    dm = Dims(B, G, V, r, d)
+    need = int(lib().dspark_loop_workspace_bytes(ctypes.byref(dm)))
+    if need == 0:
+        raise DsparkError("dspark_loop_workspace_bytes: dims out of range")
+    wsb = _workspace(dev, need, ws)
+    _check(lib().dspark_closed_loop(
+        ctypes.byref(dm), _ptr(U), _ptr(W1), _ptr(W2t), _wdtype(W1), _ptr(h), _wdtype(h),
+        _ptr(w), _wdtype(w), _ptr(anchor), _ptr(sps), int(sched_mode), float(temperature),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, float(target_sigma),
+        int(target_seed) & 0xFFFFFFFFFFFFFFFF, R, _ptr(out["anchors"]), _ptr(out["tokens"]),
+        _ptr(out["c"]), _ptr(out["ell"]), _ptr(out["theta"]), _ptr(out["n_total"]),
+        _ptr(out["n_accept"]), _ptr(out["out_tokens"]), _ptr(out["pt_tok"]), _ptr(wsb),
+        wsb.numel(), _stream_handle(stream)))
+    return out
 
 
 def dspark_draft_loss(zd, zt, labels, conf_logit, alphas=(0.1, 0.9, 1.0), grads=True,

@@ -18,6 +18,8 @@
  *      dspark_schedule_topk  its production form: top-K admission, K from history [XTL §7]
  *   4. dspark_verify         lossless rejection-sampling verification         [XTL §1; AIMSG 2]
  *   5. dspark_accept_rate_tv analytic accept rate 1 - |p_d - p_t|_1 / 2       [CSDN Eq. 8; XTL §5]
+ *   7. dspark_closed_loop    rounds 1-5 chained on the GPU with a synthetic Markov target,
+ *                            the accepted length tau per round           [CSDN Eq. 1]
  * and, on the training side of the same heads:
  *   6. dspark_draft_loss     distribution-matching loss (CE + L1 + confidence BCE, position
  *                            weights) and its gradients                   [XTL §9, §5, §8]
@@ -257,6 +259,39 @@ dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, con
                                     const int32_t* tokens, const float* lse, const float* T,
                                     float temperature, float* alpha, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/*
+ * A closed loop of `rounds` rounds on `stream`, with no host synchronisation between them.
+ * Round t (0-based) drafts from anchor_t (anchor_0 = anchor, later the last token the
+ * previous round emitted), scores the block with the confidence head, schedules it
+ * (sched_mode as for dspark_schedule), builds the stand-in target logits and verifies,
+ * each call as documented above with seed_t = seed + t.  The accepted length of request b
+ * in round t is n_accept + 1 tokens; the latency per token of the speculative loop is
+ * (T_draft + T_verify) / tau [CSDN Eq. 1].
+ * Stand-in target (a synthetic Markov chain over tokens, not part of the method): position
+ * j + 1 (j = 0..gamma) of request b has logits
+ *   T[b][j][v] = U[b][min(j, gamma-1)][v] + target_sigma sqrt(3) (2 u - 1),
+ *   u = u(target_seed, prev, 0, 3, v),   prev = anchor_t[b] (j = 0) or tokens[b][j-1],
+ * a zero-mean transition term of variance target_sigma^2 keyed by the previous token.
+ * Arguments: dims, U, W1, W2t, wdt, temperature as for dspark_draft_markov; h, hdt, w, wvdt
+ * as for dspark_confidence; sps, sched_mode as for dspark_schedule; target_sigma >= 0.
+ * Outputs, one slice per round (row-major, round first):
+ *   anchors [R][B] (or NULL), tokens [R][B][gamma], c [R][B][gamma], ell [R][B],
+ *   theta [R] (or NULL), n_total [R], n_accept [R][B], out_tokens [R][B][gamma+1],
+ *   pt_tok [R][B][gamma] (or NULL).
+ * rounds in 1..65536.  Workspace: dspark_loop_workspace_bytes(dims) bytes (it holds one
+ * round's target logits, B (gamma+1) V floats).
+ */
+size_t dspark_loop_workspace_bytes(const dspark_dims* dims);
+dspark_status dspark_closed_loop(const dspark_dims* dims, const float* U, const void* W1,
+                                 const void* W2t, int wdt, const void* h, int hdt,
+                                 const void* w, int wvdt, const int32_t* anchor,
+                                 const double* sps, int sched_mode, float temperature,
+                                 uint64_t seed, float target_sigma, uint64_t target_seed,
+                                 int32_t rounds, int32_t* anchors, int32_t* tokens, float* c,
+                                 int32_t* ell, double* theta, int32_t* n_total,
+                                 int32_t* n_accept, int32_t* out_tokens, float* pt_tok,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Distribution-matching training loss of the draft and confidence heads, forward and

@@ -116,6 +116,29 @@ def test_draft_loss_validation():
     assert L.dspark_loss_workspace_bytes(128, 16, 151936) >= 2048 * 38 * 6 * 8
 
 
+def test_closed_loop_validation():
+    L = ds.lib()
+    dm = _dims()
+    ws = 1 << 34
+    f = L.dspark_closed_loop
+
+    def call(dims=ctypes.byref(dm), U=P, anchor=P, rounds=3, sigma=0.5, temp=1.0, mode=0,
+             wsb=ws, tokens=P):
+        return f(dims, U, P, P, 1, P, 1, P, 1, anchor, P, mode, temp, 1, sigma, 2, rounds,
+                 None, tokens, P, P, None, P, P, P, None, P, wsb, None)
+    assert call(U=None) == 1
+    assert call(tokens=None) == 1
+    assert call(rounds=0) == 2
+    assert call(rounds=65537) == 2
+    assert call(sigma=-1.0) == 4
+    assert call(sigma=float("nan")) == 4
+    assert call(temp=0.0) == 4
+    assert call(mode=7) == 4
+    need = L.dspark_loop_workspace_bytes(ctypes.byref(dm))
+    assert need >= dm.batch * (dm.gamma + 1) * dm.vocab * 4
+    assert call(wsb=need - 1) == 5
+
+
 def test_verify_confidence_tv_validation():
     L = ds.lib()
     dm = _dims()
