@@ -179,6 +179,37 @@ def main():
     torch.cuda.synchronize()
     verify_ms = vf0.elapsed_time(vf1) / args.steps
 
+    # the draft side of a round alone (draft, confidence, schedule)
+    ds0 = torch.cuda.Event(enable_timing=True)
+    ds1 = torch.cuda.Event(enable_timing=True)
+    ds0.record(stream)
+    for _ in range(args.steps):
+        ds.dspark_draft_markov(U, W1, W2t, anchor, temp, inp.seed, out=(tokens, logp, lse),
+                               ws=ws_d)
+        ds.dspark_confidence(h, W1, w, anchor, tokens, out=conf)
+        ds.dspark_schedule(conf, sps, cfg.sched_mode, out=(ell, theta, ntot))
+    ds1.record(stream)
+    torch.cuda.synchronize()
+    draft_side_ms = ds0.elapsed_time(ds1) / args.steps
+
+    # closed loop: LOOP_R rounds chained on the device (next anchor = last emitted token)
+    # with the synthetic Markov stand-in target (transition term sigma = 0.5); the loop's
+    # latency per token is the round time over tau, the tokens a request gains per round
+    LOOP_R = 8
+    ds.dspark_closed_loop(U, W1, W2t, h, w, anchor, sps, 2, temp, inp.seed, cfg.sched_mode,
+                          0.5, 1, pt_tok=False)
+    lp0 = torch.cuda.Event(enable_timing=True)
+    lp1 = torch.cuda.Event(enable_timing=True)
+    lp0.record(stream)
+    loop_out = ds.dspark_closed_loop(U, W1, W2t, h, w, anchor, sps, LOOP_R, temp, inp.seed,
+                                     cfg.sched_mode, 0.5, 1, pt_tok=False)
+    lp1.record(stream)
+    torch.cuda.synchronize()
+    loop_round_ms = lp0.elapsed_time(lp1) / LOOP_R
+    loop_tau = (loop_out["n_accept"].double() + 1.0).mean(dim=1).cpu().numpy()
+    del loop_out
+    torch.cuda.empty_cache()
+
     # the production form of the scheduler (top-K admission, K from history): timed alone at
     # this round's admitted count; one workgroup, latency-bound, so reported in us only
     k_admit = int(ntot.cpu()[0]) - B
@@ -297,6 +328,14 @@ def main():
         "schedule_topk_us": round(topk_us, 2),
         "sts_calibrate_ms": round(sts_ms, 4),
         "sts_sigmoids_per_s": round(131072 * 256 * G / (sts_ms * 1e-3), 1),
+        "loop_rounds": LOOP_R,
+        "loop_round_ms": round(loop_round_ms, 4),
+        "loop_draft_side_ms": round(draft_side_ms, 4),
+        "loop_verify_side_ms": round(loop_round_ms - draft_side_ms, 4),
+        "loop_tau_per_round": [round(float(x), 3) for x in loop_tau],
+        "loop_tau": round(float(loop_tau.mean()), 4),
+        "loop_ms_per_token": round(loop_round_ms / float(loop_tau.mean()), 4),
+        "loop_tokens_per_s": round(B * float(loop_tau.mean()) / (loop_round_ms * 1e-3), 1),
         "loss_call_ms": round(loss_ms, 4),
         "loss_hbm_frac": round(loss_bytes / (loss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "loss_value": round(loss_val, 6),

@@ -26,7 +26,8 @@ namespace dspark {
 constexpr int kTargetChunk = 256 * 4;   // vocab entries per workgroup of k_markov_target
 
 // one workgroup per (row b*(G+1)+j, chunk of 1024 vocab entries); a thread writes 4
-// consecutive entries from one Philox call
+// consecutive entries from one Philox call (16-byte accesses when rows are 16-byte aligned)
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_markov_target(const float* __restrict__ U,
                                                        const int32_t* __restrict__ anchor,
                                                        const int32_t* __restrict__ tokens,
@@ -42,12 +43,19 @@ __global__ __launch_bounds__(256) void k_markov_target(const float* __restrict__
   const int v0 = 4 * q;
   if (v0 >= V) return;
   const U4 w = philox10((uint32_t)q, 0u, (uint32_t)prev, 3u, key0, key1);
-  const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+  // 2u - 1 is exact in fp32 (u is an odd multiple of 2^-24)
+  const float n0 = scale * (2.f * word_to_uniform(w.x) - 1.f);
+  const float n1 = scale * (2.f * word_to_uniform(w.y) - 1.f);
+  const float n2 = scale * (2.f * word_to_uniform(w.z) - 1.f);
+  const float n3 = scale * (2.f * word_to_uniform(w.w) - 1.f);
+  if constexpr (VEC) {   // V % 4 == 0: the quad lies inside the row
+    const float4 bv = *reinterpret_cast<const float4*>(base + v0);
+    *reinterpret_cast<float4*>(out + v0) = make_float4(bv.x + n0, bv.y + n1, bv.z + n2, bv.w + n3);
+  } else {
+    const float nz[4] = {n0, n1, n2, n3};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = v0 + i;
-    // 2u - 1 is exact in fp32 (u is an odd multiple of 2^-24)
-    if (v < V) out[v] = base[v] + scale * (2.f * word_to_uniform(words[i]) - 1.f);
+    for (int i = 0; i < 4; ++i)
+      if (v0 + i < V) out[v0 + i] = base[v0 + i] + nz[i];
   }
 }
 
@@ -135,6 +143,7 @@ extern "C" dspark_status dspark_closed_loop(
   const float scale = (float)((double)target_sigma * std::sqrt(3.0));
   const uint32_t tk0 = (uint32_t)target_seed, tk1 = (uint32_t)(target_seed >> 32);
   const unsigned bgrid = (unsigned)((B + 255) / 256);
+  const bool vec_target = V % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)lw.T % 16 == 0;
   if (anchors) {
     hipLaunchKernelGGL(k_copy_i32, dim3(bgrid), dim3(256), 0, st, anchor, B, anchors);
     if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
@@ -156,8 +165,12 @@ extern "C" dspark_status dspark_closed_loop(
     s = dspark_schedule(B, G, c_t, sps, sched_mode, ell_t, theta ? theta + t : lw.theta,
                         n_total + t, nullptr, 0, stream);
     if (s != DSPARK_OK) return s;
-    hipLaunchKernelGGL(k_markov_target, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0, st, U,
-                       anc_t, tok_t, G, V, nchunk, scale, tk0, tk1, lw.T);
+    if (vec_target)
+      hipLaunchKernelGGL(k_markov_target<true>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0, st,
+                         U, anc_t, tok_t, G, V, nchunk, scale, tk0, tk1, lw.T);
+    else
+      hipLaunchKernelGGL(k_markov_target<false>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0,
+                         st, U, anc_t, tok_t, G, V, nchunk, scale, tk0, tk1, lw.T);
     if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
     s = dspark_verify(dims, U, W1, W2t, wdt, anc_t, tok_t, lw.logp, lw.lse, lw.T, ell_t,
                       temperature, seed_t, n_t, out_t, pt_tok ? pt_tok + (size_t)t * BG : nullptr,
