@@ -28,13 +28,14 @@
 //     does not see, so nothing waits for them before they are needed;
 //   * the stream meets once per row: one exchange carries the current row's L1 and S
 //     partials together with the next row's (max, sum) partials, which the waves compute
-//     from the LDS copy; wave 0 publishes them with device-scope atomic stores, counts
-//     arrivals on a per-exchange counter, polls it, and combines the C partials in fp64 in
-//     one round trip of loads.  No cache-wide fence is involved;
+//     from the LDS copy; wave 0 publishes each as one 64-bit word (a written-mark and the
+//     fp32 value) with a device-scope atomic store, then polls the C workgroups' words
+//     directly -- the data arrive with the poll -- and combines them in fp64.  No counter,
+//     no store-completion wait and no cache-wide fence is involved;
 //   * every wait is bounded: a poll that runs past its limit raises a fault word, the
 //     stream stops, and the loss is written as NaN.
-// HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 32 bytes of
-// partials per chunk and row.
+// HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 48 bytes of
+// published partials per chunk and row (cleared before the launch).
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_common.h"
@@ -46,12 +47,13 @@ constexpr int kLossThreads = kLossWaves * kWave;          // 256: one wave per S
 constexpr int kLossPer = 16;                              // entries per lane per row
 constexpr int kLossChunk = kLossThreads * kLossPer;       // 4096 entries
 constexpr int kLossMaxVocab = 1 << 22;
-// Arrival counters sit 128 bytes apart: the pollers of rows in flight at once never share
-// a line.
-constexpr int kCntStride = 32;
-// Polls of a counter between two looks at the fault word (every poller reading one shared
-// word each time would make it a hot spot).
+// Polls between two looks at the fault word (every poller reading one shared word each
+// time would make it a hot spot).
 constexpr uint32_t kFaultCheckPolls = 64;
+// A published partial is the 64-bit word kSlotValid | (fp32 bits): the words are cleared to
+// zero before the launch, so one atomic store both carries a value and announces it, and a
+// reader needs no separate arrival counter.
+constexpr unsigned long long kSlotValid = 1ull << 32;
 
 struct LossArgs {
   const float* zd;
@@ -62,9 +64,8 @@ struct LossArgs {
   float* grad_conf;     // [R] or null
   float* terms;         // [R][3] or null
   double* rowloss;      // [R] weighted row contributions
-  double* part1;        // [R][C][4] (max_d, sum_d, max_t, sum_t)
-  double* part2;        // [R][C][2] (l1, S)
-  uint32_t* cnt;        // [R + P][kCntStride]: arrivals per exchange (word 0 used)
+  unsigned long long* part1;   // [R][C][4] published (max_d, sum_d, max_t, sum_t)
+  unsigned long long* part2;   // [R][C][2] published (l1, S)
   uint32_t* fault;
   int R, G, V, C, L, P;
   double a_ce, a_l1, a_conf, inv_W;
@@ -77,52 +78,64 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ double ld_dev(const double* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(double* p, double v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Wave 0: publish this workgroup's partials -- lanes 0..na-1 hold the values of slot_a,
+// lanes na..na+nb-1 those of slot_b.  Each lane's word is a device-scope atomic store that
+// needs no ordering against any other (see kSlotValid), so nothing waits for it.
+__device__ __forceinline__ void publish(unsigned long long* slot_a, int na,
+                                        unsigned long long* slot_b, int nb, double v, int lane) {
+  unsigned long long* w = lane < na ? slot_a + lane : (lane < na + nb ? slot_b + (lane - na) : nullptr);
+  if (w)
+    __hip_atomic_store(w, kSlotValid | (unsigned long long)__float_as_uint((float)v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0: publish this workgroup's partials -- lanes 0..na-1 hold the values of slot_a,
-// lanes na..na+nb-1 those of slot_b -- arrive on the exchange's counter and wait for all C
-// arrivals.  Lane 0 does the stores, the increment and the polling.  Every access to the
-// exchanged words is a device-scope atomic (they bypass the non-coherent caches), so the
-// ordering needs no cache-wide fence: the partials' stores are complete (s_waitcnt) before
-// the increment is issued, and the partials are loaded only after the poll has seen every
-// increment.  (A release/acquire fence pair would write back and invalidate the whole L2
-// at every exchange.)  Returns false when the wait gave up.
-__device__ __forceinline__ bool exchange(const LossArgs& a, double* slot_a, int na,
-                                         double* slot_b, int nb, double v, uint32_t* counter,
-                                         int lane) {
-  double vals[6];
+// Poll the NA words at pa and the NB words at pb (device-scope atomic loads, which bypass
+// the non-coherent caches) until every one is published; their values into qa, qb.  Returns
+// false when the wait gave up: its poll limit ran out (the fault word is raised) or another
+// workgroup raised the fault word.
+template <int NA, int NB>
+__device__ __forceinline__ bool await_words(const LossArgs& a, const unsigned long long* pa,
+                                            const unsigned long long* pb, float* qa,
+                                            float* qb) {
+  uint32_t polls = 0;
+  for (;;) {
+    unsigned long long wa[NA], wb[NB > 0 ? NB : 1];
 #pragma unroll
-  for (int i = 0; i < 6; ++i) vals[i] = __shfl(v, i, kWave);
-  bool ok = true;
-  if (lane == 0) {
+    for (int i = 0; i < NA; ++i)
+      wa[i] = __hip_atomic_load(pa + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      if (i < na) st_dev(slot_a + i, vals[i]);
-      else if (i < na + nb) st_dev(slot_b + (i - na), vals[i]);
+    for (int i = 0; i < NB; ++i)
+      wb[i] = __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      all = all && (wa[i] >> 32) != 0ull;
+      qa[i] = __uint_as_float((uint32_t)wa[i]);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t polls = 0;
-    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-           (uint32_t)a.C) {
-      ++polls;
-      if (polls > a.spin_limit ||
-          (polls % kFaultCheckPolls == 0 &&
-           __hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
-        __hip_atomic_store(a.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      all = all && (wb[i] >> 32) != 0ull;
+      qb[i] = __uint_as_float((uint32_t)wb[i]);
     }
+    if (all) return true;
+    ++polls;
+    if (polls > a.spin_limit ||
+        (polls % kFaultCheckPolls == 0 &&
+         __hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+      __hip_atomic_store(a.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
   }
-  asm volatile("" ::: "memory");   // the partials' loads stay after the poll
-  return __shfl(ok ? 1 : 0, 0, kWave) != 0;
+}
+
+// online (max, sum) merge of one published partial pair into (m, s), in fp64
+__device__ __forceinline__ void ml_add(double& m, double& s, float pm, float ps) {
+  if (ps > 0.f) {
+    const double mm = fmax(m, (double)pm);
+    s = s * (double)fast_exp((float)(m - mm)) + (double)ps * (double)fast_exp((float)((double)pm - mm));
+    m = mm;
+  }
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -321,23 +334,17 @@ __device__ __forceinline__ RowScalars row_scalars(const LossArgs& a, int r) {
 // wave 0, after the prologue's exchange: row r's normalisers from its C chunk partials
 // -> sh.r1 (lane 0 writes); returns lse of the draft logits in fp64
 __device__ __forceinline__ double combine_part1(const LossArgs& a, LossShared& sh, int r,
-                                                int lane) {
-  // per lane: online (max, sum) over its chunks; all loads of a pass issued together
+                                                int lane, bool& ok) {
+  // per lane: online (max, sum) over its chunks, each polled until published
   double m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
-  for (int cc = lane; cc < a.C; cc += kWave) {
-    const double* p = a.part1 + ((size_t)r * a.C + cc) * 4;
-    const double pm_d = ld_dev(p), ps_d = ld_dev(p + 1), pm_t = ld_dev(p + 2), ps_t = ld_dev(p + 3);
-    if (ps_d > 0.0) {
-      const double m = fmax(m_d, pm_d);
-      s_d = s_d * (double)fast_exp((float)(m_d - m)) + ps_d * (double)fast_exp((float)(pm_d - m));
-      m_d = m;
-    }
-    if (ps_t > 0.0) {
-      const double m = fmax(m_t, pm_t);
-      s_t = s_t * (double)fast_exp((float)(m_t - m)) + ps_t * (double)fast_exp((float)(pm_t - m));
-      m_t = m;
-    }
+  bool mine = true;
+  for (int cc = lane; cc < a.C && mine; cc += kWave) {
+    float q[4];
+    mine = await_words<4, 0>(a, a.part1 + ((size_t)r * a.C + cc) * 4, nullptr, q, nullptr);
+    ml_add(m_d, s_d, q[0], q[1]);
+    ml_add(m_t, s_t, q[2], q[3]);
   }
+  ok = __ballot(!mine) == 0ull;
   const double M_d = wave_max_d(m_d), M_t = wave_max_d(m_t);
   s_d = s_d > 0.0 ? s_d * (double)fast_exp((float)(m_d - M_d)) : 0.0;
   s_t = s_t > 0.0 ? s_t * (double)fast_exp((float)(m_t - M_t)) : 0.0;
@@ -357,29 +364,24 @@ __device__ __forceinline__ double combine_part1(const LossArgs& a, LossShared& s
 // lse_d: in, row r's; out, row rn's.
 __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, int r, int rn,
                                              bool has_next, int c, double& lse_d,
-                                             const RowScalars& rs, int lane) {
+                                             const RowScalars& rs, int lane, bool& ok) {
   double l1 = 0.0, S = 0.0, m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
-  for (int cc = lane; cc < a.C; cc += kWave) {
-    const double* p2 = a.part2 + ((size_t)r * a.C + cc) * 2;
-    const double* p1 = a.part1 + ((size_t)(has_next ? rn : r) * a.C + cc) * 4;
-    const double q0 = ld_dev(p2), q1 = ld_dev(p2 + 1);
-    double pm_d = -INFINITY, ps_d = 0.0, pm_t = -INFINITY, ps_t = 0.0;
+  bool mine = true;
+  for (int cc = lane; cc < a.C && mine; cc += kWave) {
+    const unsigned long long* p2 = a.part2 + ((size_t)r * a.C + cc) * 2;
+    float q2[2], q1[4];
     if (has_next) {
-      pm_d = ld_dev(p1); ps_d = ld_dev(p1 + 1); pm_t = ld_dev(p1 + 2); ps_t = ld_dev(p1 + 3);
+      mine = await_words<2, 4>(a, p2, a.part1 + ((size_t)rn * a.C + cc) * 4, q2, q1);
+      ml_add(m_d, s_d, q1[0], q1[1]);
+      ml_add(m_t, s_t, q1[2], q1[3]);
+    } else {
+      mine = await_words<2, 0>(a, p2, nullptr, q2, nullptr);
     }
-    l1 += q0;
-    S += q1;
-    if (ps_d > 0.0) {
-      const double m = fmax(m_d, pm_d);
-      s_d = s_d * (double)fast_exp((float)(m_d - m)) + ps_d * (double)fast_exp((float)(pm_d - m));
-      m_d = m;
-    }
-    if (ps_t > 0.0) {
-      const double m = fmax(m_t, pm_t);
-      s_t = s_t * (double)fast_exp((float)(m_t - m)) + ps_t * (double)fast_exp((float)(pm_t - m));
-      m_t = m;
-    }
+    l1 += (double)q2[0];
+    S += (double)q2[1];
   }
+  ok = __ballot(!mine) == 0ull;
+  if (!ok) return;
   l1 = wave_sum_d(l1);
   S = wave_sum_d(S);
   if (lane == 0) {
@@ -444,7 +446,6 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
   uint32_t mask = 0;
 #pragma unroll
   for (int e = 0; e < kLossPer; ++e) mask |= (slice_off(tid, e) < len ? 1u : 0u) << e;
-  uint32_t* const cnt_end = a.cnt + (size_t)(a.R + p) * kCntStride;
   float d[kLossPer], t[kLossPer];
   double lse_cur = 0.0;   // wave 0: lse of the current row's draft logits
 
@@ -466,9 +467,9 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
   raw_barrier();
   if (lead) {
     const double v = combine_waves1(sh, lane);
-    const bool ok = exchange(a, a.part1 + ((size_t)p * a.C + c) * 4, 4, nullptr, 0, v,
-                             a.cnt + (size_t)p * kCntStride, lane);
-    if (ok) lse_cur = combine_part1(a, sh, p, lane);
+    publish(a.part1 + ((size_t)p * a.C + c) * 4, 4, nullptr, 0, v, lane);
+    bool ok = true;
+    lse_cur = combine_part1(a, sh, p, lane, ok);
     if (lane == 0) sh.stop = ok ? 0 : 1;
   }
   raw_barrier();
@@ -510,11 +511,10 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
       double v = has_next ? combine_waves1(sh, lane - 2 < 0 ? 63 : lane - 2) : 0.0;
       if (lane < 2)
         for (int w = 0; w < kLossWaves; ++w) v += (double)sh.w2[w][lane];
-      const bool ok =
-          exchange(a, a.part2 + ((size_t)r * a.C + c) * 2, 2,
-                   a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v,
-                   has_next ? a.cnt + (size_t)rn * kCntStride : cnt_end, lane);
-      if (ok) combine_step(a, sh, r, rn, has_next, c, lse_cur, rs, lane);
+      publish(a.part2 + ((size_t)r * a.C + c) * 2, 2,
+              a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v, lane);
+      bool ok = true;
+      combine_step(a, sh, r, rn, has_next, c, lse_cur, rs, lane, ok);
       if (lane == 0) sh.stop = ok ? 0 : 1;
     }
     raw_barrier();
@@ -543,10 +543,11 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
   if constexpr (VEC) wait_vm<0>();   // nothing in flight into LDS when the workgroup ends
 }
 
-__global__ __launch_bounds__(256) void k_loss_init(uint32_t* __restrict__ cnt, size_t n,
-                                                   uint32_t* __restrict__ fault) {
+// clears the published words (part1 and part2, n words from `words`) and the fault word
+__global__ __launch_bounds__(256) void k_loss_init(unsigned long long* __restrict__ words,
+                                                   size_t n, uint32_t* __restrict__ fault) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  for (size_t j = i; j < n; j += (size_t)gridDim.x * blockDim.x) cnt[j] = 0u;
+  for (size_t j = i; j < n; j += (size_t)gridDim.x * blockDim.x) words[j] = 0ull;
   if (i == 0) *fault = 0u;
 }
 
@@ -573,10 +574,10 @@ using namespace dspark;
 namespace {
 
 struct LossWs {
-  double* part1;
-  double* part2;
+  unsigned long long* part1;   // published words: part1 then part2, one block
+  unsigned long long* part2;
+  size_t nwords;
   double* rowloss;
-  uint32_t* cnt;
   uint32_t* fault;
   size_t bytes;
 };
@@ -587,10 +588,10 @@ LossWs loss_ws(int R, int V, void* base) {
   const int C = loss_chunks(V);
   Carve c(base);
   LossWs w;
-  w.part1 = c.take<double>((size_t)R * C * 4);
-  w.part2 = c.take<double>((size_t)R * C * 2);
+  w.nwords = (size_t)R * C * 6;
+  w.part1 = c.take<unsigned long long>(w.nwords);
+  w.part2 = w.part1 ? w.part1 + (size_t)R * C * 4 : nullptr;
   w.rowloss = c.take<double>((size_t)R);
-  w.cnt = c.take<uint32_t>(((size_t)R + 1024) * kCntStride);
   w.fault = c.take<uint32_t>(1);
   w.bytes = align_up(c.off, 256);
   return w;
@@ -646,21 +647,21 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
   LossArgs a;
   a.zd = zd; a.zt = zt; a.labels = labels; a.conf = conf_logit;
   a.grad = grad_zd; a.grad_conf = grad_conf; a.terms = terms;
-  a.rowloss = w.rowloss; a.part1 = w.part1; a.part2 = w.part2; a.cnt = w.cnt; a.fault = w.fault;
+  a.rowloss = w.rowloss; a.part1 = w.part1; a.part2 = w.part2; a.fault = w.fault;
   a.R = R; a.G = G; a.V = V;
   a.C = loss_chunks(V);
   a.L = (V + 4 * a.C - 1) / (4 * a.C) * 4;
   if (cap < a.C) return DSPARK_E_HIP;   // no cooperative launch, or a row does not fit
-  a.P = std::min(std::min(R, cap / a.C), 1024);   // the end-of-stream counters hold 1024
+  a.P = std::min(R, cap / a.C);
   double wsum = 0.0;
   for (int k = 0; k < G; ++k) wsum += std::exp(-(double)k / G);
   a.inv_W = 1.0 / ((double)B * wsum);
   a.a_ce = alpha_ce; a.a_l1 = alpha_l1; a.a_conf = alpha_conf;
   a.spin_limit = 1u << 22;
   hipStream_t st = (hipStream_t)stream;
-  const size_t ncnt = ((size_t)R + 1024) * kCntStride;
-  hipLaunchKernelGGL(k_loss_init, dim3((unsigned)std::min<size_t>(256, (ncnt + 255) / 256)),
-                     dim3(256), 0, st, w.cnt, ncnt, w.fault);
+  hipLaunchKernelGGL(k_loss_init,
+                     dim3((unsigned)std::min<size_t>(2048, (w.nwords + 255) / 256)), dim3(256),
+                     0, st, w.part1, w.nwords, w.fault);
   if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
   void* args[] = {&a};
   const void* fn = vec ? (const void*)k_draft_loss<true> : (const void*)k_draft_loss<false>;
