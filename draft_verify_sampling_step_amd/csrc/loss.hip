@@ -19,10 +19,10 @@
 // compute unit, and re-reading them twice from HBM would more than double the traffic.
 // Instead one cooperative launch keeps every logit on chip from its single read to the
 // gradient write:
-//   * a row's vocabulary is cut into C chunks of at most 4096 entries; a "stream" of C
+//   * a row's vocabulary is cut into C chunks of at most 8192 entries; a "stream" of C
 //     workgroups (chunk c of rows p, p + P, p + 2P, ...) works through its rows together,
 //     P streams at once, every workgroup resident (cooperative launch);
-//   * a workgroup is four waves (one per SIMD, so four workgroups pack evenly on a compute
+//   * a workgroup is eight waves (two per SIMD, so two workgroups pack evenly on a compute
 //     unit), 16 entries of the current row per lane in registers; the next row's chunk
 //     streams into LDS by direct global-to-LDS loads, which the compiler's wait counting
 //     does not see, so nothing waits for them before they are needed;
@@ -42,10 +42,12 @@
 
 namespace dspark {
 
-constexpr int kLossWaves = 4;                             // every wave holds entries
-constexpr int kLossThreads = kLossWaves * kWave;          // 256: one wave per SIMD
+constexpr int kLossWaves = 8;                             // every wave holds entries
+constexpr int kLossThreads = kLossWaves * kWave;          // two waves per SIMD
+constexpr int kLossWavesPerSimd = 4;                      // occupancy target (<= 128 VGPRs)
 constexpr int kLossPer = 16;                              // entries per lane per row
-constexpr int kLossChunk = kLossThreads * kLossPer;       // 4096 entries
+constexpr int kLossChunk = kLossThreads * kLossPer;       // 8192 entries
+constexpr int kQuad = 4 * kLossThreads;                   // chunk offset between a lane's quads
 constexpr int kLossMaxVocab = 1 << 22;
 // Polls between two looks at the fault word (every poller reading one shared word each
 // time would make it a hot spot).
@@ -151,11 +153,11 @@ __device__ __forceinline__ double wave_max_d(double v) {
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-// Entry e of a lane's slice: chunk-relative offset 4*lane' + 1024*(e/4) + e%4, lane' the
-// lane index in the workgroup.  Quad e/4 of the four waves is one contiguous 4 KiB piece of
-// the chunk, 1 KiB per wave.  The LDS stage mirrors the chunk: draft logits at float 0,
+// Entry e of a lane's slice: chunk-relative offset 4*lane' + kQuad*(e/4) + e%4, lane' the
+// lane index in the workgroup.  Quad e/4 of all the waves is one contiguous piece of the
+// chunk, 1 KiB per wave.  The LDS stage mirrors the chunk: draft logits at float 0,
 // target logits at float kLossChunk, each entry where its owner lane reads it back.
-__device__ __forceinline__ int slice_off(int ct, int e) { return 4 * ct + 1024 * (e >> 2) + (e & 3); }
+__device__ __forceinline__ int slice_off(int ct, int e) { return 4 * ct + kQuad * (e >> 2) + (e & 3); }
 
 // Start staging row r's chunk into LDS.  16-byte rows: direct global-to-LDS loads, which the
 // compiler's wait counting does not see (nothing waits for them until wait_stage).  A lane
@@ -182,11 +184,11 @@ __device__ __forceinline__ void stage_row(const LossArgs& a, int r, int c, int c
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // earlier reads of the stage are done
 #pragma unroll
     for (int q = 0; q < kLossPer / 4; ++q) {
-      const int o = 4 * ct + 1024 * q;
+      const int o = 4 * ct + kQuad * q;
       const uint32_t voff = 4u * (uint32_t)(o < len ? o : len - 4);
       // wave-uniform LDS address (M0), formed in scalar registers
       const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)ct >> 6);
-      const uint32_t dst = stage_lds + 4u * (1024u * q + 256u * wv);
+      const uint32_t dst = stage_lds + 4u * ((uint32_t)kQuad * q + 256u * wv);
       dma16(pd, voff, dst);
       dma16(pt, voff, dst + 4u * kLossChunk);
     }
@@ -212,8 +214,8 @@ __device__ __forceinline__ void wait_stage() {
 __device__ __forceinline__ void read_stage(const float* stage, int ct, float* d, float* t) {
 #pragma unroll
   for (int q = 0; q < kLossPer / 4; ++q) {
-    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + 1024 * q);
-    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + 1024 * q);
+    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + kQuad * q);
+    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + kQuad * q);
     d[4 * q] = vd.x; d[4 * q + 1] = vd.y; d[4 * q + 2] = vd.z; d[4 * q + 3] = vd.w;
     t[4 * q] = vt.x; t[4 * q + 1] = vt.y; t[4 * q + 2] = vt.z; t[4 * q + 3] = vt.w;
   }
@@ -229,7 +231,7 @@ __device__ __forceinline__ void store_grad(const LossArgs& a, int r, int c, int 
   if constexpr (VEC) {
 #pragma unroll
     for (int q = 0; q < kLossPer / 4; ++q) {
-      const int o = 4 * ct + 1024 * q;
+      const int o = 4 * ct + kQuad * q;
       if (o < len)
         __builtin_nontemporal_store(f4v{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]},
                                     reinterpret_cast<f4v*>(out + o));
@@ -253,8 +255,8 @@ __device__ __forceinline__ void stage_ml(const float* stage, int ct, uint32_t ma
   float xd = -INFINITY, xt = -INFINITY;
 #pragma unroll
   for (int q = 0; q < kLossPer / 4; ++q) {
-    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + 1024 * q);
-    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + 1024 * q);
+    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + kQuad * q);
+    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + kQuad * q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool on = live(mask, 4 * q + i);
@@ -266,8 +268,8 @@ __device__ __forceinline__ void stage_ml(const float* stage, int ct, uint32_t ma
   float sd = 0.f, st = 0.f;
 #pragma unroll
   for (int q = 0; q < kLossPer / 4; ++q) {
-    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + 1024 * q);
-    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + 1024 * q);
+    const f4v vd = *reinterpret_cast<const f4v*>(stage + 4 * ct + kQuad * q);
+    const f4v vt = *reinterpret_cast<const f4v*>(stage + kLossChunk + 4 * ct + kQuad * q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool on = live(mask, 4 * q + i);
@@ -286,6 +288,8 @@ struct LossShared {
   float r2[3];               // current row: (S, w alpha_ce, w alpha_l1)
   int y;                     // current row: the label, clamped into the vocabulary
   int stop;
+  double lse;                // wave 0's: lse of the current row's draft logits (kept in LDS
+                             // rather than across the sweeps in registers)
 };
 
 // wave 0: the four waves' (max, sum) pairs of one logit set combined in fp64 (lanes 0..3
@@ -361,9 +365,9 @@ __device__ __forceinline__ double combine_part1(const LossArgs& a, LossShared& s
 // wave 0, after a loop exchange: row r's l1 and S and (has_next) row rn's normalisers from
 // the C chunk partials, all loaded in one round trip; the row's scalar outputs (chunk 0's
 // workgroup) and the gradient coefficients -> sh.r2, sh.y; rn's normalisers -> sh.r1.
-// lse_d: in, row r's; out, row rn's.
+// sh.lse: read as row r's lse, then replaced by row rn's.
 __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, int r, int rn,
-                                             bool has_next, int c, double& lse_d,
+                                             bool has_next, int c,
                                              const RowScalars& rs, int lane, bool& ok) {
   double l1 = 0.0, S = 0.0, m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
   bool mine = true;
@@ -392,7 +396,7 @@ __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, 
     sh.r2[2] = (float)(wk * a.a_l1);
     sh.y = rs.y;
     if (c == 0) {
-      const double ce = lse_d - (double)rs.zy;
+      const double ce = sh.lse - (double)rs.zy;
       const double at = 1.0 - 0.5 * l1;
       // log(1 + e^l) and sigmoid(l) in fp32 through e = exp(-|l|) in (0, 1]
       const float lf = rs.lf;
@@ -421,7 +425,7 @@ __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, 
       sh.r1[0] = (float)M_d; sh.r1[1] = ls_d;
       sh.r1[2] = (float)M_t; sh.r1[3] = ls_t;
     }
-    lse_d = M_d + (double)ls_d;
+    if (lane == 0) sh.lse = M_d + (double)ls_d;
   }
 }
 
@@ -433,7 +437,7 @@ __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, 
 //   3. every wave: the gradient of r; rn moves from the stage to the registers and the row
 //      after it starts streaming into the stage.
 template <bool VEC>
-__global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
+__global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(LossArgs a) {
   __shared__ LossShared sh;
   __shared__ __align__(16) float stage[2 * kLossChunk];
   const int p = blockIdx.x / a.C, c = blockIdx.x % a.C;
@@ -447,7 +451,6 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
 #pragma unroll
   for (int e = 0; e < kLossPer; ++e) mask |= (slice_off(tid, e) < len ? 1u : 0u) << e;
   float d[kLossPer], t[kLossPer];
-  double lse_cur = 0.0;   // wave 0: lse of the current row's draft logits
 
   // prologue: row p's normalisers
   stage_row<VEC>(a, p, c, tid, wave, stage_lds, stage);
@@ -469,7 +472,8 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
     const double v = combine_waves1(sh, lane);
     publish(a.part1 + ((size_t)p * a.C + c) * 4, 4, nullptr, 0, v, lane);
     bool ok = true;
-    lse_cur = combine_part1(a, sh, p, lane, ok);
+    const double lse0 = combine_part1(a, sh, p, lane, ok);
+    if (lane == 0) sh.lse = lse0;
     if (lane == 0) sh.stop = ok ? 0 : 1;
   }
   raw_barrier();
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(kLossThreads, 4) void k_draft_loss(LossArgs a) {
       publish(a.part2 + ((size_t)r * a.C + c) * 2, 2,
               a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v, lane);
       bool ok = true;
-      combine_step(a, sh, r, rn, has_next, c, lse_cur, rs, lane, ok);
+      combine_step(a, sh, r, rn, has_next, c, rs, lane, ok);
       if (lane == 0) sh.stop = ok ? 0 : 1;
     }
     raw_barrier();

@@ -112,8 +112,8 @@ def test_draft_loss_validation():
     assert L.dspark_loss_workspace_bytes(2, 4, 0) == 0
     assert f(2, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, P, need - 1, None) == 5
     assert f(2, 4, 100, P, P, P, P, 0.1, 0.9, 1.0, P, None, P, P, None, need, None) == 5
-    # the vocabulary is split into ceil(V / 4096) chunks of partials per row
-    assert L.dspark_loss_workspace_bytes(128, 16, 151936) >= 2048 * 38 * 6 * 8
+    # the vocabulary is split into ceil(V / 8192) chunks of published partials per row
+    assert L.dspark_loss_workspace_bytes(128, 16, 151936) >= 2048 * 19 * 6 * 8
 
 
 def test_closed_loop_validation():
