@@ -606,22 +606,27 @@ bool loss_shape_ok(int B, int G, int V) {
          V <= kLossMaxVocab;
 }
 
-// resident workgroups of the loss kernel on the current device (0 when cooperative launch
-// is unavailable)
+// Resident workgroups of the loss kernel on the current device (0 when cooperative launch
+// is unavailable), looked up once per device.
+constexpr int kMaxDevices = 64;
+
 template <bool VEC>
 int loss_capacity() {
-  static int cap = -1;
-  if (cap < 0) {
-    int dev = 0, coop = 0, ncu = 0, per_cu = 0;
-    cap = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+  static int cap[kMaxDevices];
+  static bool known[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (!known[dev]) {
+    int coop = 0, ncu = 0, per_cu = 0;
+    cap[dev] = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_draft_loss<VEC>,
                                                      kLossThreads, 0) == hipSuccess && coop)
-      cap = per_cu * ncu;
+      cap[dev] = per_cu * ncu;
+    known[dev] = true;
   }
-  return cap;
+  return cap[dev];
 }
 
 }  // namespace
