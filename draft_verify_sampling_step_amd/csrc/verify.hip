@@ -23,6 +23,10 @@
 
 namespace dspark {
 
+// 16-byte loads per thread and item of the target-row pass (an item is 4 * 256 * this many
+// entries of one row)
+constexpr int kVerifyQuads = 8;
+
 // Flattened ragged row list: rows (b, k) with k <= ell_b + 1, in request order.  One
 // workgroup; writes the list, its length and the number of (row, slice) work items, and
 // clears the bonus-race words.
@@ -83,10 +87,10 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
     const bool is_bonus = (k == (Lb < 0 ? 0 : (Lb > G ? G : Lb)) + 1);
     const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
     const float* trow = T + (size_t)row * V;
-    if ((V & 3) == 0 && slice_len == 4 * 256 * 8) {
+    if ((V & 3) == 0 && slice_len == 4 * 256 * kVerifyQuads) {
       // every thread's eight 16-byte loads are issued before any is consumed; entries past
       // the slice read as -inf
-      constexpr int kQ = 8;
+      constexpr int kQ = kVerifyQuads;
       f32x4_t q[kQ];
 #pragma unroll
       for (int i = 0; i < kQ; ++i) {
@@ -380,8 +384,8 @@ int resid_slices(const dspark_dims* d, bool mfma) {
 
 }  // namespace
 
-// Target rows are streamed in slices of 8192 entries (32 KB per workgroup item).
-constexpr int kVerifySlice = 8192;
+// Target rows are streamed in slices of kVerifySlice entries per workgroup item.
+constexpr int kVerifySlice = 4 * 256 * kVerifyQuads;
 
 size_t dspark_verify_workspace(const dspark_dims* d) {
   const int ns = (d->vocab + kVerifySlice - 1) / kVerifySlice;
