@@ -50,6 +50,9 @@ __device__ __forceinline__ int merge_split(const SKey* A, int la, const SKey* Bv
 // mode of k_schedule beyond the two public ones: admit the first k_admit candidates
 constexpr int kSchedTopK = 2;
 
+// SPS entries B..B+kSpsWin staged in LDS for the walk (the walk usually stops early)
+constexpr int kSpsWin = 512;
+
 __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
                                                    const double* __restrict__ sps, int B,
                                                    int G, int mode, int k_admit,
@@ -61,6 +64,8 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
   const int tid = threadIdx.x, n = B * G;
   SKey* X = reinterpret_cast<SKey*>(smem);   // [n], then [n] for the other merge buffer
   SKey* Y = X + n;
+  __shared__ double sps_win[kSpsWin + 1];    // sps[B + i], i <= min(n, kSpsWin)
+  for (int i = tid; i <= min(n, kSpsWin); i += blockDim.x) sps_win[i] = sps[B + i];
   // 1. prefix survival, one thread per request, left to right in fp64.  With every
   // c <= 1 a request's run is already in order (a non-increasing, index increasing); a run
   // that is not (some c > 1) is put in order by insertion.
@@ -87,17 +92,26 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
     }
   }
   __syncthreads();
-  // 2. bottom-up merge of adjacent runs (length G, 2G, ...) into the full order; every
-  // output slot finds its source by a merge-path search
+  // 2. bottom-up merge of adjacent runs (length G, 2G, ...) into the full order.  A thread
+  // makes two consecutive output slots: the merge-path search locates the first, the second
+  // follows by one more comparison (a merged block has even length except the last, which
+  // ends at n, so both slots lie in one block).
   for (int L = G; L < n; L <<= 1) {
-    for (int p = tid; p < n; p += blockDim.x) {
+    for (int p = 2 * tid; p < n; p += 2 * blockDim.x) {
       const int base = p / (2 * L) * (2 * L);
       const int la = min(L, n - base), lb = min(L, max(0, n - base - L));
       const SKey* A = X + base;
       const SKey* Bv = A + la;
       const int d = p - base;
-      const int i = merge_split(A, la, Bv, lb, d), j = d - i;
-      Y[p] = (i < la && (j >= lb || sched_before(A[i], Bv[j]))) ? A[i] : Bv[j];
+      int i = merge_split(A, la, Bv, lb, d), j = d - i;
+      bool take_a = i < la && (j >= lb || sched_before(A[i], Bv[j]));
+      Y[p] = take_a ? A[i] : Bv[j];
+      if (p + 1 < n) {
+        i += take_a ? 1 : 0;
+        j += take_a ? 0 : 1;
+        take_a = i < la && (j >= lb || sched_before(A[i], Bv[j]));
+        Y[p + 1] = take_a ? A[i] : Bv[j];
+      }
     }
     __syncthreads();
     SKey* t = X;
@@ -121,19 +135,28 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
       double before = 0.0, after = 0.0, cur = tau;
       const unsigned long long atb = (unsigned long long)__double_as_longlong(at);
       const uint32_t at_lo = (uint32_t)atb, at_hi = (uint32_t)(atb >> 32);
-      for (int i = 0; i < cnt; ++i) {
-        // candidate i's a, read from lane i into scalar registers
+      // candidate i's a, read from lane i into scalar registers; a full chunk is unrolled,
+      // so the lane numbers are immediates and only the chain of adds is serial
+      auto link = [&](int i) {
         const uint32_t lo = __builtin_amdgcn_readlane(at_lo, i);
         const uint32_t hi = __builtin_amdgcn_readlane(at_hi, i);
         const double ai = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
         before = (lane == i) ? cur : before;
         cur = cur + ai;
         after = (lane == i) ? cur : after;
+      };
+      if (cnt == 64) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) link(i);
+      } else {
+        for (int i = 0; i < cnt; ++i) link(i);
       }
       bool halt = false;
       if (mode == DSPARK_SCHED_GREEDY && t < n) {
-        const double th_next = after * sps[B + t + 1];
-        const double th_best = before * sps[B + t];
+        const double sp1 = t + 1 <= kSpsWin ? sps_win[t + 1] : sps[B + t + 1];
+        const double sp0 = t <= kSpsWin ? sps_win[t] : sps[B + t];
+        const double th_next = after * sp1;
+        const double th_best = before * sp0;
         halt = th_next <= th_best;
       } else if (mode == kSchedTopK && t < n) {
         halt = t == k_admit;                   // the first k_admit are in, no more
