@@ -35,6 +35,9 @@ def _run_loop(inp, D, rounds, sigma, tseed, seed=None):
 
 LOOPS = {
     "tiny": (workload.CONFIGS["tiny"], 6, 0.5),
+    # V % 4 != 0 (the stand-in target's entry-by-entry path), full-block verification
+    "odd_v_full": (workload.custom(name="loopodd", B=5, gamma=3, V=1001, r=16, d=32,
+                                   sched_mode=1), 4, 0.8),
     # bf16 weights with r = 256: the matrix-core draft and residual paths
     "bf16_b40": (workload.custom(name="loopbf16", B=40, gamma=8, V=8192, r=256, d=256,
                                  bf16=True, logits="zipf", sigma0=0.3, sigma1=0.05,

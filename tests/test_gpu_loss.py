@@ -120,6 +120,31 @@ def test_draft_loss_matches_oracle(B, G, V, seed, extra):
     check_loss(tr, g=g)
 
 
+@pytest.mark.parametrize("alphas", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 2.5),
+                                    (0.3, 0.3, 0.3)])
+def test_draft_loss_term_weights(alphas):
+    """Each term alone and other weights: the kernel takes the weights as arguments."""
+    _flush(f"draft loss alphas={alphas}")
+    tr = _case(3, 5, 7000, 9)
+    loss, terms, gz, gc = ds.dspark_draft_loss(dev(tr.zd), dev(tr.zt), dev(tr.labels),
+                                               dev(tr.conf_logit), alphas)
+    o = oracle.draft_loss(tr.zd, tr.zt, tr.labels, tr.conf_logit, alphas)
+    assert abs(float(host(loss)[0]) - o["loss"]) <= 2e-5 * abs(o["loss"]) + 1e-12
+    w = _row_weights(3, 5)
+    gz_o = o["grad_zd"]
+    pd = special.softmax(tr.zd.astype(np.float64), axis=2)
+    pt = special.softmax(tr.zt.astype(np.float64), axis=2)
+    near = np.abs(pd - pt) <= 1e-5 * np.maximum(pd, pt)
+    tol = 1e-4 * np.abs(gz_o) + 1e-5 * pd * w[..., None] * (alphas[0] + alphas[1]) + 1e-30
+    step = alphas[1] * pd * w[..., None]
+    ok = np.abs(host(gz) - gz_o) <= tol
+    for m in (-2, -1, 1, 2):
+        ok |= near & (np.abs(host(gz) - (gz_o + m * step)) <= tol)
+    assert ok.all()
+    gc_o = o["grad_conf"]
+    assert np.all(np.abs(host(gc) - gc_o) <= 1e-4 * np.abs(gc_o) + 1e-6 * w)
+
+
 def test_draft_loss_forward_only_and_deterministic():
     tr = _case(8, 16, 20000, 8)
     args = (dev(tr.zd), dev(tr.zt), dev(tr.labels), dev(tr.conf_logit), ALPHAS)
