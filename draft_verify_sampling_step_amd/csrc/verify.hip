@@ -201,25 +201,10 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
   }
 }
 
-// lse (natural log) of one target row from its base-2 slice partials; wave-cooperative.
-__device__ __forceinline__ float wave_row_lse(const float2* p, int n, int lane) {
-  float m = -3.0e38f, l = 0.f;
-  for (int s = lane; s < n; s += kWave) {
-    const float mn = fmaxf(m, p[s].x);
-    l = l * __builtin_amdgcn_exp2f(m - mn) + p[s].y * __builtin_amdgcn_exp2f(p[s].x - mn);
-    m = mn;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
-    const float mn = fmaxf(m, om);
-    l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
-    m = mn;
-  }
-  return (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
-}
-
-// one wave per request
+// One wave per request, one lane per draft row k = lane + 1 (gamma <= 64): all rows of a
+// request are decided at once.  Lane k merges the base-2 slice partials of target row k in
+// slice order into its lse, then takes p_t(x_k) and the accept test u * p_d(x_k) < p_t(x_k).
+// The accepted prefix ends at the first rejected row, found by a ballot.
 __global__ __launch_bounds__(256) void k_verify_decide(
     const float* __restrict__ T, const int32_t* __restrict__ tokens,
     const float* __restrict__ logp, const int32_t* __restrict__ ell,
@@ -231,36 +216,41 @@ __global__ __launch_bounds__(256) void k_verify_decide(
   if (b >= B) return;
   const int Lb = ell[b];
   const int L = Lb < 0 ? 0 : (Lb > G ? G : Lb);   // ell outside [0, gamma] is clamped
-  int n = 0, j = 0;
-  float lj = 0.f;
-  for (int k = 1; k <= G; ++k) {
-    if (k > L) {
-      if (pt_tok && lane == 0) pt_tok[(size_t)b * G + (k - 1)] = __builtin_nanf("");
-      continue;
-    }
-    const float lt = wave_row_lse(part + ((size_t)b * (G + 1) + (k - 1)) * nslices, nslices, lane);
+  const int k = lane + 1;
+  const bool live = k <= L;
+  float lt = 0.f, pt = __builtin_nanf("");
+  bool rejected = false;
+  if (live) {
+    const size_t row = (size_t)b * (G + 1) + (k - 1);
     const int x = clamp_tok(tokens[(size_t)b * G + (k - 1)], V);
-    const float pt = fast_exp(T[((size_t)b * (G + 1) + (k - 1)) * V + x] * invT - lt);
-    if (pt_tok && lane == 0) pt_tok[(size_t)b * G + (k - 1)] = pt;
-    if (j == 0) {
-      const U4 w = philox10(0u, (uint32_t)k, (uint32_t)b, 1u, key0, key1);
-      const float u = word_to_uniform(w.x);
-      const float pd = fast_exp(logp[(size_t)b * G + (k - 1)]);
-      if (u * pd < pt) {
-        ++n;
-      } else {
-        j = k;
-        lj = lt;
-      }
+    const float tx = T[row * V + x];
+    const float lp = logp[(size_t)b * G + (k - 1)];
+    const float2* p = part + row * nslices;
+    float m = -3.0e38f, l = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < nslices; ++s) {
+      const float2 q = p[s];
+      const float mn = fmaxf(m, q.x);
+      l = l * __builtin_amdgcn_exp2f(m - mn) + q.y * __builtin_amdgcn_exp2f(q.x - mn);
+      m = mn;
     }
+    lt = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+    pt = fast_exp(tx * invT - lt);
+    const U4 w = philox10(0u, (uint32_t)k, (uint32_t)b, 1u, key0, key1);
+    rejected = !(word_to_uniform(w.x) * fast_exp(lp) < pt);
   }
+  if (pt_tok && k <= G) pt_tok[(size_t)b * G + (k - 1)] = pt;
+  const unsigned long long rej = __ballot(rejected);   // bit k-1: row k rejected
+  const int n = rej ? __builtin_ctzll(rej) : L;          // leading accepts
+  const int j = rej ? n + 1 : 0;                         // residual row, 0 = none
+  const float lj = __shfl(lt, j > 0 ? j - 1 : 0, kWave);
   int32_t* out = out_tokens + (size_t)b * (G + 1);
   for (int i = lane; i <= G; i += kWave) out[i] = i < n ? tokens[(size_t)b * G + i] : -1;
   if (lane == 0) {
     if (j == 0) out[n] = (int32_t)packed_index(bonus[b]);
     n_accept[b] = n;
     jrow[b] = j;
-    lse_t_row[b] = lj;
+    lse_t_row[b] = j > 0 ? lj : 0.f;
   }
 }
 
