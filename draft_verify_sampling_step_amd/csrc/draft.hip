@@ -4,8 +4,8 @@
 //
 // One launch per position; the launch boundary carries the device-wide dependency
 // x_{k-1} -> bias of position k (on MI355X an in-kernel grid barrier, with the next
-// position's independent loads prefetched across it, measured no faster).  Each workgroup covers a vocabulary slice for every
-// request and reports
+// position's independent loads prefetched across it, measured no faster).  Each workgroup
+// covers a vocabulary slice for every request and reports
 //   - its best Gumbel candidate as a packed (score, index) word through a 64-bit atomic
 //     max per request (order-free, so the winner is deterministic), and
 //   - its base-2 softmax state (max, sum) to a fixed slot.

@@ -54,6 +54,8 @@ struct MfmaBiasArgs {
   uint32_t key0, key1;
   int ncols;                             // columns of this launch (<= 256)
   int col0;                              // first global column of this launch
+  int thin_max;                          // resid: > 0 = leave at once when the launch
+                                         // has 1..thin_max residual rows (thin pass)
 };
 
 // The MFMA path handles bf16 weights with r = 256 (16 k-steps of 16).

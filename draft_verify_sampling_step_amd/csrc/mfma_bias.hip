@@ -131,6 +131,9 @@ k_mfma_bias(const MfmaBiasArgs a) {
     if (tid == NT - 1) clist[NC] = off + __popcll(bal);
     __syncthreads();
     n_live = clist[NC];
+    // none at all, or few enough for the thin pass: nothing to do here (uniform exit, no
+    // load issued yet)
+    if (n_live == 0 || n_live <= a.thin_max) return;
   }
   // ---- column metadata: request, position, conditioning token, logit row offsets, lse
   for (int c = tid; c < NC; c += NT) {

@@ -305,6 +305,164 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
         make_float4(b1.s, __uint_as_float(b1.i), b2.s, __uint_as_float(b2.i));
 }
 
+// Thin residual pass, for at most kThinMax requests with a residual row (the usual case:
+// few rejections per round) and bf16 weights of rank kR.  Grid: the nslices slices of the
+// residual partials; 256 threads.  Every workgroup first lists the requests with a residual
+// row in request order and leaves at once unless there are 1..kThinMax of them (the matrix-
+// core pass takes more, and leaves at once in this case).  Each wave then takes four
+// vocabulary rows per step, 16 lanes per row: lane part p holds elements 16 p .. 16 p + 15
+// of W2t[v] and of every listed request's W1[x_{j-1}], the dot products are summed over the
+// 16 lanes, and lane p < n runs the residual and fallback races of request p on row v with
+// the same arithmetic as the row kernel above.
+constexpr int kThinMax = 2;
+
+// Sum over each 16-lane row of the wave by DPP moves (quad swaps 1,0,3,2 and 2,3,0,1, then
+// the half-row and row mirrors): each step adds a commutative pair, so all 16 lanes end
+// with the same total.
+__device__ __forceinline__ float dpp_row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+__global__ __launch_bounds__(256) void k_verify_resid_thin(
+    const float* __restrict__ U, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W2t, const float* __restrict__ T,
+    const int32_t* __restrict__ anchor, const int32_t* __restrict__ tokens,
+    const float* __restrict__ lse_d, const int32_t* __restrict__ jrow,
+    const float* __restrict__ lse_t_row, int B, int G, int V, float invT, uint32_t key0,
+    uint32_t key1, int nslices, float4* __restrict__ res_part) {
+  __shared__ int s_list[kThinMax];
+  __shared__ int s_cnt;
+  __shared__ float4 s_cand[16][kThinMax];   // [wave * 4 + row quad][request]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (wave == 0) {
+    int cnt = 0;
+    for (int c0 = 0; c0 < B; c0 += kWave) {
+      const int bb = c0 + lane;
+      const bool act = bb < B && jrow[bb] > 0;
+      const unsigned long long bal = __ballot(act);
+      const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (act && at < kThinMax) s_list[at] = bb;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) s_cnt = cnt;
+  }
+  __syncthreads();
+  const int n = s_cnt;
+  if (n == 0 || n > kThinMax) return;
+
+  const int part = lane & 15, quad = lane >> 4;
+  float w1[kThinMax][16];
+  const float* urow = U;
+  const float* trow = T;
+  float ld = 0.f, lt = 0.f;
+  int myb = 0, myj = 1;
+#pragma unroll
+  for (int i = 0; i < kThinMax; ++i) {
+    int b = 0, j = 1;
+    if (i < n) { b = s_list[i]; j = jrow[b]; }
+    const int prev = clamp_tok((j == 1) ? anchor[b] : tokens[(size_t)b * G + (j - 2)], V);
+    const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(W1 + (size_t)prev * kR + 16 * part);
+    const u32x4_t q0 = wp[0], q1 = wp[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w1[i][2 * e] = __uint_as_float(q0[e] << 16);
+      w1[i][2 * e + 1] = __uint_as_float(q0[e] & 0xFFFF0000u);
+      w1[i][8 + 2 * e] = __uint_as_float(q1[e] << 16);
+      w1[i][8 + 2 * e + 1] = __uint_as_float(q1[e] & 0xFFFF0000u);
+    }
+    if (i == part && i < n) {
+      myb = b;
+      myj = j;
+      urow = U + ((size_t)b * G + (j - 1)) * V;
+      trow = T + ((size_t)b * (G + 1) + (j - 1)) * V;
+      ld = lse_d[(size_t)b * G + (j - 1)];
+      lt = lse_t_row[b];
+    }
+  }
+  const int len = (V + nslices - 1) / nslices;
+  const int vb = blockIdx.x * len, ve = min(V, vb + len);
+  Cand c1{-INFINITY, 0xFFFFFFFFu, 0.f}, c2{-INFINITY, 0xFFFFFFFFu, 0.f};
+  // four row groups per iteration (rows v0 + 16 u + quad), every load issued first; rows
+  // past the slice load row v0 and are not raced
+  for (int v0 = vb + 4 * wave; v0 < ve; v0 += 64) {
+    u32x4_t xq[4][2];
+    float uq[4], tq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vu = v0 + 16 * u + quad;
+      const int vv = vu < ve ? vu : v0;
+      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(W2t + (size_t)vv * kR + 16 * part);
+      xq[u][0] = xp[0];
+      xq[u][1] = xp[1];
+      uq[u] = urow[vv];
+      tq[u] = trow[vv];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 16 * u + quad;
+      float xf[16];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xf[2 * e] = __uint_as_float(xq[u][0][e] << 16);
+        xf[2 * e + 1] = __uint_as_float(xq[u][0][e] & 0xFFFF0000u);
+        xf[8 + 2 * e] = __uint_as_float(xq[u][1][e] << 16);
+        xf[8 + 2 * e + 1] = __uint_as_float(xq[u][1][e] & 0xFFFF0000u);
+      }
+      float d[kThinMax];
+#pragma unroll
+      for (int i = 0; i < kThinMax; ++i) {
+        d[i] = 0.f;
+        if (i < n) {   // uniform
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc = fmaf(xf[e], w1[i][e], acc);
+          d[i] = dpp_row_sum16(acc);
+        }
+      }
+      if (v < ve && part < n) {
+        float bias = d[0];
+#pragma unroll
+        for (int i = 1; i < kThinMax; ++i) bias = part == i ? d[i] : bias;
+        const float zd = (uq[u] + bias) * invT;
+        const float zt = tq[u] * invT;
+        const float rho = fast_exp(zt - lt) - fast_exp(zd - ld);
+        const U4 w = philox10((uint32_t)v >> 2, (uint32_t)myj, (uint32_t)myb, 2u, key0, key1);
+        const uint32_t word =
+            (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
+        const float gn = gumbel_from_uniform(word_to_uniform(word));
+        if (rho > 0.f) {
+          const float sc = fast_log(rho) + gn;
+          if (sc > c1.s) c1 = Cand{sc, (uint32_t)v, 0.f};
+        }
+        const float sc2 = zt + gn;
+        if (sc2 > c2.s) c2 = Cand{sc2, (uint32_t)v, 0.f};
+      }
+    }
+  }
+  // merge the candidates of request p over the 16 (wave, row quad) lanes, ties to the lower
+  // index
+  if (part < n)
+    s_cand[wave * 4 + quad][part] =
+        make_float4(c1.s, __uint_as_float(c1.i), c2.s, __uint_as_float(c2.i));
+  __syncthreads();
+  if (tid < n) {
+    float s1 = -INFINITY, s2 = -INFINITY;
+    uint32_t i1 = 0xFFFFFFFFu, i2 = 0xFFFFFFFFu;
+    for (int g = 0; g < 16; ++g) {
+      const float4 p = s_cand[g][tid];
+      const uint32_t pi1 = __float_as_uint(p.y), pi2 = __float_as_uint(p.w);
+      if (p.x > s1 || (p.x == s1 && pi1 < i1)) { s1 = p.x; i1 = pi1; }
+      if (p.z > s2 || (p.z == s2 && pi2 < i2)) { s2 = p.z; i2 = pi2; }
+    }
+    res_part[(size_t)blockIdx.x * B + s_list[tid]] =
+        make_float4(s1, __uint_as_float(i1), s2, __uint_as_float(i2));
+  }
+}
+
 // One wave per request with a residual row: reduce the residual (and fallback p_t) races
 // over the slice partials in a fixed order; write the token after the accepted prefix.
 __global__ __launch_bounds__(256) void k_verify_final(const int32_t* __restrict__ jrow,
@@ -423,6 +581,14 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
     a.jrow = w.jrow; a.rpart = w.res_part;
     a.B = B; a.G = G; a.V = V; a.r = r; a.k = 0; a.invT = invT; a.key0 = key0; a.key1 = key1;
     a.ncols = B; a.col0 = 0;
+    // up to kThinMax residual rows take the thin pass; the matrix-core pass leaves at once
+    // then (and the thin one when there are more)
+    const bool thin = B <= 256;
+    a.thin_max = thin ? kThinMax : 0;
+    if (thin)
+      hipLaunchKernelGGL(k_verify_resid_thin, dim3(nres), dim3(256), 0, st, U,
+                         (const uint16_t*)W1, (const uint16_t*)W2t, T, anchor, tokens, lse,
+                         w.jrow, w.lse_t_row, B, G, V, invT, key0, key1, nres, w.res_part);
     if (launch_mfma_bias(a, nres, st) != DSPARK_OK) return DSPARK_E_HIP;
   } else {
     const RowSlices rr = row_slices(V, B);

@@ -135,6 +135,40 @@ def test_round_parity_second_seed():
     run_round_parity(SMALL["mfma_b40_ragged"], seed=11, extra_ells=False)
 
 
+@pytest.mark.parametrize("nrej", [0, 1, 4, 5, 40])
+def test_residual_pass_by_rejection_count(nrej):
+    """Verification with exactly `nrej` requests rejected at their first draft row: 1..4
+    take the thin residual pass, more the matrix-core pass, and with none neither pass has
+    work.  The target rows 1..gamma are the draft logits themselves (every test accepts),
+    except that the chosen requests get +40 on one token other than x_1 in row 1, so x_1 is
+    rejected there and the residual mass sits on that token."""
+    _flush(f"residual pass with {nrej} rejected requests")
+    cfg = workload.custom(name=f"rej{nrej}", B=96, gamma=3, V=4096, r=256, d=64, bf16=True,
+                          wsigma=0.1, logits="zipf", table="serve")
+    inp = workload.generate(cfg, 5)
+    D = DeviceInputs(inp)
+    od = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed)
+    tok = od["tokens"]
+    T = workload.synthesize_target(inp, tok).astype(np.float32)
+    W1f, W2f = oracle.widen(inp.W1), oracle.widen(inp.W2t)
+    prev = np.concatenate([inp.anchor[:, None], tok[:, :-1]], axis=1)
+    for k in range(cfg.gamma):
+        T[:, k, :] = (inp.U[:, k, :].astype(np.float64) + W1f[prev[:, k]] @ W2f.T)
+    rej = np.random.default_rng(nrej).permutation(cfg.B)[:nrej]
+    for b in rej:
+        T[b, 0, (tok[b, 0] + 1) % cfg.V] += 40.0
+    ell = np.full(cfg.B, cfg.gamma, np.int32)
+    forced = dev(tok)
+    _, lg, sg = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, 1.0, inp.seed,
+                                       forced=forced)
+    n_g, out_g, pt_g = ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, forced, lg, sg, dev(T),
+                                        dev(ell), 1.0, inp.seed)
+    ref = check_verify(inp, tok, T, ell, host(n_g), host(out_g), host(pt_g))
+    assert sorted(np.nonzero(ref["n_accept"] < ell)[0].tolist()) == sorted(rej.tolist())
+    assert np.array_equal(host(n_g), ref["n_accept"])
+    torch.cuda.synchronize()
+
+
 def test_deterministic():
     cfg = SMALL["mfma_b64_v_odd"]
     inp = workload.generate(cfg, 1)
