@@ -12,7 +12,8 @@ from the round's drafted tokens -- every step re-drafts the identical tokens (sa
 Prints one JSON line.  `value` = drafted+verified positions per second = B * gamma / step.
 `roofline` covers the dominant kernel, one draft position: its algorithmic bytes (W2t once
 and the B base-logit rows of the position) over its mean launch duration, measured with
-HIP events around each launch on the launch stream in a timed pass of its own.
+HIP events around each launch on the launch stream in a timed pass of its own; beside it,
+`read_probe` is a plain streaming read of the same bytes per launch, the achievable rate.
 `cpu_baseline` times the fp64 oracle on a bounded sample of requests on the host.
 """
 from __future__ import annotations
@@ -168,6 +169,16 @@ def main():
     log(f"draft sampling kernel: {kern_ms * 1e3:.2f} us mean over {kern_n} launches of "
         f"{kern_pos:g} positions each")
 
+    # the achievable read rate at the same bytes per launch: a plain streaming-read kernel
+    # over four rotating regions (so that consecutive launches miss the caches)
+    probe_bytes = (V * r * 2 + B * V * 4) // 16 * 16
+    probe_buf = torch.empty(4 * probe_bytes, dtype=torch.uint8, device=dev)
+    probe_ms = ds.dspark_stream_read_probe(probe_buf, probe_bytes, reps=40)
+    del probe_buf
+    probe_gbs = probe_bytes / (probe_ms * 1e-3) / 1e9
+    log(f"plain streaming read of {probe_bytes} bytes: {probe_ms * 1e3:.2f} us "
+        f"({probe_gbs:.0f} GB/s)")
+
     # verification alone (rows pass, decisions, residual pass, final), same inputs as a step
     vf0 = torch.cuda.Event(enable_timing=True)
     vf1 = torch.cuda.Event(enable_timing=True)
@@ -319,6 +330,14 @@ def main():
             "positions_per_launch": kern_pos,
             "ms_per_launch": round(kern_ms, 5),
             "launches": kern_n,
+            "read_probe": {
+                "kind": "plain 16-byte streaming read of the same bytes per launch, four "
+                        "rotating regions",
+                "achieved": round(probe_gbs, 1),
+                "ms_per_launch": round(probe_ms, 5),
+                "bytes_per_launch": probe_bytes,
+            },
+            "frac_of_read_probe": round(achieved / probe_gbs, 4),
         },
         "draft_call_ms": round(draft_ms, 4),
         "verify_call_ms": round(verify_ms, 4),

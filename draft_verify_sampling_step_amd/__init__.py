@@ -100,11 +100,14 @@ def lib() -> ctypes.CDLL:
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(_I),
                                               ctypes.POINTER(ctypes.c_double)]
+            L.dspark_stream_read_probe.argtypes = [_P, _SZ, _SZ, _I, _P,
+                                                   ctypes.POINTER(ctypes.c_double), _P]
             for fn in ("dspark_draft_markov", "dspark_confidence",
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
                        "dspark_draft_loss", "dspark_closed_loop", "dspark_rng_uniforms",
-                       "dspark_profile_start", "dspark_profile_stop"):
+                       "dspark_profile_start", "dspark_profile_stop",
+                       "dspark_stream_read_probe"):
                 getattr(L, fn).restype = _I
             _lib = L
     return _lib
@@ -440,6 +443,17 @@ def dspark_profile_stop():
     pos = ctypes.c_double()
     _check(lib().dspark_profile_stop(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(pos)))
     return ms.value, n.value, pos.value
+
+
+def dspark_stream_read_probe(buf, launch_bytes: int, reps: int = 20, stream=None) -> float:
+    """Mean milliseconds of one plain streaming read of `launch_bytes` bytes (measurement
+    support): launches rotate over the launch_bytes-sized regions of the device tensor `buf`."""
+    nbytes = buf.numel() * buf.element_size()
+    sink = torch.zeros(1, dtype=torch.float32, device=buf.device)
+    ms = ctypes.c_double()
+    _check(lib().dspark_stream_read_probe(_ptr(buf), nbytes, int(launch_bytes), int(reps),
+                                          _ptr(sink), ctypes.byref(ms), _stream_handle(stream)))
+    return ms.value
 
 
 # ------------------------------------------------------------------------------------

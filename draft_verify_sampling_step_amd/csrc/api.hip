@@ -122,3 +122,64 @@ extern "C" dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t
                      (uint32_t)seed, (uint32_t)(seed >> 32), b, k, s, v0, n, out);
   return launch_status();
 }
+
+namespace dspark {
+
+// Plain streaming read: grid-stride 16-byte non-temporal loads, four in flight per thread.
+// The sum is stored only when it equals 1e30 exactly (the sink is valid memory either way),
+// a data-dependent condition, so the loads cannot be removed.
+typedef float sr_f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_stream_read(const sr_f32x4* __restrict__ p,
+                                                     size_t n16, float* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float s = 0.f;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const sr_f32x4 a = __builtin_nontemporal_load(p + i);
+    const sr_f32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const sr_f32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const sr_f32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+    s += (a[0] + b[1]) + (c[2] + d[3]);
+  }
+  for (; i < n16; i += stride) s += __builtin_nontemporal_load(p + i)[0];
+  if (s == 1.0e30f) sink[0] = s;
+}
+
+}  // namespace dspark
+
+extern "C" dspark_status dspark_stream_read_probe(const void* buf, size_t buf_bytes,
+                                                  size_t launch_bytes, int reps, float* sink,
+                                                  double* mean_ms, void* stream) {
+  if (!buf || !sink || !mean_ms) return DSPARK_E_NULL;
+  if (launch_bytes < 16 || launch_bytes % 16 != 0 || launch_bytes > buf_bytes ||
+      ((uintptr_t)buf & 15u) != 0)
+    return DSPARK_E_SHAPE;
+  if (reps < 1 || reps > 10000) return DSPARK_E_VALUE;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t nreg = buf_bytes / launch_bytes;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return DSPARK_E_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return DSPARK_E_HIP;
+  }
+  auto launch = [&](int i) {
+    const char* base = static_cast<const char*>(buf) + (size_t)(i % nreg) * launch_bytes;
+    hipLaunchKernelGGL(k_stream_read, dim3(1024), dim3(256), 0, st,
+                       reinterpret_cast<const sr_f32x4*>(base), launch_bytes / 16, sink);
+  };
+  dspark_status rc = DSPARK_OK;
+  for (int i = 0; i < 2; ++i) launch(i + 1);   // warm-up
+  if (hipEventRecord(e0, st) != hipSuccess) rc = DSPARK_E_HIP;
+  for (int i = 0; i < reps && rc == DSPARK_OK; ++i) launch(i);
+  float ms = 0.f;
+  if (rc == DSPARK_OK &&
+      (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+       hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+    rc = DSPARK_E_HIP;
+  if (rc == DSPARK_OK) rc = launch_status();
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc == DSPARK_OK) *mean_ms = (double)ms / reps;
+  return rc;
+}

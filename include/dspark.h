@@ -353,6 +353,20 @@ dspark_status dspark_profile_start(int max_launches);
 dspark_status dspark_profile_stop(double* mean_ms, int* launches,
                                   double* positions_per_launch);
 
+/*
+ * Achievable HBM read rate (measurement support, not part of the method).  Times `reps`
+ * launches of a plain streaming-read kernel (16-byte loads, every byte read once, nothing
+ * written) on `stream`; launch i reads the i-th of the buf_bytes / launch_bytes regions of
+ * `buf` in turn, so that consecutive launches do not hit data left in the caches.  Writes
+ * the mean duration of one launch in milliseconds to *mean_ms; waits for its own events.
+ * buf: device memory, 16-byte aligned, owned by the caller; launch_bytes: a multiple of 16,
+ * 16 <= launch_bytes <= buf_bytes; reps: 1..10000; sink: one device float the kernel may
+ * write.  Errors: DSPARK_E_NULL, DSPARK_E_SHAPE (sizes or alignment), DSPARK_E_VALUE
+ * (reps), DSPARK_E_HIP (launch or events).
+ */
+dspark_status dspark_stream_read_probe(const void* buf, size_t buf_bytes, size_t launch_bytes,
+                                       int reps, float* sink, double* mean_ms, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -181,3 +181,20 @@ def test_profile_switch_validation():
     assert L.dspark_profile_start(0) == 4            # DSPARK_E_VALUE, no HIP call made
     assert L.dspark_profile_start(1 << 17) == 4
     assert L.dspark_profile_stop(None, None, None) == 1    # DSPARK_E_NULL
+
+
+def test_stream_read_probe_validation():
+    import ctypes
+    L = ds.lib()
+    ms = ctypes.c_double()
+    buf = ctypes.c_void_p(4096)      # never dereferenced: validation fails first
+    sink = ctypes.c_void_p(8192)
+    assert L.dspark_stream_read_probe(None, 64, 16, 1, sink, ctypes.byref(ms), None) == 1
+    assert L.dspark_stream_read_probe(buf, 64, 16, 1, None, ctypes.byref(ms), None) == 1
+    assert L.dspark_stream_read_probe(buf, 64, 16, 1, sink, None, None) == 1
+    assert L.dspark_stream_read_probe(buf, 64, 24, 1, sink, ctypes.byref(ms), None) == 2
+    assert L.dspark_stream_read_probe(buf, 64, 128, 1, sink, ctypes.byref(ms), None) == 2
+    assert L.dspark_stream_read_probe(ctypes.c_void_p(4100), 64, 16, 1, sink,
+                                      ctypes.byref(ms), None) == 2
+    assert L.dspark_stream_read_probe(buf, 64, 16, 0, sink, ctypes.byref(ms), None) == 4
+    assert L.dspark_stream_read_probe(buf, 64, 16, 10001, sink, ctypes.byref(ms), None) == 4
