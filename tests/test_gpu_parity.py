@@ -323,6 +323,14 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
 
 
+def test_stream_read_probe_times_a_read():
+    """The measurement aid reads its regions and reports a physically possible duration."""
+    buf = torch.empty(4 * (16 << 20), dtype=torch.uint8, device="cuda")
+    ms = ds.dspark_stream_read_probe(buf, 16 << 20, reps=5)
+    gbs = (16 << 20) / (ms * 1e-3) / 1e9
+    assert 0.0 < ms and 10.0 < gbs < 20000.0, (ms, gbs)
+
+
 def test_zz_near_tie_rate():
     """Excused near-tie mismatches stay within 0.01% of all compared samples (or at most
     one when fewer than 10^4 samples were compared)."""
