@@ -9,7 +9,9 @@ from the round's drafted tokens -- every step re-drafts the identical tokens (sa
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serve128]
 
-Prints one JSON line.  `value` = drafted+verified positions per second = B * gamma / step.
+Prints one JSON line.  `value` = drafted+verified positions per second = B * gamma / step,
+the step timed as one HIP-graph replay of the eager step (its outputs checked against the
+eager step's in the same run; `ms_per_step_eager` is the eager time).
 `roofline` covers the dominant kernel, one draft position: its algorithmic bytes (W2t once
 and the B base-logit rows of the position) over its mean launch duration, measured with
 HIP events around each launch on the launch stream in a timed pass of its own; beside it,
@@ -158,6 +160,57 @@ def main():
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}), "
         f"draft {draft_ms:.3f} ms")
 
+    # the same step captured once in a HIP graph (every call launches on the current stream
+    # and none uses a memset), replayed; each replay is checked against the eager outputs,
+    # with eager work between replays, before its time is used
+    outs = (tokens, logp, lse, conf, ell, theta, ntot, nacc, outtok) + ((alpha,) if cfg.tv else ())
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    graph_ok, graph_note = False, ""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph_ok = True
+        for _ in range(4):
+            for t in outs:
+                t.fill_(-7)
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ok = graph_ok and all(torch.equal(a, b) for a, b in zip(ref, outs))
+            step()
+            torch.cuda.synchronize()
+        if not graph_ok:
+            graph_note = "a replay differed from the eager step"
+    except RuntimeError as exc:          # capture refused: report the eager time only
+        graph_note = f"capture failed: {exc}"
+        graph_ok = False
+    ms_step_eager = ms_step
+    if graph_ok:
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {ms_step:.3f} ms/step (eager {ms_step_eager:.3f})")
+        del graph
+    else:
+        log(f"graph replay not used: {graph_note}")
+
     # the dominant kernel, one draft position (fused bias MFMA + softmax + Gumbel race):
     # HIP events around each of its launches on the launch stream, in a pass of its own so
     # that the events do not perturb the step timing above
@@ -304,6 +357,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_step_eager, 4),
+        "launch": "HIP graph replay of the step (checked against the eager step)" if graph_ok
+                  else f"eager ({graph_note})",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -169,6 +169,67 @@ def test_residual_pass_by_rejection_count(nrej):
     torch.cuda.synchronize()
 
 
+def test_graph_replay_matches_eager():
+    """A round (draft, confidence, schedule, verify) captured in a HIP graph: every replay,
+    with eager work and synchronisation between replays, equals the eager round bit for bit."""
+    _flush("graph replay of a round")
+    cfg = SMALL["mfma_b128"]
+    inp = workload.generate(cfg, 3)
+    D = DeviceInputs(inp)
+    B, G = cfg.B, cfg.gamma
+    dev_ = torch.device("cuda")
+    tok = torch.empty((B, G), dtype=torch.int32, device=dev_)
+    lp = torch.empty((B, G), dtype=torch.float32, device=dev_)
+    ls = torch.empty((B, G), dtype=torch.float32, device=dev_)
+    cf = torch.empty((B, G), dtype=torch.float32, device=dev_)
+    ell = torch.empty(B, dtype=torch.int32, device=dev_)
+    th = torch.empty(1, dtype=torch.float64, device=dev_)
+    nt = torch.empty(1, dtype=torch.int32, device=dev_)
+    na = torch.empty(B, dtype=torch.int32, device=dev_)
+    ot = torch.empty((B, G + 1), dtype=torch.int32, device=dev_)
+    ws_d = torch.empty(ds.workspace_bytes(ds.OP_DRAFT, B, G, cfg.V, cfg.r), dtype=torch.uint8,
+                       device=dev_)
+    ws_v = torch.empty(ds.workspace_bytes(ds.OP_VERIFY, B, G, cfg.V, cfg.r),
+                       dtype=torch.uint8, device=dev_)
+    temp = cfg.temperature
+    ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, temp, inp.seed, out=(tok, lp, ls),
+                           ws=ws_d)
+    torch.cuda.synchronize()
+    Td = dev(workload.synthesize_target(inp, host(tok)))
+
+    def step():
+        ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, temp, inp.seed, out=(tok, lp, ls),
+                               ws=ws_d)
+        ds.dspark_confidence(D.h, D.W1, D.w, D.anchor, tok, out=cf)
+        ds.dspark_schedule(cf, D.sps, cfg.sched_mode, out=(ell, th, nt))
+        ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, tok, lp, ls, Td, ell, temp, inp.seed,
+                         out=(na, ot, None), ws=ws_v)
+
+    outs = (tok, lp, ls, cf, ell, th, nt, na, ot)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for t in outs:
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a, b), f"replay {i} differs from the eager round"
+        step()
+        torch.cuda.synchronize()
+    del g
+
+
 def test_deterministic():
     cfg = SMALL["mfma_b64_v_odd"]
     inp = workload.generate(cfg, 1)
