@@ -135,7 +135,7 @@ def test_round_parity_second_seed():
     run_round_parity(SMALL["mfma_b40_ragged"], seed=11, extra_ells=False)
 
 
-@pytest.mark.parametrize("nrej", [0, 1, 2, 3, 40])
+@pytest.mark.parametrize("nrej", [0, 1, 2, 3, 5, 40])
 def test_residual_pass_by_rejection_count(nrej):
     """Verification with exactly `nrej` requests rejected at their first draft row: 1 or 2
     take the thin residual pass, more the matrix-core pass, and with none neither pass has
