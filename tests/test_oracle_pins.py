@@ -525,6 +525,197 @@ def test_verify_losslessness_check_has_power():
     assert _chi2_p(hist, law) < 1e-12
 
 
+# ---- exact enumeration of the verification law ([XTL] §1 and §6: lossless rejection
+# sampling).  Every draft block is enumerated with the oracle's own draft distributions,
+# and every branch of the step with its exact probability: x_k accepted with
+# min(1, p_t/p_d), a rejection resampled from max(0, p_t - p_d) normalised, and the bonus
+# from p_t.  Each emitted prefix is completed with the target chain.  The law of the
+# completed strings must be the target chain's law.
+def _enum_tables(seed, V, G, r):
+    """Draft rows p_d,k(. | prev) from the oracle (one request per prev, the prefix forced
+    to prev) and Markov target rows p_t,k(. | prev), k = 1..G+1."""
+    rng = np.random.default_rng(seed)
+    U1 = rng.normal(size=(G, V)) * 1.2
+    W1 = rng.normal(size=(V, r)) * 0.8
+    W2t = rng.normal(size=(V, r)) * 0.8
+    U = np.broadcast_to(U1, (V, G, V)).copy()
+    prevs = np.arange(V, dtype=np.int32)
+    d = oracle.draft(U, W1, W2t, prevs, 1.0, 1, forced=np.repeat(prevs[:, None], G, axis=1),
+                     want_probs=True)
+    pd = np.transpose(d["probs"], (1, 0, 2))                   # [G][prev][V]
+    logpt = _markov_tables(rng, G, V, 0.7)                     # [G+1][prev][V]
+    return U1, W1, W2t, pd, logpt
+
+
+def _completions(pt, G, V):
+    """C[m][prev]: law of the tokens at positions m..G given the token before them."""
+    C = [None] * (G + 2)
+    C[G + 1] = np.ones((V, 1))
+    for m in range(G, -1, -1):
+        C[m] = np.stack([np.concatenate([pt[m][pv][y] * C[m + 1][y] for y in range(V)])
+                         for pv in range(V)])
+    return C
+
+
+def _emitted_law(pd, pt, C, a0, x, ell, G, V):
+    """Law over the (G+1)-strings of one verification of the block x with budget ell."""
+    law = np.zeros(V ** (G + 1))
+    prevs = (a0,) + tuple(x)
+
+    def add(prefix, w):
+        code = 0
+        for y in prefix:
+            code = code * V + y
+        n = V ** (G + 1 - len(prefix))
+        law[code * n:(code + 1) * n] += w * C[len(prefix)][prefix[-1]]
+
+    acc = 1.0
+    for k in range(ell):
+        q_t, q_d = pt[k][prevs[k]], pd[k][prevs[k]]
+        a = min(1.0, q_t[x[k]] / q_d[x[k]])
+        rho = np.maximum(0.0, q_t - q_d)
+        if a < 1.0:
+            for y in np.nonzero(rho > 0)[0]:
+                add(tuple(x[:k]) + (int(y),), acc * (1.0 - a) * rho[y] / rho.sum())
+        acc *= a
+    for y in range(V):
+        add(tuple(x[:ell]) + (y,), acc * pt[ell][prevs[ell]][y])
+    return law
+
+
+def _block_prob(pd, a0, x):
+    p, prev = 1.0, a0
+    for k, y in enumerate(x):
+        p *= pd[k][prev][y]
+        prev = y
+    return p
+
+
+def _enumerate(pd, pt, a0, G, V, ell_of):
+    C = _completions(pt, G, V)
+    law = np.zeros(V ** (G + 1))
+    for x in itertools.product(range(V), repeat=G):
+        law += _block_prob(pd, a0, x) * _emitted_law(pd, pt, C, a0, x, ell_of(x), G, V)
+    return law
+
+
+@pytest.mark.parametrize("rule", ["full", "ell0", "ell1", "ell2", "scheduler"])
+def test_verify_is_lossless_by_exact_enumeration(rule):
+    """V = 8, gamma = 3: all 512 draft blocks and every branch; the law of the completed
+    strings equals the target chain's to 1e-12."""
+    V, G, r, a0 = 8, 3, 3, 2
+    U1, W1, W2t, pd, logpt = _enum_tables(11, V, G, r)
+    pt = np.exp(logpt)
+    if rule == "full":
+        ell_of = lambda x: G
+    elif rule.startswith("ell"):
+        ell_of = lambda x, e=int(rule[3:]): e
+    else:
+        # confidence head + greedy scheduler, one request: c_k depends on x_{k-1} only
+        rng = np.random.default_rng(5)
+        h = rng.normal(size=(1, G, 4))
+        w = rng.normal(size=4 + r)
+        W1c = rng.normal(size=(V, r)) * 2.0
+        N = np.arange(G + 2, dtype=np.float64)
+        sps = 1000.0 / (10.0 + 3.0 * N + N ** 2)
+        table = {}
+        for x in itertools.product(range(V), repeat=G):
+            c = oracle.confidence(h, W1c, w, np.array([a0]), np.array([x], np.int32))
+            table[x] = int(oracle.schedule(c.astype(np.float32), sps, 0)[0][0])
+        assert len(set(table.values())) > 1          # the budget does vary with the block
+        ell_of = table.__getitem__
+    law = _enumerate(pd, pt, a0, G, V, ell_of)
+    target = _target_law(logpt, a0, G, V)
+    assert abs(law.sum() - 1.0) < 1e-12
+    assert np.max(np.abs(law - target)) < 1e-12
+
+
+def test_verify_lossless_enumeration_two_coupled_requests():
+    """B = 2, V = 4, gamma = 2 with the greedy scheduler choosing both budgets from both
+    blocks: the joint law of the two completed strings is the product of the target laws."""
+    V, G, r = 4, 2, 2
+    U1, W1, W2t, pd, logpt = _enum_tables(12, V, G, r)
+    pt = np.exp(logpt)
+    a = (1, 3)
+    C = _completions(pt, G, V)
+    rng = np.random.default_rng(17)
+    h = rng.normal(size=(2, G, 3)) * 0.3
+    w = rng.normal(size=3 + r)
+    W1c = rng.normal(size=(V, r)) * 2.0
+    N = np.arange(2 * (G + 1) + 1, dtype=np.float64)
+    sps = 1000.0 / (30.0 + N + 0.5 * N ** 2)
+    joint = np.zeros((V ** (G + 1), V ** (G + 1)))
+    budgets = set()
+    for x1 in itertools.product(range(V), repeat=G):
+        for x2 in itertools.product(range(V), repeat=G):
+            toks = np.array([x1, x2], np.int32)
+            c = oracle.confidence(h, W1c, w, np.array(a), toks).astype(np.float32)
+            ell = oracle.schedule(c, sps, 0)[0]
+            budgets.add(tuple(int(e) for e in ell))
+            l1 = _emitted_law(pd, pt, C, a[0], x1, int(ell[0]), G, V)
+            l2 = _emitted_law(pd, pt, C, a[1], x2, int(ell[1]), G, V)
+            joint += _block_prob(pd, a[0], x1) * _block_prob(pd, a[1], x2) * np.outer(l1, l2)
+    assert len(budgets) >= 4          # each request's budget depends on both blocks
+    target = np.outer(_target_law(logpt, a[0], G, V), _target_law(logpt, a[1], G, V))
+    assert np.max(np.abs(joint - target)) < 1e-12
+
+
+def test_verify_enumeration_detects_an_anticipating_budget():
+    """Negative control: a budget that stops before the first drafted token the target
+    likes less than the draft (it looks at x_k itself) changes the law."""
+    V, G, r, a0 = 8, 3, 3, 2
+    U1, W1, W2t, pd, logpt = _enum_tables(11, V, G, r)
+    pt = np.exp(logpt)
+
+    def anticipating(x):
+        prevs = (a0,) + tuple(x)
+        for k in range(G):
+            if pt[k][prevs[k]][x[k]] < pd[k][prevs[k]][x[k]]:
+                return k
+        return G
+
+    law = _enumerate(pd, pt, a0, G, V, anticipating)
+    # total variation 0.027 here, against below 1e-12 per string for every rule above
+    assert 0.5 * np.abs(law - _target_law(logpt, a0, G, V)).sum() > 1e-2
+
+
+def test_oracle_verify_takes_the_enumerated_branches():
+    """The oracle's verification follows the branches enumerated above: on every one of the
+    512 blocks, x_k is accepted exactly when u * p_d(x_k) < p_t(x_k) for its uniform u, a
+    correction token has positive residual mass, and a bonus token has positive p_t."""
+    V, G, r, a0 = 8, 3, 3, 2
+    U1, W1, W2t, pd, logpt = _enum_tables(11, V, G, r)
+    pt = np.exp(logpt)
+    blocks = np.array(list(itertools.product(range(V), repeat=G)), np.int32)
+    B = len(blocks)
+    anchor = np.full(B, a0, np.int32)
+    prevs = np.concatenate([anchor[:, None], blocks], axis=1)
+    T = np.stack([logpt[k][prevs[:, k]] for k in range(G + 1)], axis=1)
+    U = np.broadcast_to(U1, (B, G, V)).copy()
+    seed = 4242
+    v = oracle.verify(U, W1, W2t, anchor, blocks, T, np.full(B, G, np.int32), 1.0, seed)
+    kinds = set()
+    for b in range(B):
+        n = int(v["n_accept"][b])
+        out = v["out_tokens"][b]
+        assert np.array_equal(out[:n], blocks[b][:n])
+        for k in range(min(n + 1, G)):
+            u = oracle.uniforms(seed, b, k + 1, 1, 0, 1)[0]
+            q_t, q_d = pt[k][prevs[b, k]], pd[k][prevs[b, k]]
+            accepted = u * q_d[blocks[b][k]] < q_t[blocks[b][k]]
+            assert accepted == (k < n), (b, k)
+        y = int(out[n])
+        if n < G:
+            rho = np.maximum(0.0, pt[n][prevs[b, n]] - pd[n][prevs[b, n]])
+            assert rho[y] > 0
+            kinds.add("residual")
+        else:
+            assert pt[G][prevs[b, G]][y] > 0
+            kinds.add("bonus")
+        assert np.all(out[n + 1:] == -1)
+    assert kinds == {"residual", "bonus"}
+
+
 def test_verify_acceptance_frequency_equals_tv_rate():
     """P(accept x_1) = sum_v min(p_d, p_t) = alpha (Monte Carlo, 5-sigma)."""
     rng = np.random.default_rng(4)
