@@ -103,9 +103,12 @@ __global__ __launch_bounds__(256) void k_draft_row(
   }
 }
 
-// Final merge: one wave per (request, position).  part is [gamma][slices][B] base-2
-// states merged in slice order; the winner's logit z_x = (U[x] + W1[prev] . W2t[x]) / T
-// is recomputed here (one dot of length r).
+// Final merge: one workgroup of four waves per (position, 8 consecutive requests).  Lane
+// (i, p) = (l % 8, l / 8) of wave w takes request b0 + i and merges, in order, the base-2
+// states of the slots 8 w + p + 32 j, j = 0, 1, ...; one load instruction thus reads eight
+// slots of 64 contiguous bytes each (the slots are [slots][B]).  The 32 phases are combined
+// by a fixed butterfly over the lanes and then over the waves, in wave order.  The winner's
+// logit z_x = (U[x] + W1[prev] . W2t[x]) / T is recomputed with the rank split the same way.
 template <typename WT>
 __global__ __launch_bounds__(256) void k_draft_final(
     const float2* __restrict__ part, const unsigned long long* __restrict__ best,
@@ -113,41 +116,59 @@ __global__ __launch_bounds__(256) void k_draft_final(
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ forced, int B, int G, int V,
     int r, float invT, int nslices, int32_t* __restrict__ tokens, float* __restrict__ logp,
     float* __restrict__ lse) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wid >= B * G) return;
-  const int b = wid % B, kk = wid / B;
-  const uint32_t idx = packed_index(best[(size_t)kk * B + b]);
+  __shared__ float red[4][8][3];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int noct = (B + 7) / 8;
+  const int kk = blockIdx.x / noct, i8 = lane & 7, ph = 8 * wv + (lane >> 3);
+  const int b = (blockIdx.x % noct) * 8 + i8;
+  const bool live = b < B;
+  const int bb = live ? b : B - 1;   // lanes past B work on a valid request, report nothing
+  const float2* pp = part + (size_t)kk * nslices * B + bb;
   float m = -3.0e38f, l = 0.f;
-  for (int s = lane; s < nslices; s += kWave) {
-    const float2 p = part[((size_t)kk * nslices + s) * B + b];
-    const float mn = fmaxf(m, p.x);
-    l = l * __builtin_amdgcn_exp2f(m - mn) + p.y * __builtin_amdgcn_exp2f(p.x - mn);
+#pragma unroll 4
+  for (int s = ph; s < nslices; s += 32) {
+    const float2 q = pp[(size_t)s * B];
+    const float mn = fmaxf(m, q.x);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + q.y * __builtin_amdgcn_exp2f(q.x - mn);
     m = mn;
   }
+  const uint32_t idx = packed_index(best[(size_t)kk * B + bb]);
+  const bool won = idx < (uint32_t)V;   // false only if no candidate had a finite score
+  const int x = won ? (int)idx : 0;
+  const int prev = draft_prev(anchor, forced, kk > 0 ? best + (size_t)(kk - 1) * B : nullptr,
+                              bb, G, kk + 1, V);
+  float dot = 0.f;
+  for (int i = ph; i < r; i += 32)
+    dot = fmaf(Elem<WT>::get(W1, (size_t)prev * r + i), Elem<WT>::get(W2t, (size_t)x * r + i),
+               dot);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
+  for (int o = 8; o < 64; o <<= 1) {
     const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
     const float mn = fmaxf(m, om);
     l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
     m = mn;
+    dot += __shfl_xor(dot, o, kWave);
   }
-  const int prev = draft_prev(anchor, forced, kk > 0 ? best + (size_t)(kk - 1) * B : nullptr,
-                              b, G, kk + 1, V);
-  const bool won = idx < (uint32_t)V;   // false only if no candidate had a finite score
-  const int x = won ? (int)idx : 0;
-  float dot = 0.f;
-  for (int i = lane; i < r; i += kWave)
-    dot = fmaf(Elem<WT>::get(W1, (size_t)prev * r + i), Elem<WT>::get(W2t, (size_t)x * r + i),
-               dot);
-  dot = wave_sum(dot);
-  if (lane == 0) {
-    const float lz = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
-    const float zx = (U[((size_t)b * G + kk) * V + x] + dot) * invT;
-    const size_t o = (size_t)b * G + kk;
-    tokens[o] = won ? (int32_t)idx : -1;
-    lse[o] = lz;
-    logp[o] = won ? zx - lz : __builtin_nanf("");
+  if (lane < 8) {
+    red[wv][i8][0] = m;
+    red[wv][i8][1] = l;
+    red[wv][i8][2] = dot;
   }
+  __syncthreads();
+  if (wv != 0 || lane >= 8 || !live) return;
+  for (int w = 1; w < 4; ++w) {
+    const float om = red[w][i8][0], ol = red[w][i8][1];
+    const float mn = fmaxf(m, om);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+    m = mn;
+    dot += red[w][i8][2];
+  }
+  const float lz = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+  const float zx = (U[((size_t)b * G + kk) * V + x] + dot) * invT;
+  const size_t o = (size_t)b * G + kk;
+  tokens[o] = won ? (int32_t)idx : -1;
+  lse[o] = lz;
+  logp[o] = won ? zx - lz : __builtin_nanf("");
 }
 
 }  // namespace dspark
@@ -246,12 +267,13 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
       prof_end(st, 1);
     }
   }
+  const int fblocks = G * ((B + 7) / 8);   // one workgroup per (position, 8 requests)
   if (wdt == DSPARK_BF16)
-    hipLaunchKernelGGL(k_draft_final<uint16_t>, dim3((B * G + 3) / 4), dim3(256), 0, st, part,
+    hipLaunchKernelGGL(k_draft_final<uint16_t>, dim3(fblocks), dim3(256), 0, st, part,
                        best, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced, B, G,
                        V, r, invT, plan.nslices, tokens, logp, lse);
   else
-    hipLaunchKernelGGL(k_draft_final<float>, dim3((B * G + 3) / 4), dim3(256), 0, st, part, best,
+    hipLaunchKernelGGL(k_draft_final<float>, dim3(fblocks), dim3(256), 0, st, part, best,
                        U, (const float*)W1, (const float*)W2t, anchor, forced, B, G, V, r, invT,
                        plan.nslices, tokens, logp, lse);
   return launch_status();
