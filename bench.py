@@ -373,9 +373,8 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "k_draft16<8>: fused bias MFMA (16x16x32 bf16, 16-column waves) + "
-                      "softmax + Gumbel race over W2t and the B base-logit rows, one draft "
-                      "position per launch",
+            "kernel": draft_kernel_name(B, V, r) + ": fused bias + softmax + Gumbel race "
+                      "over W2t and the B base-logit rows, one draft position per launch",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -453,6 +452,16 @@ def measured_traffic(workload_name: str):
     if h.hexdigest() != m_sha.group(1):
         return None
     return int(m_b.group(1))
+
+
+def draft_kernel_name(B: int, V: int, r: int) -> str:
+    """The draft position kernel the library dispatches for this shape (bf16 weights)."""
+    if r == 256 and 64 < B <= 256 and V % 4 == 0:
+        return ("k_draft16<8>" if B <= 128 else "k_draft16<16>") + \
+            " (16x16x32 bf16 MFMA, 16-column waves)"
+    if r == 256 and B >= 32:
+        return "k_mfma_bias<NCB, draft> (32x32x16 bf16 MFMA, 32-column waves)"
+    return "k_draft_row (row kernel, one request per workgroup row)"
 
 
 def cpu_baseline(inp, budget_s: float):
