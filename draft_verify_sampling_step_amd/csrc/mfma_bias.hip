@@ -511,11 +511,12 @@ int mfma_grid(int V, int ncols, int mode) {
 }
 
 dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st) {
-  // columns beyond 256 run as further launches over the same vocabulary tiles
-  for (int c0 = 0; c0 < args.ncols; c0 += 256) {
+  // columns beyond one group run as further launches over the same vocabulary tiles
+  const int group = mfma_column_group(args.mode);
+  for (int c0 = 0; c0 < args.ncols; c0 += group) {
     MfmaBiasArgs a = args;
     a.col0 = args.col0 + c0;
-    a.ncols = std::min(256, args.ncols - c0);
+    a.ncols = std::min(group, args.ncols - c0);
     dspark_status s = DSPARK_OK;
     if (a.mode == kModeDraft)
       s = draft16_supported(a) ? launch_draft16(a, nwg, st) : launch_mode<kModeDraft>(a, nwg, st);

@@ -121,7 +121,8 @@ TvWs tv_ws(const dspark_dims* d, int nrow_slices, int nsum_slices, void* base) {
 
 int tv_sum_slices(const dspark_dims* d, bool mfma) {
   const long long n = (long long)d->batch * d->gamma;
-  return mfma ? mfma_grid(d->vocab, (int)std::min<long long>(n, 256), kModeTV)
+  return mfma ? mfma_grid(d->vocab, (int)std::min<long long>(n, mfma_column_group(kModeTV)),
+                         kModeTV)
               : row_slices(d->vocab, n).count;
 }
 
