@@ -305,7 +305,7 @@ static dspark_status launch16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
 }
 
 bool draft16_supported(const MfmaBiasArgs& a) {
-  return a.mode == kModeDraft && a.ncols > 64 && a.ncols <= 256 && (a.V & 3) == 0;
+  return a.mode == kModeDraft && a.ncols > 32 && a.ncols <= 256 && (a.V & 3) == 0;
 }
 
 dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {

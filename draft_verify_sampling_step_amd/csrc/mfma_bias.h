@@ -72,7 +72,7 @@ dspark_status launch_mfma_bias(const MfmaBiasArgs& a, int nwg, hipStream_t st);
 // only one does), which measured faster although W2t is streamed twice as often.
 inline int mfma_column_group(int mode) { return mode == kModeTV ? 128 : 256; }
 
-// Draft mode on 16-column waves (mfma16.hip): 65..256 columns, V % 4 == 0; same grid and
+// Draft mode on 16-column waves (mfma16.hip): 33..256 columns, V % 4 == 0; same grid and
 // partial-slot layout as the 32-column kernel.
 bool draft16_supported(const MfmaBiasArgs& a);
 dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st);
