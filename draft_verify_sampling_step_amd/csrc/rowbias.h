@@ -3,7 +3,8 @@
 //
 // A workgroup of 256 threads computes one tile of 256 vocab rows: eight lanes share a
 // W2t row (each lane reads a contiguous r/8 slice with 16-byte loads, then the eight
-// partial sums are combined with xor-shuffles), 32 rows per pass, 8 passes per tile.
+// partial sums are combined with xor-shuffles), 32 rows per pass, 8 passes per tile.  For
+// bf16 weights of rank 256 the loads of four passes are in flight together.
 #pragma once
 
 #include "dspark_dev.h"
@@ -64,6 +65,42 @@ __device__ __forceinline__ void row_bias_tile(const WT* W2t, const float* w1s, f
                                               int r, int tile0, int v_end) {
   const int tid = threadIdx.x, sub = tid & 7, rowi = tid >> 3;
   const int len = r >> 3, i0 = sub * len;
+  if constexpr (sizeof(WT) == 2) {
+    if (r == 256) {
+      // bf16, rank 256: each lane's slice is 32 elements (four 16-byte loads).  Four passes'
+      // loads are issued before any is used; rows at or past v_end load row v_end - 1 and
+      // report 0.
+      for (int pass0 = 0; pass0 < 8; pass0 += 4) {
+        uint4 q[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int v = min(tile0 + (pass0 + p) * 32 + rowi, v_end - 1);
+          const uint4* src = reinterpret_cast<const uint4*>(W2t + (size_t)v * 256 + i0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) q[p][c] = src[c];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float acc = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t e[4] = {q[p][c].x, q[p][c].y, q[p][c].z, q[p][c].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc = fmaf(w1s[i0 + 8 * c + 2 * j], __uint_as_float(e[j] << 16), acc);
+              acc = fmaf(w1s[i0 + 8 * c + 2 * j + 1], __uint_as_float(e[j] & 0xFFFF0000u), acc);
+            }
+          }
+          acc += __shfl_xor(acc, 1, kWave);
+          acc += __shfl_xor(acc, 2, kWave);
+          acc += __shfl_xor(acc, 4, kWave);
+          const int t = (pass0 + p) * 32 + rowi;
+          if (sub == 0) bias_s[t] = tile0 + t < v_end ? acc : 0.f;
+        }
+      }
+      return;
+    }
+  }
   for (int pass = 0; pass < 8; ++pass) {
     const int t = pass * 32 + rowi;
     const int v = tile0 + t;
