@@ -7,7 +7,7 @@
 //                 conditioning tokens are known, so one pass over W2t serves up to 256
 //                 columns (bf16 MFMA path) -- with p_d = exp(z - lse_d) using the draft's
 //                 lse and p_t = exp(T/temperature - lse_t); partial sums per slice
-//  4. k_tv_final  alpha = partial sums added in slice order
+//  4. k_tv_final  alpha = partial sums added in a fixed order
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_bias.h"
@@ -24,13 +24,40 @@ __global__ __launch_bounds__(256) void k_tv_rows(const float* __restrict__ T, in
   const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
   const float* row = T + ((size_t)b * (G + 1) + kk) * V;
   ML st{-INFINITY, 0.f};
-  for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
-    const float z = row[v] * invT;
-    if (z > st.m) {
-      st.l = st.l * fast_exp(st.m - z) + 1.f;
-      st.m = z;
-    } else {
-      st.l += fast_exp(z - st.m);
+  if ((V & 3) == 0 && (slice_len & 3) == 0) {
+    // chunks of 8192 entries: each thread's eight 16-byte loads are issued before any is
+    // used, then the chunk's max and one exponential per entry (entries past the slice
+    // read as -inf; a finite floor keeps an all-padding thread at l = 0)
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    for (int c0 = v_begin; c0 < v_end; c0 += 8 * 1024) {
+      f32x4 q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int v = c0 + 4 * (threadIdx.x + 256 * i);
+        q[i] = v < v_end ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + v))
+                         : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+      float mq = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        mq = fmaxf(mq, fmaxf(fmaxf(q[i][0], q[i][1]), fmaxf(q[i][2], q[i][3])));
+      const float m = fmaxf(mq * invT, -3.0e38f);
+      float l = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l += fast_exp(fmaf(q[i][j], invT, -m));
+      st = ml_merge(st, ML{m, l});
+    }
+  } else {
+    for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
+      const float z = row[v] * invT;
+      if (z > st.m) {
+        st.l = st.l * fast_exp(st.m - z) + 1.f;
+        st.m = z;
+      } else {
+        st.l += fast_exp(z - st.m);
+      }
     }
   }
   st = block_ml(st, red, red + 4);
@@ -86,13 +113,26 @@ __global__ __launch_bounds__(256) void k_tv_row(
   if (tid == 0) tv_part[(size_t)s * ((size_t)B * G) + col] = acc;
 }
 
+// alpha of each (request, position) column: its partial sums over the slices, in a fixed
+// order.  Block of 256 threads = 32 columns x 8 slice phases; phase p adds the slices p,
+// p + 8, ... and the eight phase sums are added in phase order.
 __global__ __launch_bounds__(256) void k_tv_final(const float* __restrict__ tv_part, int n,
                                                   int nslices, float* __restrict__ alpha) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+  __shared__ float red[8][32];
+  const int c = threadIdx.x & 31, p = threadIdx.x >> 5;
+  const int i = blockIdx.x * 32 + c;
   float s = 0.f;
-  for (int q = 0; q < nslices; ++q) s += tv_part[(size_t)q * n + i];
-  alpha[i] = s;
+  if (i < n) {
+#pragma unroll 8
+    for (int q = p; q < nslices; q += 8) s += tv_part[(size_t)q * n + i];
+  }
+  red[p][c] = s;
+  __syncthreads();
+  if (p == 0 && i < n) {
+    float t = red[0][c];
+    for (int k = 1; k < 8; ++k) t += red[k][c];
+    alpha[i] = t;
+  }
 }
 
 }  // namespace dspark
@@ -180,7 +220,7 @@ extern "C" dspark_status dspark_accept_rate_tv(const dspark_dims* dm, const floa
                          (const float*)W1, (const float*)W2t, T, anchor, tokens, lse, w.lse_t,
                          B, G, V, r, rr.len, invT, w.tv_part);
   }
-  hipLaunchKernelGGL(k_tv_final, dim3((n + 255) / 256), dim3(256), 0, st, w.tv_part, n, nsum,
+  hipLaunchKernelGGL(k_tv_final, dim3((n + 31) / 32), dim3(256), 0, st, w.tv_part, n, nsum,
                      alpha);
   return launch_status();
 }
