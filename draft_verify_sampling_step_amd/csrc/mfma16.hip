@@ -21,7 +21,7 @@ namespace dspark {
 
 constexpr int kKS32 = kR / 32;   // k-steps of 32
 
-template <int NW>
+template <int NW, bool TV = false>
 struct Shape16 {
   static constexpr int NT = 64 * NW;
   static constexpr int NC = 16 * NW;          // columns
@@ -29,7 +29,7 @@ struct Shape16 {
   static constexpr int UD = 3;                // logit register buffers
   static constexpr int WG_PER_CU = 16 / NW;   // four waves per SIMD
   static constexpr int NA = 16 / NW;          // DMA instructions per wave per step
-  static constexpr int NU = 2;                // logit loads per wave per step
+  static constexpr int NU = TV ? 4 : 2;       // logit (and target) loads per wave per step
   // The stage of step s is waited for at step s.  A stage issued inside the loop (at step
   // s-SA+1) is followed by at least the loads of the SA-2 steps after that one (each step
   // issues NA + NU), so once at most that many are outstanding it has landed.
@@ -50,20 +50,28 @@ struct Shape16 {
     return early_after(p) < kWaitSS ? early_after(p) : kWaitSS;
   }
   static constexpr size_t kOffMeta = (size_t)SA * kTileBytes;
-  static constexpr size_t kLds = kOffMeta + (size_t)NC * (8 + 4 + 4);
+  // column metadata: logit row offset, column, conditioning token; TV adds the target row
+  // offset and the two base-2 normalisers
+  static constexpr size_t kLds = kOffMeta + (size_t)NC * (8 + 4 + 4) + (TV ? (size_t)NC * 16 : 0);
   static_assert(NW == 8 || NW == 16, "16 or 32 DMA rows per wave pair");
   static_assert(kLds * WG_PER_CU <= 160 * 1024, "LDS budget");
   static_assert(kWaitSS < 64, "vmcnt range");
 };
 
-template <int NW>
+// TV = true: the same stream computes the TV accept rate [CSDN Eq. 8] of up to 128 (request,
+// position) columns instead of a draft position: p_d = 2^(z log2 e - lse_d), p_t from the
+// target slices loaded beside the logit slices, and the per-lane sum of min(p_d, p_t).
+template <int NW, bool TV = false>
 __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
-  using S = Shape16<NW>;
+  using S = Shape16<NW, TV>;
   constexpr int NC = S::NC, SA = S::SA, UD = S::UD;
   extern __shared__ __align__(16) unsigned char smem[];
   long long* col_urow = reinterpret_cast<long long*>(smem + S::kOffMeta);   // [NC]
   int* col_b = reinterpret_cast<int*>(col_urow + NC);
   int* col_prev = col_b + NC;
+  long long* col_trow = reinterpret_cast<long long*>(col_prev + NC);   // TV: [NC]
+  float* col_ld = reinterpret_cast<float*>(col_trow + NC);             // TV: [NC] base 2
+  float* col_lt = col_ld + NC;                                        // TV: [NC] base 2
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, n16 = lane & 15;
@@ -99,15 +107,36 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
   // ---- column metadata: request, conditioning token, base-logit row offset
   for (int c = tid; c < NC; c += S::NT) {
     int b = -1, prev = 0;
-    if (c < a.ncols) {
-      b = a.col0 + c;
-      prev = (a.k == 1) ? a.anchor[b]
-                        : (a.forced ? a.forced[(size_t)b * G + (a.k - 2)]
-                                    : (int)packed_index(a.best_prev[b]));
+    if constexpr (TV) {
+      // column = (request, position): b = gc / G, k = gc % G + 1
+      long long urow = -1, trow = -1;
+      float ld = 0.f, lt = 0.f;
+      if (c < a.ncols) {
+        const int gc = a.col0 + c, rb = gc / G, k = gc % G + 1;
+        b = gc;
+        prev = (k == 1) ? a.anchor[rb] : a.tokens[(size_t)rb * G + (k - 2)];
+        urow = ((long long)rb * G + (k - 1)) * V;
+        trow = ((long long)rb * (G + 1) + (k - 1)) * V;
+        ld = a.lse_d[(size_t)rb * G + (k - 1)] * kLog2e;
+        lt = a.lse_t[(size_t)rb * G + (k - 1)] * kLog2e;
+      }
+      col_b[c] = b;
+      col_prev[c] = clamp_tok(prev, V);
+      col_urow[c] = urow;
+      col_trow[c] = trow;
+      col_ld[c] = ld;
+      col_lt[c] = lt;
+    } else {
+      if (c < a.ncols) {
+        b = a.col0 + c;
+        prev = (a.k == 1) ? a.anchor[b]
+                          : (a.forced ? a.forced[(size_t)b * G + (a.k - 2)]
+                                      : (int)packed_index(a.best_prev[b]));
+      }
+      col_b[c] = b;
+      col_prev[c] = clamp_tok(prev, V);
+      col_urow[c] = b >= 0 ? ((long long)b * G + (a.k - 1)) * V : -1;
     }
-    col_b[c] = b;
-    col_prev[c] = clamp_tok(prev, V);
-    col_urow[c] = b >= 0 ? ((long long)b * G + (a.k - 1)) * V : -1;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -117,6 +146,8 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
   const int col = wave * 16 + n16;
   const int cb = col_b[col];
   const long long curow = col_urow[col];
+  const long long ctrow = TV ? col_trow[col] : -1;   // TV: target row, base-2 normalisers
+  const float cld = TV ? col_ld[col] : 0.f, clt = TV ? col_lt[col] : 0.f;
   u32x4_t Bop[kKS32];
   if constexpr (S::kW1Staged) {
     // whole 512-byte rows by DMA, two rows per instruction in the pair layout, then the
@@ -143,7 +174,8 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
 
   // ---- base logits of one step in the output layout: block rb, rows 16 rb + 4q + i
   f32x4_t Ub[UD][2];
-  auto load_logits = [&](int step, f32x4_t (&u)[2]) {
+  f32x4_t Tb[TV ? UD : 1][2];                  // TV: the target slices, same layout
+  auto load_logits = [&](int step, f32x4_t (&u)[2], f32x4_t (&tt)[2]) {
     const int t = t0 + step;
     const bool live = cb >= 0 && t < t1;       // else one valid dummy address per load
     const int vb = t * 32 + 4 * q;
@@ -152,6 +184,10 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
       const int v = min(vb + 16 * rb, V - 4);
       const float* pu = live ? a.U + curow + v : a.U;
       u[rb] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pu));
+      if constexpr (TV) {
+        const float* pt = live ? a.T + ctrow + v : a.T;
+        tt[rb] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(pt));
+      }
     }
     if (__builtin_expect((t + 1) * 32 > V, 0)) {
       // the vocabulary's last tile: a whole run lies past V (V % 4 == 0); its logits
@@ -169,12 +205,13 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
 #pragma unroll
   for (int p = 0; p < S::PRE; ++p) {
     if (p < SA - 1) issue_dma(p);
-    if (p < UD - 1) load_logits(p, Ub[p]);
+    if (p < UD - 1) load_logits(p, Ub[p], Tb[TV ? p : 0]);
   }
 
   // per-lane running state of the lane's column
   float st_m = kNegBig, st_l = 0.f, st_s = -INFINITY;
   uint32_t st_v = 0xFFFFFFFFu;
+  float st_tv = 0.f;                           // TV: running sum of min(p_d, p_t)
 
   // lane's A-fragment base within a stage: row n16 of block rb, chunk 4 kk + q
   const int a_lane = (n16 >> 1) * kPairBytes + (2 * q + (n16 & 1)) * 16;
@@ -191,7 +228,7 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
     }
     barrier_no_fence();
     issue_dma(step + SA - 1);
-    load_logits(step + UD - 1, Ub[NXT]);
+    load_logits(step + UD - 1, Ub[NXT], Tb[TV ? NXT : 0]);
 
     const int t = t0 + step;
     if (t >= t1) return;                       // wave-uniform (also every step >= nsteps);
@@ -220,6 +257,16 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = acc[e >> 2][e & 3];
+    if constexpr (TV) {
+      // p_d = 2^(z s2 - lse_d), p_t = 2^(t s2 - lse_t) (rows past V: p_d = 0)
+      float mn[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        mn[e] = fminf(ex2(fmaf(y[e], s2, -cld)), ex2(fmaf(Tb[BUF][0][e], s2, -clt))) +
+                fminf(ex2(fmaf(y[e + 4], s2, -cld)), ex2(fmaf(Tb[BUF][1][e], s2, -clt)));
+      st_tv += (mn[0] + mn[1]) + (mn[2] + mn[3]);
+      return;
+    }
     float mx = fmaxf(y[0], y[1]);
 #pragma unroll
     for (int e = 2; e < 8; ++e) mx = fmaxf(mx, y[e]);
@@ -269,6 +316,13 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
     unroll_steps<0, UD, -1>(step, step_body);
   __builtin_amdgcn_s_waitcnt(0);   // dummy DMAs of the last steps have landed
 
+  if constexpr (TV) {
+    float sum = st_tv;
+    sum += __shfl_xor(sum, 16, kWave);
+    sum += __shfl_xor(sum, 32, kWave);
+    if (q == 0 && cb >= 0) a.tv_part[(size_t)wg * ((size_t)a.B * a.G) + cb] = sum;
+    return;
+  }
   // ---- merge the four row quads of each column (lanes n16 + 16 q), in a fixed order
   float m = st_m, l = st_l, sc = st_s;
   uint32_t v = st_v;
@@ -289,26 +343,28 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
   }
 }
 
-template <int NW>
+template <int NW, bool TV = false>
 static dspark_status launch16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
-  using S = Shape16<NW>;
+  using S = Shape16<NW, TV>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_draft16<NW>,
+    if (hipFuncSetAttribute((const void*)k_draft16<NW, TV>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) !=
         hipSuccess)
       return DSPARK_E_HIP;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_draft16<NW>, dim3(nwg), dim3(S::NT), S::kLds, st, a);
+  hipLaunchKernelGGL((k_draft16<NW, TV>), dim3(nwg), dim3(S::NT), S::kLds, st, a);
   return launch_status();
 }
 
 bool draft16_supported(const MfmaBiasArgs& a) {
+  if (a.mode == kModeTV) return a.ncols > 32 && a.ncols <= 128 && (a.V & 3) == 0;
   return a.mode == kModeDraft && a.ncols > 32 && a.ncols <= 256 && (a.V & 3) == 0;
 }
 
 dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
+  if (a.mode == kModeTV) return launch16<8, true>(a, nwg, st);
   return a.ncols <= 128 ? launch16<8>(a, nwg, st) : launch16<16>(a, nwg, st);
 }
 

@@ -521,7 +521,7 @@ dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st
     if (a.mode == kModeDraft)
       s = draft16_supported(a) ? launch_draft16(a, nwg, st) : launch_mode<kModeDraft>(a, nwg, st);
     else if (a.mode == kModeResid) s = launch_mode<kModeResid>(a, nwg, st);
-    else s = launch_mode<kModeTV>(a, nwg, st);
+    else s = draft16_supported(a) ? launch_draft16(a, nwg, st) : launch_mode<kModeTV>(a, nwg, st);
     if (s != DSPARK_OK) return s;
   }
   return DSPARK_OK;
