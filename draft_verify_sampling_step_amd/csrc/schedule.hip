@@ -8,7 +8,10 @@
 //     the key (a, b*gamma + j - 1) is a total order.  Each request's run of gamma is in
 //     order already (its prefix products never increase when every c <= 1; a run that is
 //     not is sorted by insertion), so adjacent runs are merged level by level in LDS,
-//     every output slot locating its source with a merge-path binary search;
+//     every output slot locating its source with a merge-path binary search.  The merged
+//     blocks hold consecutive requests, so every index of the left block is below every
+//     index of the right one: a tie of a goes to the left, and the merge compares the a
+//     values alone (kept apart from the indices, 8 bytes per LDS read);
 //  3. the greedy walk: tau accumulates in fp64 in sorted order (a sequential chain, the
 //     plain definition's rounding); the stop tests of 64 candidates at a time run in
 //     parallel on one wave; the walk stops at the first candidate that does not raise
@@ -20,26 +23,19 @@
 
 namespace dspark {
 
-// One candidate of the order: (a, index) with index = b * gamma + j - 1; 16 bytes in LDS.
-struct SKey {
-  double a;
-  uint32_t i;
-  uint32_t pad;
-};
-
-// the scheduler's total order: a descending, then index ascending (indices are distinct)
-__device__ __forceinline__ bool sched_before(const SKey& x, const SKey& y) {
-  return x.a > y.a || (x.a == y.a && x.i < y.i);
-}
+// LDS bytes per candidate: its a (fp64) and its index b * gamma + j - 1 (u32), each in
+// two buffers (merge source and destination)
+constexpr size_t kSchedBytesPer = 2 * (sizeof(double) + sizeof(uint32_t));
 
 // Number of elements of A (length la) among the first `diag` elements of the merge of the
-// sorted runs A and B (merge-path search; the order is strict, so the split is unique).
-__device__ __forceinline__ int merge_split(const SKey* A, int la, const SKey* Bv, int lb,
+// sorted runs A and B, where every index in A is below every index in B (so an element of
+// B goes first only when its a is strictly larger; the split is unique).
+__device__ __forceinline__ int merge_split(const double* A, int la, const double* Bv, int lb,
                                            int diag) {
   int lo = diag > lb ? diag - lb : 0, hi = diag < la ? diag : la;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (sched_before(Bv[diag - 1 - mid], A[mid]))
+    if (Bv[diag - 1 - mid] > A[mid])
       hi = mid;
     else
       lo = mid + 1;
@@ -62,32 +58,40 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
 #pragma clang fp contract(off)
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, n = B * G;
-  SKey* X = reinterpret_cast<SKey*>(smem);   // [n], then [n] for the other merge buffer
-  SKey* Y = X + n;
+  double* XA = reinterpret_cast<double*>(smem);   // a: [n], then [n] for the other buffer
+  double* YA = XA + n;
+  uint32_t* XI = reinterpret_cast<uint32_t*>(YA + n);   // index: [n], then [n]
+  uint32_t* YI = XI + n;
   __shared__ double sps_win[kSpsWin + 1];    // sps[B + i], i <= min(n, kSpsWin)
   for (int i = tid; i <= min(n, kSpsWin); i += blockDim.x) sps_win[i] = sps[B + i];
   // 1. prefix survival, one thread per request, left to right in fp64.  With every
   // c <= 1 a request's run is already in order (a non-increasing, index increasing); a run
   // that is not (some c > 1) is put in order by insertion.
   for (int b = tid; b < B; b += blockDim.x) {
-    SKey* run = X + (size_t)b * G;
+    double* ra = XA + (size_t)b * G;
+    uint32_t* ri = XI + (size_t)b * G;
     double a = 1.0;
     bool sorted = true;
     for (int j = 0; j < G; ++j) {
       const double prev = a;
       a = a * (double)c[(size_t)b * G + j];
       sorted = sorted && !(a > prev);
-      run[j] = SKey{a, (uint32_t)(b * G + j), 0u};
+      ra[j] = a;
+      ri[j] = (uint32_t)(b * G + j);
     }
     if (!sorted) {
+      // (a descending, index ascending) within the run
       for (int j = 1; j < G; ++j) {
-        const SKey key = run[j];
+        const double ka = ra[j];
+        const uint32_t ki = ri[j];
         int q = j - 1;
-        while (q >= 0 && sched_before(key, run[q])) {
-          run[q + 1] = run[q];
+        while (q >= 0 && (ka > ra[q] || (ka == ra[q] && ki < ri[q]))) {
+          ra[q + 1] = ra[q];
+          ri[q + 1] = ri[q];
           --q;
         }
-        run[q + 1] = key;
+        ra[q + 1] = ka;
+        ri[q + 1] = ki;
       }
     }
   }
@@ -100,57 +104,79 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
     for (int p = 2 * tid; p < n; p += 2 * blockDim.x) {
       const int base = p / (2 * L) * (2 * L);
       const int la = min(L, n - base), lb = min(L, max(0, n - base - L));
-      const SKey* A = X + base;
-      const SKey* Bv = A + la;
+      const double* A = XA + base;
+      const double* Bv = A + la;
       const int d = p - base;
       int i = merge_split(A, la, Bv, lb, d), j = d - i;
-      bool take_a = i < la && (j >= lb || sched_before(A[i], Bv[j]));
-      Y[p] = take_a ? A[i] : Bv[j];
+      // the left element goes first unless the right one's a is strictly larger
+      bool take_a = i < la && (j >= lb || A[i] >= Bv[j]);
+      YA[p] = take_a ? A[i] : Bv[j];
+      YI[p] = XI[base + (take_a ? i : la + j)];
       if (p + 1 < n) {
         i += take_a ? 1 : 0;
         j += take_a ? 0 : 1;
-        take_a = i < la && (j >= lb || sched_before(A[i], Bv[j]));
-        Y[p + 1] = take_a ? A[i] : Bv[j];
+        take_a = i < la && (j >= lb || A[i] >= Bv[j]);
+        YA[p + 1] = take_a ? A[i] : Bv[j];
+        YI[p + 1] = XI[base + (take_a ? i : la + j)];
       }
     }
     __syncthreads();
-    SKey* t = X;
-    X = Y;
-    Y = t;
+    double* ta = XA;
+    XA = YA;
+    YA = ta;
+    uint32_t* ti = XI;
+    XI = YI;
+    YI = ti;
   }
   // greedy walk on wave 0, 64 candidates per chunk.  tau_t follows the sequential fp64
-  // chain tau_{t+1} = tau_t + a_(t) exactly (lane order, each a_(t) broadcast from its lane);
-  // the best Theta before candidate t is tau_t * sps[B + t] (each admission raises it to
-  // exactly that product), so the stop tests of a chunk are independent and run in parallel.
+  // chain tau_{t+1} = tau_t + a_(t) exactly: every lane runs the whole chain of the chunk
+  // on a_(t) values read from LDS ahead of it (one address for all lanes), and after each
+  // add all lanes store the same running value into chain[i + 1], so lane i then reads the
+  // values before and after its own add.  The best Theta before candidate t is
+  // tau_t * sps[B + t] (each admission raises it to exactly that product), so the stop
+  // tests of a chunk are independent and run in parallel.
   __shared__ int stop_s;
   __shared__ double tau_s;
+  __shared__ double chain[65];
   if (tid < 64) {
     const int lane = tid;
     double tau = (double)B;
     int stop = n;
     for (int base = 0; base < n; base += 64) {
       const int t = base + lane;
-      const double at = t < n ? X[t].a : 0.0;
       const int cnt = min(64, n - base);
-      double before = 0.0, after = 0.0, cur = tau;
-      const unsigned long long atb = (unsigned long long)__double_as_longlong(at);
-      const uint32_t at_lo = (uint32_t)atb, at_hi = (uint32_t)(atb >> 32);
-      // candidate i's a, read from lane i into scalar registers; a full chunk is unrolled,
-      // so the lane numbers are immediates and only the chain of adds is serial
-      auto link = [&](int i) {
-        const uint32_t lo = __builtin_amdgcn_readlane(at_lo, i);
-        const uint32_t hi = __builtin_amdgcn_readlane(at_hi, i);
-        const double ai = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-        before = (lane == i) ? cur : before;
-        cur = cur + ai;
-        after = (lane == i) ? cur : after;
-      };
+      const double* ab = XA + base;
+      double cur = tau;
+      chain[0] = cur;
       if (cnt == 64) {
+        // a full chunk: 16 values in registers at a time, the next 16 loaded before the
+        // adds of these
+        double av[16], nv[16];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) link(i);
+        for (int i = 0; i < 16; ++i) av[i] = ab[i];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          if (blk < 3) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) nv[i] = ab[16 * (blk + 1) + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            cur = cur + av[i];
+            chain[16 * blk + i + 1] = cur;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) av[i] = nv[i];
+        }
       } else {
-        for (int i = 0; i < cnt; ++i) link(i);
+        for (int i = 0; i < cnt; ++i) {
+          cur = cur + ab[i];
+          chain[i + 1] = cur;
+        }
       }
+      __builtin_amdgcn_wave_barrier();
+      const double before = chain[lane];
+      const double after = chain[lane + 1];
       bool halt = false;
       if (mode == DSPARK_SCHED_GREEDY && t < n) {
         const double sp1 = t + 1 <= kSpsWin ? sps_win[t + 1] : sps[B + t + 1];
@@ -181,7 +207,7 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
   __syncthreads();
   // admitted candidates form a prefix of each request's block: ell_b = the largest j
   for (int t = tid; t < stop; t += blockDim.x) {
-    const uint32_t i = X[t].i;
+    const uint32_t i = XI[t];
     atomicMax(&ell[i / G], (int)(i % G) + 1);
   }
   if (tid == 0) {
@@ -201,7 +227,7 @@ dspark_status set_sched_attr() {
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((size_t)2 * kMaxSchedCandidates * sizeof(SKey))) != hipSuccess)
+                            (int)((size_t)kMaxSchedCandidates * kSchedBytesPer)) != hipSuccess)
       return DSPARK_E_HIP;
     attr_set = true;
   }
@@ -218,7 +244,7 @@ extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, c
   if (!c || !sps || !ell || !theta || !n_total) return DSPARK_E_NULL;
   if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (mode != DSPARK_SCHED_GREEDY && mode != DSPARK_SCHED_FULL) return DSPARK_E_VALUE;
-  const size_t sh = (size_t)2 * B * G * sizeof(SKey);
+  const size_t sh = (size_t)B * G * kSchedBytesPer;
   if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, 0, ell,
@@ -236,7 +262,7 @@ extern "C" dspark_status dspark_schedule_topk(int32_t B, int32_t G, const float*
   if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (k_admit < 0) return DSPARK_E_VALUE;
   const int k = (long long)k_admit > (long long)B * G ? B * G : k_admit;
-  const size_t sh = (size_t)2 * B * G * sizeof(SKey);
+  const size_t sh = (size_t)B * G * kSchedBytesPer;
   if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, (hipStream_t)stream, c, sps, B, G,
                      kSchedTopK, k, ell, theta, n_total);
