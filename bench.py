@@ -486,7 +486,7 @@ def measured_traffic(workload_name: str):
 def draft_kernel_name(B: int, V: int, r: int) -> str:
     """The draft position kernel the library dispatches for this shape (bf16 weights)."""
     if r == 256 and 32 < B <= 256 and V % 4 == 0:
-        return ("k_draft16<8>" if B <= 128 else "k_draft16<16>") + \
+        return ("k_draft16<8, false>" if B <= 128 else "k_draft16<16, false>") + \
             " (16x16x32 bf16 MFMA, 16-column waves)"
     if r == 256 and B >= 32:
         return "k_mfma_bias<NCB, draft> (32x32x16 bf16 MFMA, 32-column waves)"
