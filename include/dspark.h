@@ -189,7 +189,10 @@ dspark_status dspark_sts_calibrate(int32_t n, int32_t gamma, const float* logit,
  * are admitted one at a time from ell = 0 (tau = B, N = B), tau and Theta updated in fp64
  * in that order; the walk stops at the first candidate whose Theta <= the best Theta so
  * far.  FULL: every candidate is admitted (ell_b = gamma).
- *   c      [B][gamma] fp32 confidences in [0, 1].
+ *   c      [B][gamma] fp32 confidences in [0, 1] (sigmoid outputs).  Values above 1 are
+ *          not rejected: the order and the walk are still exact, but a can then grow
+ *          along a request, and ell_b is the largest admitted j, which need not be a
+ *          prefix of what was admitted.
  *   sps    [B*(gamma+1)+1] fp64 target steps per second at N verify tokens.
  *   ell    out [B] int32 verify lengths in 0..gamma.
  *   theta  out [1] fp64 final Theta; n_total out [1] int32 final N.
