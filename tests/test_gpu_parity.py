@@ -258,6 +258,13 @@ def test_schedule_edge_cases_bit_exact():
     cases.append((rng.uniform(size=(1, 4)).astype(np.float32), np.full(6, 3.0), 0))
     flat = np.full(4096 + 64 + 1, 5.0)
     cases.append((rng.uniform(0.5, 1, size=(64, 64)).astype(np.float32), flat, 0))
+    # candidate counts that are not powers of two: the merge's last blocks are ragged
+    for Br, Gr in ((5, 3), (100, 7), (37, 16), (129, 16)):
+        cr = rng.uniform(0.3, 1, size=(Br, Gr)).astype(np.float32)
+        cr[::4, : min(3, Gr)] = 1.0     # ties of a across requests in different blocks
+        sr = 1000.0 / (12.0 + 0.05 * np.arange(Br * (Gr + 1) + 1))
+        cases.append((cr, sr, 0))
+        cases.append((cr, sr, 1))
     for c, sps_, mode in cases:
         ell_o, th_o, n_o = oracle.schedule(c, sps_, mode)
         ell_g, th_g, n_g = ds.dspark_schedule(dev(c), dev(np.asarray(sps_, np.float64)), mode)
