@@ -158,6 +158,93 @@ def test_draft_global_request_id_keys_randomness():
     assert np.array_equal(full["tokens"][2:], sub["tokens"])
 
 
+def _scores_by_library(U, W1, W2t, prev, temperature, seed, b, k):
+    """Gumbel scores of one draft position computed apart from the oracle: numpy's matmul
+    for the bias, the pinned uniforms of stream 0, G = -ln(-ln u)."""
+    z = (np.asarray(U, np.float64) + oracle.widen(W1)[prev] @ oracle.widen(W2t).T) / temperature
+    u = oracle.uniforms(seed, b, k, 0, 0, z.shape[0])
+    return z - np.log(-np.log(u))
+
+
+def test_draft_gap_is_the_top_two_score_margin():
+    """The oracle's reported gap (what excuses a GPU/oracle token mismatch) equals the
+    margin between the two largest Gumbel scores computed apart (sorted fp64 scores), and
+    its token is the largest."""
+    inp = _tiny(seed=2, B=3, gamma=4, V=300, r=8, temperature=0.8)
+    T = 0.8
+    out = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, T, inp.seed)
+    tok = out["tokens"]
+    for b in range(3):
+        prev = [int(inp.anchor[b])] + [int(x) for x in tok[b, :-1]]
+        for k in range(4):
+            sc = _scores_by_library(inp.U[b, k], inp.W1, inp.W2t, prev[k], T, inp.seed, b, k + 1)
+            top = np.sort(sc)[::-1]
+            assert tok[b, k] == int(np.argmax(sc))
+            assert abs(out["gap"][b, k] - (top[0] - top[1])) <= 1e-9
+
+
+def test_draft_gap_moves_with_the_winning_logit():
+    """Raising the winner's base logit by d raises the gap by d/T; lowering it by half the
+    gap (times T) halves the gap; lowering it by 1.5 gaps hands the draw to the runner-up,
+    whose gap is then the smaller of half the old gap and its own lead over the third.  The
+    prefix is teacher-forced so only that position changes."""
+    inp = _tiny(seed=4, B=2, gamma=3, V=200, r=8)
+    T = 1.25
+    base = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, T, inp.seed)
+    tok = base["tokens"]
+    for b, k in [(0, 0), (1, 2)]:
+        g0 = base["gap"][b, k]
+        x = tok[b, k]
+        prev = int(inp.anchor[b]) if k == 0 else int(tok[b, k - 1])
+        sc = _scores_by_library(inp.U[b, k], inp.W1, inp.W2t, prev, T, inp.seed, b, k + 1)
+        s1, s2, s3 = np.sort(sc)[::-1][:3]
+        runner = int(np.argsort(sc)[::-1][1])
+        for shift, moves in [(0.7, False), (-0.5 * g0 * T, False), (-1.5 * g0 * T, True)]:
+            U = inp.U.copy()
+            U[b, k, x] += np.float32(shift)
+            d = (float(U[b, k, x]) - float(inp.U[b, k, x])) / T   # the score change, fp32-rounded
+            out = oracle.draft(U, inp.W1, inp.W2t, inp.anchor, T, inp.seed, forced=tok)
+            if moves:
+                assert out["tokens"][b, k] == runner
+                expect = s2 - max(s1 + d, s3)
+            else:
+                assert out["tokens"][b, k] == x
+                expect = s1 + d - s2
+            assert abs(out["gap"][b, k] - expect) <= 1e-9, (shift, out["gap"][b, k], expect)
+
+
+def test_verify_margin_and_decisions_computed_apart():
+    """The margin |u p_d(x) - p_t(x)| / p_t(x) the oracle reports for each accept test (what
+    excuses a GPU/oracle decision flip) and the decisions themselves, against p_d and p_t
+    from scipy's softmax of the draft and target logits and the pinned stream-1 uniforms;
+    NaN where no test is made (beyond the first rejection or beyond ell)."""
+    inp = _tiny(seed=6, B=6, gamma=4, V=60, r=8, temperature=0.9)
+    T = 0.9
+    d = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, T, inp.seed)
+    tok = d["tokens"]
+    Tl = workload.synthesize_target(inp, tok).astype(np.float64)
+    ell = np.array([4, 4, 3, 2, 1, 0], np.int32)
+    v = oracle.verify(inp.U, inp.W1, inp.W2t, inp.anchor, tok, Tl, ell, T, inp.seed)
+    W1, W2t = oracle.widen(inp.W1), oracle.widen(inp.W2t)
+    n_tests = 0
+    for b in range(6):
+        prev = [int(inp.anchor[b])] + [int(x) for x in tok[b, :-1]]
+        n = int(v["n_accept"][b])
+        made = min(n + 1, int(ell[b]))
+        for k in range(4):
+            if k >= made:
+                assert np.isnan(v["margin"][b, k])
+                continue
+            x = tok[b, k]
+            pd = special.softmax((inp.U[b, k].astype(np.float64) + W1[prev[k]] @ W2t.T) / T)[x]
+            pt = special.softmax(Tl[b, k] / T)[x]
+            u = oracle.uniforms(inp.seed, b, k + 1, 1, 0, 1)[0]
+            assert abs(v["margin"][b, k] - abs(u * pd - pt) / pt) <= 1e-10 * max(1.0, u * pd / pt)
+            assert (u * pd < pt) == (k < n)
+            n_tests += 1
+    assert n_tests >= 8 and (v["n_accept"] < ell).any()
+
+
 # ------------------------------------------------------------------------------------
 # confidence head
 # ------------------------------------------------------------------------------------
@@ -658,6 +745,155 @@ def test_verify_lossless_enumeration_two_coupled_requests():
     assert len(budgets) >= 4          # each request's budget depends on both blocks
     target = np.outer(_target_law(logpt, a[0], G, V), _target_law(logpt, a[1], G, V))
     assert np.max(np.abs(joint - target)) < 1e-12
+
+
+def _emitted_prefixes(pd, pt, a0, x, ell, V):
+    """Law over the variable-length token strings one verification of block x with budget
+    ell emits (x_1..x_n and the residual or bonus token), as {string: probability}."""
+    out = {}
+    prevs = (a0,) + tuple(x)
+    acc = 1.0
+    for k in range(ell):
+        q_t, q_d = pt[k][prevs[k]], pd[k][prevs[k]]
+        a = min(1.0, q_t[x[k]] / q_d[x[k]])
+        rho = np.maximum(0.0, q_t - q_d)
+        if a < 1.0:
+            for y in np.nonzero(rho > 0)[0]:
+                key = tuple(x[:k]) + (int(y),)
+                out[key] = out.get(key, 0.0) + acc * (1.0 - a) * rho[y] / rho.sum()
+        acc *= a
+    for y in range(V):
+        key = tuple(x[:ell]) + (y,)
+        out[key] = out.get(key, 0.0) + acc * pt[ell][prevs[ell]][y]
+    return out
+
+
+class _ChainedRounds:
+    """Two requests (B = 2), V = 4, gamma = 2, Markov draft and target tables, a confidence
+    head with its own hidden states per round, and the greedy scheduler's step-time table."""
+    V, G, B, r = 4, 2, 2, 2
+
+    def __init__(self, seed):
+        V, G, r = self.V, self.G, self.r
+        _, _, _, self.pd, logpt = _enum_tables(seed, V, G, r)
+        self.logpt = logpt
+        self.pt = np.exp(logpt)
+        self.C = _completions(self.pt, G, V)
+        rng = np.random.default_rng(seed + 100)
+        self.h = rng.normal(size=(3, self.B, G, 3)) * 0.3      # hidden states of rounds 0-2
+        self.w = rng.normal(size=3 + r)
+        self.W1c = rng.normal(size=(V, r)) * 4.0
+        N = np.arange(self.B * (G + 1) + 1, dtype=np.float64)
+        self.sps = 1000.0 / (10.0 + N + 0.3 * N ** 2)
+        self.blocks = list(itertools.product(range(V), repeat=G))
+
+    def conf(self, rnd, anchors, x1, x2):
+        toks = np.array([x1, x2], np.int32)
+        return oracle.confidence(self.h[rnd], self.W1c, self.w, np.array(anchors),
+                                 toks).astype(np.float32)
+
+    def block_pairs(self, anchors):
+        for x1 in self.blocks:
+            p1 = _block_prob(self.pd, anchors[0], x1)
+            for x2 in self.blocks:
+                yield x1, x2, p1 * _block_prob(self.pd, anchors[1], x2)
+
+    def target_pair(self, anchors):
+        return np.outer(_target_law(self.logpt, anchors[0], self.G, self.V),
+                        _target_law(self.logpt, anchors[1], self.G, self.V))
+
+    def greedy_round(self, rnd, anchors):
+        """Greedy round: ({(last token 1, last token 2, N - B): probability}, completed
+        joint law of the two requests' emitted strings)."""
+        states, joint = {}, np.zeros((self.V ** (self.G + 1),) * 2)
+        for x1, x2, w in self.block_pairs(anchors):
+            ell, _, N = oracle.schedule(self.conf(rnd, anchors, x1, x2), self.sps, 0)
+            e1 = _emitted_prefixes(self.pd, self.pt, anchors[0], x1, int(ell[0]), self.V)
+            e2 = _emitted_prefixes(self.pd, self.pt, anchors[1], x2, int(ell[1]), self.V)
+            for o1, q1 in e1.items():
+                for o2, q2 in e2.items():
+                    key = (o1[-1], o2[-1], N - self.B)
+                    states[key] = states.get(key, 0.0) + w * q1 * q2
+            joint += w * np.outer(
+                _emitted_law(self.pd, self.pt, self.C, anchors[0], x1, int(ell[0]), self.G, self.V),
+                _emitted_law(self.pd, self.pt, self.C, anchors[1], x2, int(ell[1]), self.G, self.V))
+        return states, joint
+
+    def topk_round(self, rnd, anchors, k_of):
+        """Top-K round, K = k_of(x1, x2): completed joint law of the emitted strings, and
+        whether K ever differed from the round's own greedy count."""
+        joint = np.zeros((self.V ** (self.G + 1),) * 2)
+        differs = False
+        for x1, x2, w in self.block_pairs(anchors):
+            c = self.conf(rnd, anchors, x1, x2)
+            K = k_of(x1, x2)
+            ell = oracle.schedule_topk(c, self.sps, K)[0]
+            differs |= K != oracle.schedule(c, self.sps, 0)[2] - self.B
+            joint += w * np.outer(
+                _emitted_law(self.pd, self.pt, self.C, anchors[0], x1, int(ell[0]), self.G, self.V),
+                _emitted_law(self.pd, self.pt, self.C, anchors[1], x2, int(ell[1]), self.G, self.V))
+        return joint, differs
+
+
+def test_verify_lossless_enumeration_delayed_topk_chained_rounds():
+    """The production scheduler ([XTL] §7): round t admits the first K candidates of its own
+    order with K = N - B of the greedy schedule of round t - 2.  Three chained rounds, each
+    anchored on the last tokens the round before emitted, from every anchor pair at the
+    start: rounds 0 and 1 greedy, round 2 top-K with K from round 0.  Every (anchor pair,
+    K) state round 2 can start from is enumerated (all draft blocks, every accept / residual
+    / bonus branch): its completed output law is exactly the product of the target laws from
+    its anchors, so the chain is lossless whatever history K carries.  Rounds 0 and 1 are
+    checked the same way."""
+    ch = _ChainedRounds(21)
+    after0 = {}                      # (anchor pair after round 0, K of round 0) -> probability
+    for a0 in itertools.product(range(ch.V), repeat=2):
+        st0, j0 = ch.greedy_round(0, a0)
+        assert np.max(np.abs(j0 - ch.target_pair(a0))) < 1e-12
+        for (l1, l2, K0), p in st0.items():
+            after0[(l1, l2, K0)] = after0.get((l1, l2, K0), 0.0) + p / ch.V ** 2
+    round1 = {}
+    states2 = {}                     # (anchor pair after round 1, K of round 0) -> probability
+    for (l1, l2, K0), p0 in after0.items():
+        if p0 <= 0.0:
+            continue
+        if (l1, l2) not in round1:
+            st1, j1 = ch.greedy_round(1, (l1, l2))
+            assert np.max(np.abs(j1 - ch.target_pair((l1, l2)))) < 1e-12
+            round1[(l1, l2)] = st1
+        for (m1, m2, _), p1 in round1[(l1, l2)].items():
+            if p1 > 0.0:
+                states2[(m1, m2, K0)] = states2.get((m1, m2, K0), 0.0) + p0 * p1
+    assert abs(sum(states2.values()) - 1.0) < 1e-12
+    assert len({K for _, _, K in states2}) >= 3         # the carried K does vary
+    worst, any_differs = 0.0, False
+    for (m1, m2, K0) in sorted(states2):
+        j2, differs = ch.topk_round(2, (m1, m2), lambda x1, x2, K=K0: K)
+        any_differs |= differs
+        worst = max(worst, np.max(np.abs(j2 - ch.target_pair((m1, m2)))))
+    assert worst < 1e-12
+    assert any_differs          # the delayed K is not simply the round's own greedy count
+
+
+def test_delayed_topk_enumeration_detects_a_budget_from_the_current_block():
+    """Negative control: K taken from round 2's own drafted tokens (the number of them the
+    target likes at least as much as the draft -- it looks at x_k itself) changes the law."""
+    ch = _ChainedRounds(21)
+    pd, pt = ch.pd, ch.pt
+
+    def anticipating(anchors):
+        def k_of(x1, x2):
+            n = 0
+            for a, x in ((anchors[0], x1), (anchors[1], x2)):
+                prevs = (a,) + tuple(x)
+                n += sum(pt[k][prevs[k]][x[k]] >= pd[k][prevs[k]][x[k]] for k in range(ch.G))
+            return n
+        return k_of
+
+    worst = 0.0
+    for anchors in [(1, 3), (0, 2), (2, 2)]:
+        j2, _ = ch.topk_round(2, anchors, anticipating(anchors))
+        worst = max(worst, 0.5 * np.abs(j2 - ch.target_pair(anchors)).sum())
+    assert worst > 1e-3, worst
 
 
 def test_verify_enumeration_detects_an_anticipating_budget():
