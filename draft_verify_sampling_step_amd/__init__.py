@@ -27,7 +27,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdspark.so")
 
 F32, BF16 = 0, 1
-SCHED_GREEDY, SCHED_FULL = 0, 1
+SCHED_GREEDY, SCHED_FULL, SCHED_TOPK_DELAYED = 0, 1, 2
 OP_DRAFT, OP_CONFIDENCE, OP_SCHEDULE, OP_VERIFY, OP_TV = 0, 1, 2, 3, 4
 
 _lib = None
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             L.dspark_rng_uniforms.argtypes = [_U64, ctypes.c_uint32, ctypes.c_uint32,
                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
                                               _P, _P]
+            L.dspark_gumbel_lattice.argtypes = [_I, _P, _P]
             L.dspark_loss_workspace_bytes.argtypes = [ctypes.c_int32] * 3
             L.dspark_loss_workspace_bytes.restype = _SZ
             L.dspark_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -106,6 +107,7 @@ def lib() -> ctypes.CDLL:
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
                        "dspark_draft_loss", "dspark_closed_loop", "dspark_rng_uniforms",
+                       "dspark_gumbel_lattice",
                        "dspark_profile_start", "dspark_profile_stop",
                        "dspark_stream_read_probe"):
                 getattr(L, fn).restype = _I
@@ -427,6 +429,14 @@ def dspark_rng_uniforms(seed: int, b: int, k: int, s: int, v0: int, n: int, devi
     out = torch.empty(n, dtype=torch.float32, device=device)
     _check(lib().dspark_rng_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, b, k, s, v0, n, _ptr(out),
                                      _stream_handle(stream)))
+    return out
+
+
+def dspark_gumbel_lattice(form: int, device="cuda", stream=None):
+    """The kernels' Gumbel transform on every uniform u = (2m + 1) 2^-24, m < 2^23: form 0
+    -ln(-ln u) (row kernels), form 1 -log2(-log2 u) (matrix-core kernels)."""
+    out = torch.empty(1 << 23, dtype=torch.float32, device=device)
+    _check(lib().dspark_gumbel_lattice(int(form), _ptr(out), _stream_handle(stream)))
     return out
 
 

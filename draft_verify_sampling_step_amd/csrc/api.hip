@@ -1,9 +1,13 @@
 // api.hip -- library-wide entry points: workspace sizes, status names, version, the
-// generator check hook dspark_rng_uniforms and the launch-timing switch.
+// generator check hooks dspark_rng_uniforms and dspark_gumbel_lattice, and the
+// launch-timing switch.
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "dspark_dev.h"
 #include "dspark_host.h"
+#include "mfma_common.h"
 
 size_t dspark_draft_workspace(const dspark_dims* d);
 size_t dspark_verify_workspace(const dspark_dims* d);
@@ -22,22 +26,44 @@ __global__ void k_rng_uniforms(uint32_t key0, uint32_t key1, uint32_t b, uint32_
   }
 }
 
+// Every value of the Gumbel transform on the uniform lattice u = (2m + 1) 2^-24,
+// m < 2^23, as the kernels compute it: form 0 the natural-log form of the row kernels,
+// form 1 the base-2 score offset of the matrix-core kernels (from the generator word
+// whose top 23 bits are m).
+__global__ void k_gumbel_lattice(int form, float* __restrict__ out) {
+  const uint32_t m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= (1u << 23)) return;
+  const uint32_t w = m << 9;
+  out[m] = form == 0 ? gumbel_from_uniform(word_to_uniform(w)) : neg_lglg(w);
+}
+
 // Launch timing: while enabled, the draft records a HIP event pair around each of its
-// per-position kernels on the caller's stream (measurement only; not thread-safe).
+// per-position kernels on the caller's stream (measurement only).  The state is guarded
+// by a mutex; when timing is off the hooks cost one relaxed atomic load.
 namespace {
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
 int g_prof_n = 0;              // events recorded (pairs are complete when even)
 long long g_prof_positions = 0;
 std::vector<hipEvent_t> g_prof_ev;
+
+void prof_release_events() {
+  for (hipEvent_t e : g_prof_ev) (void)hipEventDestroy(e);
+  g_prof_ev.clear();
+}
 }  // namespace
 
 void prof_begin(hipStream_t st) {
-  if (!g_prof_on || g_prof_n + 2 > (int)g_prof_ev.size()) return;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on.load(std::memory_order_relaxed) || g_prof_n + 2 > (int)g_prof_ev.size()) return;
   (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
 }
 
 void prof_end(hipStream_t st, int positions) {
-  if (!g_prof_on || (g_prof_n & 1) == 0) return;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on.load(std::memory_order_relaxed) || (g_prof_n & 1) == 0) return;
   if (positions < 0) {   // the launch was refused: drop its begin event
     --g_prof_n;
     return;
@@ -46,43 +72,75 @@ void prof_end(hipStream_t st, int positions) {
   g_prof_positions += positions;
 }
 
+namespace {
+std::mutex g_attr_mu;
+}  // namespace
+
+dspark_status LdsAttr::ensure(const void* kernel, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DSPARK_E_HIP;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return DSPARK_OK;
+  std::lock_guard<std::mutex> lk(g_attr_mu);
+  if (done.load(std::memory_order_relaxed) & bit) return DSPARK_OK;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return DSPARK_E_HIP;
+  }
+  done.fetch_or(bit, std::memory_order_release);
+  return DSPARK_OK;
+}
+
 }  // namespace dspark
 
 using namespace dspark;
 
 extern "C" dspark_status dspark_profile_start(int max_launches) {
   if (max_launches < 1 || max_launches > (1 << 16)) return DSPARK_E_VALUE;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on.store(false, std::memory_order_relaxed);
+  prof_release_events();
   const size_t need = 2 * (size_t)max_launches;
   while (g_prof_ev.size() < need) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return DSPARK_E_HIP;
+    if (hipEventCreate(&e) != hipSuccess) {
+      prof_release_events();
+      return DSPARK_E_HIP;
+    }
     g_prof_ev.push_back(e);
   }
   g_prof_n = 0;
   g_prof_positions = 0;
-  g_prof_on = true;
+  g_prof_on.store(true, std::memory_order_relaxed);
   return DSPARK_OK;
 }
 
 extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches,
                                            double* positions_per_launch) {
   if (!mean_ms || !launches || !positions_per_launch) return DSPARK_E_NULL;
-  g_prof_on = false;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on.store(false, std::memory_order_relaxed);
   const int pairs = g_prof_n / 2;
   double total = 0.0;
-  for (int i = 0; i < pairs; ++i) {
+  dspark_status rc = DSPARK_OK;
+  for (int i = 0; i < pairs && rc == DSPARK_OK; ++i) {
     float ms = 0.f;
     if (hipEventSynchronize(g_prof_ev[2 * i + 1]) != hipSuccess ||
         hipEventElapsedTime(&ms, g_prof_ev[2 * i], g_prof_ev[2 * i + 1]) != hipSuccess)
-      return DSPARK_E_HIP;
+      rc = DSPARK_E_HIP;
     total += ms;
   }
-  *launches = pairs;
-  *mean_ms = pairs ? total / pairs : 0.0;
-  *positions_per_launch = pairs ? (double)g_prof_positions / pairs : 0.0;
+  if (rc == DSPARK_OK) {
+    *launches = pairs;
+    *mean_ms = pairs ? total / pairs : 0.0;
+    *positions_per_launch = pairs ? (double)g_prof_positions / pairs : 0.0;
+  }
+  // every recorded event has completed (or the device failed): none outlives the loop
+  prof_release_events();
   g_prof_n = 0;
   g_prof_positions = 0;
-  return DSPARK_OK;
+  return rc;
 }
 
 extern "C" size_t dspark_workspace_bytes(int op, const dspark_dims* d) {
@@ -120,6 +178,14 @@ extern "C" dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(k_rng_uniforms, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (uint32_t)seed, (uint32_t)(seed >> 32), b, k, s, v0, n, out);
+  return launch_status();
+}
+
+extern "C" dspark_status dspark_gumbel_lattice(int form, float* out, void* stream) {
+  if (!out) return DSPARK_E_NULL;
+  if (form != 0 && form != 1) return DSPARK_E_VALUE;
+  hipLaunchKernelGGL(k_gumbel_lattice, dim3((1u << 23) / 256), dim3(256), 0,
+                     (hipStream_t)stream, form, out);
   return launch_status();
 }
 

@@ -234,6 +234,7 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
   draft_ws(dm, plan.nslices, &best, &part, ws);
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  if (plan.mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
   hipLaunchKernelGGL(k_fill_u64, dim3(std::min(1024, (G * B + 255) / 256)), dim3(256), 0, st,
                      best, (size_t)G * B, 0ull);
@@ -250,8 +251,9 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
       a.B = B; a.G = G; a.V = V; a.r = r; a.k = k; a.invT = invT; a.key0 = key0; a.key1 = key1;
       a.ncols = B;
       prof_begin(st);
-      if (launch_mfma_bias(a, plan.nslices, st) != DSPARK_OK) return DSPARK_E_HIP;
-      prof_end(st, 1);
+      const dspark_status ls = launch_mfma_bias(a, plan.nslices, st);
+      prof_end(st, ls == DSPARK_OK ? 1 : -1);
+      if (ls != DSPARK_OK) return DSPARK_E_HIP;
     } else {
       prof_begin(st);
       const size_t sh = sizeof(float) * (r + 256 + 16);

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dspark.h"
 
 namespace dspark {
@@ -56,6 +58,27 @@ inline int mfma_workgroups(int V) {
 // (a negative count withdraws a begin whose launch was refused).
 void prof_begin(hipStream_t st);
 void prof_end(hipStream_t st, int positions);
+
+// A kernel's dynamic-LDS limit raised to `bytes`, once per device (devices 0..63), safe to
+// call from several host threads: the first caller on a device sets the attribute under a
+// library-wide lock (api.hip), later calls read one atomic word.
+struct LdsAttr {
+  std::atomic<uint64_t> done{0};
+  dspark_status ensure(const void* kernel, int bytes);
+};
+
+// Every matrix-core kernel variant's LDS attribute set on the current device.  The entry
+// points that may launch one call it after validating their arguments and before their
+// first launch, so a refusal returns before anything is enqueued.
+dspark_status mfma_prepare();
+dspark_status draft16_prepare();
+dspark_status sched_prepare();
+
+// Top-K admission (the scheduler's production form) whose K is read on the device:
+// n_hist[0] - B, n_hist being the N of a greedy schedule made earlier on the stream.
+dspark_status schedule_topk_from_history(int B, int G, const float* c, const double* sps,
+                                         const int32_t* n_hist, int32_t* ell, double* theta,
+                                         int32_t* n_total, hipStream_t st);
 
 inline dspark_status launch_status() {
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_E_HIP;

@@ -3,6 +3,9 @@
 //   draft      gamma Markov-head positions from anchor_t            [CSDN Eq. 4; XTL §3-4]
 //   confidence c_k = sigmoid(w . [h_k ; W1[x_{k-1}]])               [CSDN Eq. 7; XTL §5]
 //   schedule   greedy prefix scheduler (or full block)              [XTL §6]
+//              or its production form: top-K admission over the round's own confidences
+//              with K = N - B of the greedy schedule made two rounds earlier, the greedy
+//              schedule itself in rounds 0 and 1                     [XTL §7]
 //   target     stand-in logits of positions 1..gamma+1 given the drafted block
 //   verify     rejection sampling, residual or bonus token          [XTL §1; AIMSG 2]
 //   anchor_{t+1} = the last token the round emitted (the corrected or bonus token),
@@ -91,6 +94,9 @@ struct LoopWs {
   float* lse;
   int32_t* anc;
   double* theta;
+  int32_t* ell_g;     // delayed top-K: the round's greedy schedule (its N is kept)
+  double* theta_g;
+  int32_t* n_greedy;  // N of the greedy schedules of the last three rounds (ring)
   void* op;
   size_t op_bytes;
   size_t bytes;
@@ -105,6 +111,9 @@ LoopWs loop_ws(const dspark_dims* d, void* base) {
   w.lse = c.take<float>(B * G);
   w.anc = c.take<int32_t>(B);
   w.theta = c.take<double>(1);
+  w.ell_g = c.take<int32_t>(B);
+  w.theta_g = c.take<double>(1);
+  w.n_greedy = c.take<int32_t>(3);
   w.op_bytes = std::max(dspark_draft_workspace(d), dspark_verify_workspace(d));
   w.op = c.take<unsigned char>(w.op_bytes);
   w.bytes = align_up(c.off, 256);
@@ -129,13 +138,17 @@ extern "C" dspark_status dspark_closed_loop(
       !n_total || !n_accept || !out_tokens)
     return DSPARK_E_NULL;
   if (!dims_ok(dims) || rounds < 1 || rounds > 65536) return DSPARK_E_SHAPE;
+  if ((long long)dims->batch * dims->gamma > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (!dtype_ok(wdt) || !dtype_ok(hdt) || !dtype_ok(wvdt)) return DSPARK_E_DTYPE;
   if (!temp_ok(temperature) || !std::isfinite(target_sigma) || target_sigma < 0.f ||
-      (sched_mode != DSPARK_SCHED_GREEDY && sched_mode != DSPARK_SCHED_FULL))
+      (sched_mode != DSPARK_SCHED_GREEDY && sched_mode != DSPARK_SCHED_FULL &&
+       sched_mode != DSPARK_SCHED_TOPK_DELAYED))
     return DSPARK_E_VALUE;
   const LoopWs need = loop_ws(dims, nullptr);
   if (!ws || ws_bytes < need.bytes) return DSPARK_E_WORKSPACE;
   const LoopWs lw = loop_ws(dims, ws);
+  // every kernel attribute the rounds need, before the first launch
+  if (mfma_prepare() != DSPARK_OK || sched_prepare() != DSPARK_OK) return DSPARK_E_HIP;
   hipStream_t st = (hipStream_t)stream;
   const int B = dims->batch, G = dims->gamma, V = dims->vocab;
   const size_t BG = (size_t)B * G, BG1 = (size_t)B * (G + 1);
@@ -162,8 +175,19 @@ extern "C" dspark_status dspark_closed_loop(
     if (s != DSPARK_OK) return s;
     s = dspark_confidence(dims, h, hdt, W1, wdt, w, wvdt, anc_t, tok_t, c_t, stream);
     if (s != DSPARK_OK) return s;
-    s = dspark_schedule(B, G, c_t, sps, sched_mode, ell_t, theta ? theta + t : lw.theta,
-                        n_total + t, nullptr, 0, stream);
+    double* theta_t = theta ? theta + t : lw.theta;
+    if (sched_mode == DSPARK_SCHED_TOPK_DELAYED) {
+      // the greedy schedule of this round, kept for round t + 2; the admission takes K from
+      // round t - 2's (from this round's own in rounds 0 and 1, which reproduces it)
+      s = dspark_schedule(B, G, c_t, sps, DSPARK_SCHED_GREEDY, lw.ell_g, lw.theta_g,
+                          lw.n_greedy + t % 3, nullptr, 0, stream);
+      if (s != DSPARK_OK) return s;
+      s = schedule_topk_from_history(B, G, c_t, sps, lw.n_greedy + (t >= 2 ? t - 2 : t) % 3,
+                                     ell_t, theta_t, n_total + t, st);
+    } else {
+      s = dspark_schedule(B, G, c_t, sps, sched_mode, ell_t, theta_t, n_total + t, nullptr, 0,
+                          stream);
+    }
     if (s != DSPARK_OK) return s;
     if (vec_target)
       hipLaunchKernelGGL(k_markov_target<true>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0, st,

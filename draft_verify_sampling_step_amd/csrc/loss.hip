@@ -36,6 +36,8 @@
 //     stream stops, and the loss is written as NaN.
 // HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 48 bytes of
 // published partials per chunk and row (cleared before the launch).
+#include <atomic>
+
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_common.h"
@@ -610,23 +612,23 @@ bool loss_shape_ok(int B, int G, int V) {
 // is unavailable), looked up once per device.
 constexpr int kMaxDevices = 64;
 
+// Each entry is the capacity + 1 once known (0 = not looked up yet); a racing second lookup
+// computes and stores the same value.
 template <bool VEC>
 int loss_capacity() {
-  static int cap[kMaxDevices];
-  static bool known[kMaxDevices];
+  static std::atomic<int> cap1[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  if (!known[dev]) {
-    int coop = 0, ncu = 0, per_cu = 0;
-    cap[dev] = 0;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_draft_loss<VEC>,
-                                                     kLossThreads, 0) == hipSuccess && coop)
-      cap[dev] = per_cu * ncu;
-    known[dev] = true;
-  }
-  return cap[dev];
+  const int known = cap1[dev].load(std::memory_order_acquire);
+  if (known > 0) return known - 1;
+  int coop = 0, ncu = 0, per_cu = 0, cap = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_draft_loss<VEC>,
+                                                   kLossThreads, 0) == hipSuccess && coop)
+    cap = per_cu * ncu;
+  cap1[dev].store(cap + 1, std::memory_order_release);
+  return cap;
 }
 
 }  // namespace

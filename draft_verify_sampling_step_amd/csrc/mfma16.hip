@@ -344,18 +344,23 @@ __global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
 }
 
 template <int NW, bool TV = false>
+static dspark_status attr16() {
+  static LdsAttr attr;
+  return attr.ensure((const void*)k_draft16<NW, TV>, (int)Shape16<NW, TV>::kLds);
+}
+
+template <int NW, bool TV = false>
 static dspark_status launch16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
   using S = Shape16<NW, TV>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_draft16<NW, TV>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::kLds) !=
-        hipSuccess)
-      return DSPARK_E_HIP;
-    attr_set = true;
-  }
+  if (attr16<NW, TV>() != DSPARK_OK) return DSPARK_E_HIP;
   hipLaunchKernelGGL((k_draft16<NW, TV>), dim3(nwg), dim3(S::NT), S::kLds, st, a);
   return launch_status();
+}
+
+dspark_status draft16_prepare() {
+  if (attr16<8>() != DSPARK_OK || attr16<16>() != DSPARK_OK || attr16<8, true>() != DSPARK_OK)
+    return DSPARK_E_HIP;
+  return DSPARK_OK;
 }
 
 bool draft16_supported(const MfmaBiasArgs& a) {

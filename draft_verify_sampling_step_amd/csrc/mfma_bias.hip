@@ -472,18 +472,28 @@ k_mfma_bias(const MfmaBiasArgs a) {
 }
 
 template <int NCB, int MODE, bool VEC4>
+static dspark_status attr_v() {
+  static LdsAttr attr;
+  return attr.ensure((const void*)k_mfma_bias<NCB, MODE, VEC4>, (int)Shape<NCB, MODE>::kLds);
+}
+
+template <int NCB, int MODE, bool VEC4>
 static dspark_status launch_v(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
   using S = Shape<NCB, MODE>;
-  const size_t sh = S::kLds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_mfma_bias<NCB, MODE, VEC4>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh) != hipSuccess)
-      return DSPARK_E_HIP;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((k_mfma_bias<NCB, MODE, VEC4>), dim3(nwg), dim3(S::NT), sh, st, a);
+  if (attr_v<NCB, MODE, VEC4>() != DSPARK_OK) return DSPARK_E_HIP;
+  hipLaunchKernelGGL((k_mfma_bias<NCB, MODE, VEC4>), dim3(nwg), dim3(S::NT), S::kLds, st, a);
   return launch_status();
+}
+
+template <int MODE>
+static dspark_status attr_mode() {
+  const dspark_status r[] = {attr_v<1, MODE, true>(), attr_v<1, MODE, false>(),
+                             attr_v<2, MODE, true>(), attr_v<2, MODE, false>(),
+                             attr_v<4, MODE, true>(), attr_v<4, MODE, false>(),
+                             attr_v<8, MODE, true>(), attr_v<8, MODE, false>()};
+  for (dspark_status x : r)
+    if (x != DSPARK_OK) return x;
+  return DSPARK_OK;
 }
 
 template <int NCB, int MODE>
@@ -508,6 +518,13 @@ int mfma_grid(int V, int ncols, int mode) {
   const int ncb = (std::min(ncols, 256) + 31) / 32;
   const int per_cu = (ncb == 2 || (ncb > 2 && ncb <= 4)) ? 2 : 1;
   return std::max(1, std::min(ntiles, per_cu * 256));
+}
+
+dspark_status mfma_prepare() {
+  if (attr_mode<kModeDraft>() != DSPARK_OK || attr_mode<kModeResid>() != DSPARK_OK ||
+      attr_mode<kModeTV>() != DSPARK_OK || draft16_prepare() != DSPARK_OK)
+    return DSPARK_E_HIP;
+  return DSPARK_OK;
 }
 
 dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st) {

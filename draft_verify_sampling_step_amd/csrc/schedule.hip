@@ -49,15 +49,19 @@ constexpr int kSchedTopK = 2;
 // SPS entries B..B+kSpsWin staged in LDS for the walk (the walk usually stops early)
 constexpr int kSpsWin = 512;
 
+// In top-K mode with n_hist not NULL, k_admit is read on the device: n_hist[0] - B,
+// clamped into [0, B * G] (n_hist is the N of a schedule made earlier on the stream).
 __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
                                                    const double* __restrict__ sps, int B,
                                                    int G, int mode, int k_admit,
+                                                   const int32_t* __restrict__ n_hist,
                                                    int32_t* __restrict__ ell,
                                                    double* __restrict__ theta,
                                                    int32_t* __restrict__ n_total) {
 #pragma clang fp contract(off)
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, n = B * G;
+  if (mode == kSchedTopK && n_hist) k_admit = min(max(n_hist[0] - B, 0), n);
   double* XA = reinterpret_cast<double*>(smem);   // a: [n], then [n] for the other buffer
   double* YA = XA + n;
   uint32_t* XI = reinterpret_cast<uint32_t*>(YA + n);   // index: [n], then [n]
@@ -221,19 +225,27 @@ __global__ __launch_bounds__(1024) void k_schedule(const float* __restrict__ c,
 
 using namespace dspark;
 
-namespace {
-// the kernel's dynamic LDS may exceed the default limit: raise it once
-dspark_status set_sched_attr() {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)k_schedule, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((size_t)kMaxSchedCandidates * kSchedBytesPer)) != hipSuccess)
-      return DSPARK_E_HIP;
-    attr_set = true;
-  }
-  return DSPARK_OK;
+namespace dspark {
+
+// the kernel's dynamic LDS may exceed the default limit: raise it once per device
+dspark_status sched_prepare() {
+  static LdsAttr attr;
+  return attr.ensure((const void*)k_schedule,
+                     (int)((size_t)kMaxSchedCandidates * kSchedBytesPer));
 }
-}  // namespace
+
+dspark_status schedule_topk_from_history(int B, int G, const float* c, const double* sps,
+                                         const int32_t* n_hist, int32_t* ell, double* theta,
+                                         int32_t* n_total, hipStream_t st) {
+  if (!c || !sps || !n_hist || !ell || !theta || !n_total) return DSPARK_E_NULL;
+  if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
+  if (sched_prepare() != DSPARK_OK) return DSPARK_E_HIP;
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), (size_t)B * G * kSchedBytesPer, st, c,
+                     sps, B, G, kSchedTopK, 0, n_hist, ell, theta, n_total);
+  return launch_status();
+}
+
+}  // namespace dspark
 
 extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, const double* sps,
                                          int mode, int32_t* ell, double* theta,
@@ -245,10 +257,10 @@ extern "C" dspark_status dspark_schedule(int32_t B, int32_t G, const float* c, c
   if (B < 1 || G < 1 || G > 64 || (long long)B * G > kMaxSchedCandidates) return DSPARK_E_SHAPE;
   if (mode != DSPARK_SCHED_GREEDY && mode != DSPARK_SCHED_FULL) return DSPARK_E_VALUE;
   const size_t sh = (size_t)B * G * kSchedBytesPer;
-  if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
+  if (sched_prepare() != DSPARK_OK) return DSPARK_E_HIP;
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, 0, ell,
-                     theta, n_total);
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, st, c, sps, B, G, mode, 0, nullptr,
+                     ell, theta, n_total);
   return launch_status();
 }
 
@@ -263,8 +275,8 @@ extern "C" dspark_status dspark_schedule_topk(int32_t B, int32_t G, const float*
   if (k_admit < 0) return DSPARK_E_VALUE;
   const int k = (long long)k_admit > (long long)B * G ? B * G : k_admit;
   const size_t sh = (size_t)B * G * kSchedBytesPer;
-  if (set_sched_attr() != DSPARK_OK) return DSPARK_E_HIP;
+  if (sched_prepare() != DSPARK_OK) return DSPARK_E_HIP;
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), sh, (hipStream_t)stream, c, sps, B, G,
-                     kSchedTopK, k, ell, theta, n_total);
+                     kSchedTopK, k, nullptr, ell, theta, n_total);
   return launch_status();
 }

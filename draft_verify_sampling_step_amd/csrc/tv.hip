@@ -194,6 +194,7 @@ extern "C" dspark_status dspark_accept_rate_tv(const dspark_dims* dm, const floa
   const int nsum = tv_sum_slices(dm, mfma);
   TvWs w = tv_ws(dm, rs.count, nsum, ws);
   const float invT = 1.0f / temperature;
+  if (mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
   hipLaunchKernelGGL(k_tv_rows, dim3(rs.count, B, G), dim3(256), 0, st, T, B, G, V, rs.len,
                      rs.count, invT, w.part);

@@ -563,6 +563,7 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   VerifyWs w = verify_ws(dm, nsl, nres, ws);
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  if (mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
   hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
                      w.counts, w.bonus);

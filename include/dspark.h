@@ -72,7 +72,10 @@ typedef enum {
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
-typedef enum { DSPARK_SCHED_GREEDY = 0, DSPARK_SCHED_FULL = 1 } dspark_sched_mode;
+/* GREEDY and FULL: see dspark_schedule.  TOPK_DELAYED: dspark_closed_loop only (see there). */
+typedef enum {
+    DSPARK_SCHED_GREEDY = 0, DSPARK_SCHED_FULL = 1, DSPARK_SCHED_TOPK_DELAYED = 2
+} dspark_sched_mode;
 
 typedef enum {
     DSPARK_OP_DRAFT = 0, DSPARK_OP_CONFIDENCE = 1, DSPARK_OP_SCHEDULE = 2,
@@ -188,7 +191,7 @@ dspark_status dspark_sts_calibrate(int32_t n, int32_t gamma, const float* logit,
  * GREEDY: candidates (b, j) ordered by a descending, then b ascending, then j ascending,
  * are admitted one at a time from ell = 0 (tau = B, N = B), tau and Theta updated in fp64
  * in that order; the walk stops at the first candidate whose Theta <= the best Theta so
- * far.  FULL: every candidate is admitted (ell_b = gamma).
+ * far.  FULL: every candidate is admitted (ell_b = gamma).  Other modes: DSPARK_E_VALUE.
  *   c      [B][gamma] fp32 confidences in [0, 1] (sigmoid outputs).  Values above 1 are
  *          not rejected: the order and the walk are still exact, but a can then grow
  *          along a request, and ell_b is the largest admitted j, which need not be a
@@ -268,7 +271,14 @@ dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, con
  * Round t (0-based) drafts from anchor_t (anchor_0 = anchor, later the last token the
  * previous round emitted), scores the block with the confidence head, schedules it
  * (sched_mode as for dspark_schedule), builds the stand-in target logits and verifies,
- * each call as documented above with seed_t = seed + t.  The accepted length of request b
+ * each call as documented above with seed_t = seed + t.  sched_mode GREEDY or FULL schedules
+ * every round with dspark_schedule; TOPK_DELAYED is the production form of [XTL §7]: round
+ * t admits the first K_t candidates in dspark_schedule's order of its own confidences
+ * (dspark_schedule_topk), where K_t = N - B of the greedy schedule of round t - 2's
+ * confidences, read on the device, so the admitted count of a round is known two rounds
+ * ahead and depends on history only; rounds 0 and 1, which have no such history, take
+ * K from their own greedy schedule, i.e. are scheduled greedily.  ell, theta and n_total
+ * report the admission made.  The accepted length of request b
  * in round t is n_accept + 1 tokens; the latency per token of the speculative loop is
  * (T_draft + T_verify) / tau [CSDN Eq. 1].
  * Stand-in target (a synthetic Markov chain over tokens, not part of the method): position
@@ -282,7 +292,8 @@ dspark_status dspark_accept_rate_tv(const dspark_dims* dims, const float* U, con
  *   anchors [R][B] (or NULL), tokens [R][B][gamma], c [R][B][gamma], ell [R][B],
  *   theta [R] (or NULL), n_total [R], n_accept [R][B], out_tokens [R][B][gamma+1],
  *   pt_tok [R][B][gamma] (or NULL).
- * rounds in 1..65536.  Workspace: dspark_loop_workspace_bytes(dims) bytes (it holds one
+ * rounds in 1..65536; B * gamma <= 4096 (the scheduler's limit), else DSPARK_E_SHAPE before
+ * anything is enqueued.  Workspace: dspark_loop_workspace_bytes(dims) bytes (it holds one
  * round's target logits, B (gamma+1) V floats).
  */
 size_t dspark_loop_workspace_bytes(const dspark_dims* dims);
@@ -340,6 +351,21 @@ dspark_status dspark_draft_loss(int32_t batch, int32_t gamma, int32_t vocab, con
  */
 dspark_status dspark_rng_uniforms(uint64_t seed, uint32_t b, uint32_t k, uint32_t s,
                                   uint32_t v0, int64_t n, float* out, void* stream);
+
+/*
+ * The Gumbel transform of the random-number definition above, as the kernels evaluate it
+ * in fp32, on the whole lattice of uniforms (for checking it exhaustively):
+ *   out[m], m = 0 .. 2^23 - 1 (out holds 2^23 floats), for u = (2m + 1) * 2^-24;
+ *   form 0: G = -ln(-ln u), the form of the row kernels;
+ *   form 1: -log2(-log2 u), the base-2 score offset of the matrix-core kernels (it equals
+ *           G / ln 2 - log2(ln 2); the constant shifts every candidate of a race alike).
+ * Both use the hardware base-2 logarithm.  Measured against fp64 on every lattice point,
+ * the error is within 3 * 2^-23 * (1 + |value|) (ULP-scale: about 3.6e-7 absolute near 0
+ * and 2.2e-5 relative to |value| ~ 17 at u -> 1) -- far inside the 1e-4 score gap below
+ * which a sampled token may differ from an exact sampler's.
+ * Errors: DSPARK_E_NULL, DSPARK_E_VALUE (form not 0 or 1), DSPARK_E_HIP.
+ */
+dspark_status dspark_gumbel_lattice(int form, float* out, void* stream);
 
 /*
  * Launch timing (measurement support, not part of the method).  Between

@@ -134,6 +134,10 @@ def test_closed_loop_validation():
     assert call(sigma=float("nan")) == 4
     assert call(temp=0.0) == 4
     assert call(mode=7) == 4
+    assert call(mode=-1) == 4
+    # the scheduler's candidate limit is checked before anything is enqueued
+    big = _dims(B=128, G=64)
+    assert call(dims=ctypes.byref(big), wsb=1 << 40) == 2
     need = L.dspark_loop_workspace_bytes(ctypes.byref(dm))
     assert need >= dm.batch * (dm.gamma + 1) * dm.vocab * 4
     assert call(wsb=need - 1) == 5
@@ -173,6 +177,13 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(ds, "LIB_PATH", "/nonexistent/libdspark.so")
     with pytest.raises(RuntimeError, match="missing"):
         ds.lib()
+
+
+def test_gumbel_lattice_validation():
+    L = ds.lib()
+    assert L.dspark_gumbel_lattice(0, None, None) == 1
+    assert L.dspark_gumbel_lattice(2, P, None) == 4
+    assert L.dspark_gumbel_lattice(-1, P, None) == 4
 
 
 def test_profile_switch_validation():
