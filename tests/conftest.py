@@ -26,3 +26,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Report the near-tie tally of the GPU parity tests (sampled tokens and accept
+    decisions compared with the oracle; flagged = inside the near-tie threshold; excused =
+    flagged and decided otherwise by the GPU)."""
+    mod = sys.modules.get("gpu_round")
+    if mod is None:
+        return
+    t = mod.TALLY
+    if not (t["samples"] or t["accept_tests"]):
+        return
+    rate = t["flagged"] / t["samples"] if t["samples"] else 0.0
+    terminalreporter.write_line(
+        f"NEAR-TIE TALLY: {t['samples']} sampled tokens compared, {t['flagged']} flagged "
+        f"(oracle top-2 gap < 1e-4; rate {rate:.2e}), {t['excused']} excused mismatches; "
+        f"{t['accept_tests']} accept decisions, {t['accept_flagged']} flagged (margin < 1e-5), "
+        f"{t['accept_excused']} excused")

@@ -42,7 +42,28 @@ LOOPS = {
     "bf16_b40": (workload.custom(name="loopbf16", B=40, gamma=8, V=8192, r=256, d=256,
                                  bf16=True, logits="zipf", sigma0=0.3, sigma1=0.05,
                                  table="serve"), 4, 0.7),
+    # the production scheduler: top-K admission with K from the greedy schedule of two
+    # rounds earlier (greedy in rounds 0 and 1)
+    "tiny_topk_delayed": (workload.custom(name="looptopk", B=4, gamma=4, V=1024, r=16, d=64,
+                                          sched_mode=ds.SCHED_TOPK_DELAYED), 7, 0.5),
+    "bf16_b40_topk_delayed": (workload.custom(name="loopbf16k", B=40, gamma=8, V=8192, r=256,
+                                              d=256, bf16=True, logits="zipf", sigma0=0.3,
+                                              sigma1=0.05, table="serve",
+                                              sched_mode=ds.SCHED_TOPK_DELAYED), 6, 0.7),
 }
+
+
+def _oracle_schedule(cfg, c_rounds, t, sps):
+    """The oracle's schedule of round t: greedy or full block, or in the delayed top-K
+    mode the first K candidates of round t's order with K = N - B of the greedy schedule
+    of round t - 2 (of round t itself in rounds 0 and 1).  Returns (ell, theta, N, K or
+    None, own greedy N)."""
+    if cfg.sched_mode != ds.SCHED_TOPK_DELAYED:
+        return oracle.schedule(c_rounds[t], sps, cfg.sched_mode) + (None, None)
+    n_own = oracle.schedule(c_rounds[t], sps, 0)[2]
+    n_hist = oracle.schedule(c_rounds[t - 2], sps, 0)[2] if t >= 2 else n_own
+    K = n_hist - cfg.B
+    return oracle.schedule_topk(c_rounds[t], sps, K) + (K, n_own)
 
 
 @pytest.mark.parametrize("name", list(LOOPS))
@@ -57,6 +78,7 @@ def test_closed_loop_matches_oracle_round_by_round(name):
     G = cfg.gamma
     assert np.array_equal(o["anchors"][0], inp.anchor)
     taus = []
+    delayed = []
     for t in range(rounds):
         anchor_t = o["anchors"][t]
         if t > 0:
@@ -74,15 +96,22 @@ def test_closed_loop_matches_oracle_round_by_round(name):
         # the rest of the round on the GPU's own block
         c_o = oracle.confidence(inp.h, inp.W1, inp.w, anchor_t, tok_g)
         assert_rel(o["c"][t], c_o, f"round {t} confidence")
-        ell_o, th_o, n_o = oracle.schedule(o["c"][t], inp.sps, cfg.sched_mode)
+        ell_o, th_o, n_o, K, n_own = _oracle_schedule(cfg, o["c"], t, inp.sps)
         assert np.array_equal(o["ell"][t], ell_o), f"round {t}: ell"
         assert o["theta"][t] == th_o and o["n_total"][t] == n_o
+        if K is not None:
+            delayed.append((t, K, n_own - cfg.B))
         T_o = oracle.markov_target(inp.U, anchor_t, tok_g, sigma, tseed)
         inp_t = dataclasses.replace(inp, anchor=anchor_t.astype(np.int32), seed=seed_t)
         check_verify(inp_t, tok_g, T_o, o["ell"][t], o["n_accept"][t], o["out_tokens"][t],
                      o["pt_tok"][t])
         taus.append(float((o["n_accept"][t] + 1).mean()))
     _flush(f"closed loop {name}: tau per round {np.round(taus, 3).tolist()}")
+    if cfg.sched_mode == ds.SCHED_TOPK_DELAYED:
+        # (round, K admitted, K its own greedy schedule would have admitted)
+        _flush(f"closed loop {name}: delayed K per round {delayed}")
+        assert any(k != own for t, k, own in delayed if t >= 2), \
+            "the delayed K never differed from the round's own: the delay went untested"
     # acceptance falls below one when the target adds a transition term the draft lacks
     assert np.mean(taus) < 1 + G
 

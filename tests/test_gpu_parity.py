@@ -1,8 +1,12 @@
 """GPU parity: the HIP library against the fp64 oracle on seeded inputs.
 
-Small shapes compare every output element; the five workload configurations at full size
-run in the benchmark's launch configuration and compare sampled requests (the oracle
-computes them one by one).  See tests/gpu_round.py for the protocol and tolerances.
+Small shapes compare every output element.  The multi-tile shapes do the same at
+V = 131072, where every matrix-core workgroup streams 8 or 16 vocabulary tiles, so the
+steady state of the tile pipeline (its prefetch ring, waits and register rotation) is
+compared element by element, with weights large enough (s.d. 0.5, a bias of s.d. about 4)
+that a stale tile would move the normaliser and the tokens.  The workload configurations
+at full size run in the benchmark's launch configuration and compare every request (the
+oracle runs on a thread pool).  See tests/gpu_round.py for the protocol and tolerances.
 """
 import numpy as np
 import pytest
@@ -12,7 +16,7 @@ import draft_verify_sampling_step_amd as ds
 import oracle
 import workload
 from gpu_round import (TALLY, DeviceInputs, assert_abs, assert_rel, check_verify,
-                       compare_tokens, dev, host)
+                       compare_tokens, dev, host, par_accept_tv, par_draft)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +42,28 @@ def test_rng_bit_exact(seed, b, k, s, v0, n):
     assert np.array_equal(g, o)
 
 
+@pytest.mark.parametrize("form", [0, 1])
+def test_gumbel_transform_on_the_whole_lattice(form):
+    """The kernels' fp32 Gumbel transform on all 2^23 uniforms u = (2m + 1) 2^-24 against
+    fp64: within 3 * 2^-23 * (1 + |value|) everywhere, including u -> 1 where the largest
+    scores (the winners of the races) come from.  Form 0 is -ln(-ln u) (row kernels),
+    form 1 is -log2(-log2 u) (matrix-core kernels)."""
+    g = host(ds.dspark_gumbel_lattice(form)).astype(np.float64)
+    m = np.arange(1 << 23, dtype=np.float64)
+    u = (2.0 * m + 1.0) * 2.0 ** -24
+    e = -np.log1p(u - 1.0)                       # -ln u, exact argument (u - 1 is exact)
+    exact = -np.log(e) if form == 0 else -np.log2(e / np.log(2.0))
+    err = np.abs(g - exact)
+    ratio = err / (3 * 2.0 ** -23 * (1.0 + np.abs(exact)))
+    i = int(np.argmax(ratio))
+    tail = err[-(1 << 16):]                      # the u closest to 1
+    _flush(f"gumbel form {form}: max abs err {err.max():.3e}, max err/bound {ratio.max():.3f} "
+           f"at u={u[i]!r} (value {exact[i]:.6f}); max abs err over the top 2^16 u "
+           f"{tail.max():.3e}")
+    assert np.all(np.isfinite(g))
+    assert ratio.max() <= 1.0, (err[i], exact[i], u[i])
+
+
 # ------------------------------------------------------------------------------------
 # whole round, every element, small shapes
 # ------------------------------------------------------------------------------------
@@ -46,7 +72,7 @@ def run_round_parity(cfg, seed=0, extra_ells=True):
     inp = workload.generate(cfg, seed)
     D = DeviceInputs(inp)
     temp = cfg.temperature
-    od = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, temp, inp.seed)
+    od = par_draft(inp)
     tok_o = od["tokens"]
     forced = dev(tok_o)
     tg, lg, sg = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, temp, inp.seed,
@@ -89,7 +115,7 @@ def run_round_parity(cfg, seed=0, extra_ells=True):
         check_verify(inp, tok_o, T, ell, host(n_g), host(out_g), host(pt_g))
 
     if cfg.tv:
-        a_o, l1 = oracle.accept_tv(inp.U, inp.W1, inp.W2t, inp.anchor, tok_o, T, temp)
+        a_o, l1 = par_accept_tv(inp, tok_o, T)
         a_g = host(ds.dspark_accept_rate_tv(D.U, D.W1, D.W2t, D.anchor, forced, sg, Td, temp))
         assert_rel(a_g, a_o, "TV accept rate")
     torch.cuda.synchronize()
@@ -135,19 +161,51 @@ def test_round_parity_second_seed():
     run_round_parity(SMALL["mfma_b40_ragged"], seed=11, extra_ells=False)
 
 
-@pytest.mark.parametrize("nrej", [0, 1, 2, 3, 5, 40])
-def test_residual_pass_by_rejection_count(nrej):
+# V = 131072 is 4096 tiles of 32 rows: 8 tiles per workgroup for 33-128 columns (512
+# workgroups), 16 for 32 or more than 128 columns (256 workgroups).
+MULTI_TILE = {
+    # 16-column draft kernel, 8-wave workgroups; TV over 192 columns (two launches)
+    "mt_b64_g3": workload.custom(name="mt_b64_g3", B=64, gamma=3, V=131072, r=256, d=64,
+                                 bf16=True, wsigma=0.5, logits="zipf", sigma_mix=True,
+                                 table="serve"),
+    # 16-column draft kernel, 16-wave workgroups; TV over 400 columns (the last 16 on the
+    # 32-column kernel)
+    "mt_b200_g2_t07": workload.custom(name="mt_b200_g2_t07", B=200, gamma=2, V=131072, r=256,
+                                      d=48, bf16=True, wsigma=0.5, temperature=0.7,
+                                      table="serve15"),
+    # 32-column kernel (one column block), V % 4 != 0: scalar logit loads, ragged last tile
+    "mt_b32_odd": workload.custom(name="mt_b32_odd", B=32, gamma=2, V=131075, r=256, d=64,
+                                  bf16=True, wsigma=0.5, logits="zipf", table="serve"),
+    # 32-column kernel with eight column blocks (more than 128 requests, V % 4 != 0)
+    "mt_b150_odd": workload.custom(name="mt_b150_odd", B=150, gamma=2, V=131073, r=256,
+                                   d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+                                   table="serve"),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(MULTI_TILE))
+def test_round_parity_multi_tile(name):
+    run_round_parity(MULTI_TILE[name], seed=4)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("nrej,V,wsigma", [(0, 4096, 0.1), (1, 4096, 0.1), (2, 4096, 0.1),
+                                           (3, 4096, 0.1), (5, 4096, 0.1), (40, 4096, 0.1),
+                                           (1, 131072, 0.5), (2, 131072, 0.5),
+                                           (5, 131072, 0.5), (40, 131072, 0.5)])
+def test_residual_pass_by_rejection_count(nrej, V, wsigma):
     """Verification with exactly `nrej` requests rejected at their first draft row: 1 or 2
     take the thin residual pass, more the matrix-core pass, and with none neither pass has
     work.  The target rows 1..gamma are the draft logits themselves (every test accepts),
     except that the chosen requests get +40 on one token other than x_1 in row 1, so x_1 is
     rejected there and the residual mass sits on that token."""
-    _flush(f"residual pass with {nrej} rejected requests")
-    cfg = workload.custom(name=f"rej{nrej}", B=96, gamma=3, V=4096, r=256, d=64, bf16=True,
-                          wsigma=0.1, logits="zipf", table="serve")
+    _flush(f"residual pass with {nrej} rejected requests, V={V}")
+    cfg = workload.custom(name=f"rej{nrej}", B=96, gamma=3, V=V, r=256, d=64, bf16=True,
+                          wsigma=wsigma, logits="zipf", table="serve")
     inp = workload.generate(cfg, 5)
     D = DeviceInputs(inp)
-    od = oracle.draft(inp.U, inp.W1, inp.W2t, inp.anchor, 1.0, inp.seed)
+    od = par_draft(inp)
     tok = od["tokens"]
     T = workload.synthesize_target(inp, tok).astype(np.float32)
     W1f, W2f = oracle.widen(inp.W1), oracle.widen(inp.W2t)
@@ -325,68 +383,72 @@ def test_calibrated_confidence_matches_oracle():
 
 
 # ------------------------------------------------------------------------------------
-# full-size workloads, sampled requests
+# full-size workloads, every request
 # ------------------------------------------------------------------------------------
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("name", ["qwen1", "serve128", "v4dspark5", "bigvocab"])
-def test_full_size_sampled(name):
+def test_full_size_all_requests(name):
     cfg = workload.CONFIGS[name]
     _flush(f"full-size {name}: generating inputs")
     inp = workload.generate(cfg, 0)
     D = DeviceInputs(inp)
     temp = cfg.temperature
-    rows = np.unique(np.array([0, cfg.B // 2, cfg.B - 1]))
-    _flush(f"full-size {name}: oracle draft rows {rows.tolist()}")
-    od = oracle.draft(inp.U[rows], inp.W1, inp.W2t, inp.anchor[rows], temp, inp.seed, gid=rows)
-    tok_o = od["tokens"]
 
     # the benchmark's configuration: a free-running draft over the whole batch
     tf, lf, sf = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, temp, inp.seed)
     tf_h = host(tf)
-    for i, b in enumerate(rows):
-        diff = np.nonzero(tf_h[b] != tok_o[i])[0]
+    _flush(f"full-size {name}: oracle draft of all {cfg.B} requests")
+    od = par_draft(inp)
+    tok_o = od["tokens"]
+    for b in range(cfg.B):
+        diff = np.nonzero(tf_h[b] != tok_o[b])[0]
         if diff.size:
-            assert od["gap"][i, diff[0]] < 1e-4, f"row {b} pos {diff[0] + 1}"
+            assert od["gap"][b, diff[0]] < 1e-4, f"row {b} pos {diff[0] + 1}"
 
-    # teacher-forced: sampled rows on the oracle's tokens, others on the GPU's own
-    forced_h = tf_h.copy()
-    forced_h[rows] = tok_o
-    forced = dev(forced_h)
+    # teacher-forced on the oracle's tokens: every position compared
+    forced = dev(tok_o)
     tg, lg, sg = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, temp, inp.seed,
                                         forced=forced)
-    tg_h, lg_h, sg_h = host(tg)[rows], host(lg)[rows], host(sg)[rows]
+    tg_h, lg_h, sg_h = host(tg), host(lg), host(sg)
     mism = compare_tokens(tg_h, tok_o, od["gap"], f"{name} draft tokens")
     assert_abs(sg_h, od["lse"], f"{name} lse", 1e-4)
     assert_rel(np.exp(lg_h.astype(np.float64)), np.exp(od["logp"]), f"{name} p_d(x)",
                mask=~mism)
 
-    c_g = host(ds.dspark_confidence(D.h, D.W1, D.w, D.anchor, forced))[rows]
-    c_o = oracle.confidence(inp.h[rows], inp.W1, inp.w, inp.anchor[rows], tok_o)
+    c_g = host(ds.dspark_confidence(D.h, D.W1, D.w, D.anchor, forced))
+    c_o = oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tok_o)
     assert_rel(c_g, c_o, f"{name} confidence")
 
-    # scheduler at full batch on seeded confidences (identical fp32 input on both sides)
-    rng = np.random.default_rng(cfg.index)
-    logits = rng.normal(0.0, 5.0, size=(cfg.B, cfg.gamma))
-    c_syn = (1.0 / (1.0 + np.exp(-logits))).astype(np.float32)
-    ell_o, th_o, n_o = oracle.schedule(c_syn, inp.sps, cfg.sched_mode)
-    ell_g, th_g, n_g = ds.dspark_schedule(dev(c_syn), D.sps, cfg.sched_mode)
+    # the scheduler at full batch on the round's own GPU confidences (the same fp32 values
+    # on both sides), and on seeded confidences that admit many more tokens
+    ell_o, th_o, n_o = oracle.schedule(c_g, inp.sps, cfg.sched_mode)
+    ell_g, th_g, n_g = ds.dspark_schedule(dev(c_g), D.sps, cfg.sched_mode)
     assert np.array_equal(host(ell_g), ell_o)
     assert host(th_g)[0] == th_o and host(n_g)[0] == n_o
+    rng = np.random.default_rng(cfg.index)
+    c_syn = (1.0 / (1.0 + np.exp(-rng.normal(0.0, 5.0, size=(cfg.B, cfg.gamma))))
+             ).astype(np.float32)
+    ell_s, th_s, n_s = oracle.schedule(c_syn, inp.sps, cfg.sched_mode)
+    ell_sg, th_sg, n_sg = ds.dspark_schedule(dev(c_syn), D.sps, cfg.sched_mode)
+    assert np.array_equal(host(ell_sg), ell_s)
+    assert host(th_sg)[0] == th_s and host(n_sg)[0] == n_s
 
     _flush(f"full-size {name}: target synthesis")
-    T = workload.synthesize_target(inp, forced_h)
+    T = workload.synthesize_target(inp, tok_o)
     Td = dev(T)
-    n_g, out_g, pt_g = ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, forced, lg, sg, Td,
-                                        dev(ell_o), temp, inp.seed)
-    _flush(f"full-size {name}: oracle verify")
-    check_verify(inp, forced_h, T[rows], ell_o, host(n_g), host(out_g), host(pt_g), rows=rows)
+    budgets = [("scheduled", ell_o)]
+    if not np.all(ell_o == cfg.gamma):
+        budgets.append(("full block", np.full(cfg.B, cfg.gamma, np.int32)))
+    for what, ell in budgets:
+        n_v, out_v, pt_v = ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, forced, lg, sg, Td,
+                                            dev(ell), temp, inp.seed)
+        _flush(f"full-size {name}: oracle verify, {what} budget (sum ell {int(ell.sum())})")
+        check_verify(inp, tok_o, T, ell, host(n_v), host(out_v), host(pt_v))
 
     if cfg.tv:
-        _flush(f"full-size {name}: TV")
-        a_g = host(ds.dspark_accept_rate_tv(D.U, D.W1, D.W2t, D.anchor, forced, sg, Td,
-                                            temp))[rows]
-        a_o, _ = oracle.accept_tv(inp.U[rows], inp.W1, inp.W2t, inp.anchor[rows], tok_o,
-                                  T[rows], temp)
+        _flush(f"full-size {name}: TV of all {cfg.B * cfg.gamma} positions")
+        a_g = host(ds.dspark_accept_rate_tv(D.U, D.W1, D.W2t, D.anchor, forced, sg, Td, temp))
+        a_o, _ = par_accept_tv(inp, tok_o, T)
         assert_rel(a_g, a_o, f"{name} TV accept rate")
     torch.cuda.synchronize()
 
@@ -400,9 +462,15 @@ def test_stream_read_probe_times_a_read():
 
 
 def test_zz_near_tie_rate():
-    """Excused near-tie mismatches stay within 0.01% of all compared samples (or at most
-    one when fewer than 10^4 samples were compared)."""
+    """Over every sampled token compared in this session: the GPU's token differs from the
+    oracle's only at flagged near-ties (asserted where each is compared), and the flagged
+    near-ties (oracle top-2 gap below 1e-4) are at most 0.01% of the samples; the same for
+    accept decisions inside the 1e-5 margin.  The counts appear in the terminal summary."""
     _flush(f"tally {TALLY}")
-    assert TALLY["samples"] > 0
-    assert TALLY["excused"] <= max(1, 1e-4 * TALLY["samples"])
-    assert TALLY["accept_excused"] <= max(1, 1e-4 * TALLY["accept_tests"])
+    if TALLY["samples"] < 10000:
+        pytest.skip(f"only {TALLY['samples']} samples compared in this session: too few to "
+                    "resolve a 0.01% rate (the whole GPU suite compares more than 10^4)")
+    assert TALLY["flagged"] <= 1e-4 * TALLY["samples"]
+    assert TALLY["excused"] <= TALLY["flagged"]
+    assert TALLY["accept_flagged"] <= 1e-4 * TALLY["accept_tests"]
+    assert TALLY["accept_excused"] <= TALLY["accept_flagged"]
