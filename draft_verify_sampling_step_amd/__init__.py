@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
             L.dspark_version.restype = _I
             L.dspark_draft_markov.argtypes = [D, _P, _P, _P, _I, _P, _P, _F, _U64, _P, _P, _P,
                                               _P, _SZ, _P]
+            L.dspark_draft_markov_noalloc.argtypes = [D, _P, _P, _P, _I, _P, _P, _F, _U64,
+                                                      _P, _P, _P, _P]
             L.dspark_confidence.argtypes = [D, _P, _I, _P, _I, _P, _I, _P, _P, _P, _P]
             L.dspark_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, _P, _P, _I, _P, _P,
                                           _P, _P, _SZ, _P]
@@ -103,7 +105,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(ctypes.c_double)]
             L.dspark_stream_read_probe.argtypes = [_P, _SZ, _SZ, _I, _P,
                                                    ctypes.POINTER(ctypes.c_double), _P]
-            for fn in ("dspark_draft_markov", "dspark_confidence",
+            for fn in ("dspark_draft_markov", "dspark_draft_markov_noalloc", "dspark_confidence",
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
                        "dspark_draft_loss", "dspark_closed_loop", "dspark_rng_uniforms",
@@ -210,6 +212,33 @@ def dspark_draft_markov(U, W1, W2t, anchor, temperature: float, seed: int, force
                                      _ptr(anchor), _ptr(forced), float(temperature),
                                      int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens), _ptr(logp),
                                      _ptr(lse), _ptr(w), w.numel(), _stream_handle(stream)))
+    return tokens, logp, lse
+
+
+def dspark_draft_markov_noalloc(U, W1, W2t, anchor, temperature: float, seed: int,
+                                forced=None, out=None, stream=None):
+    """dspark_draft_markov with the library's own static scratch (no workspace argument;
+    the C call allocates nothing).  Pass `out` to make the whole call allocation-free."""
+    B, G, V = U.shape
+    r = W1.shape[1]
+    _f32(U, "U")
+    _i32(anchor, "anchor")
+    if forced is not None:
+        _i32(forced, "forced")
+    wdt = _wdtype(W1)
+    if _wdtype(W2t) != wdt:
+        raise ValueError("W1 and W2t must have the same dtype")
+    if out is None:
+        out = (torch.empty((B, G), dtype=torch.int32, device=U.device),
+               torch.empty((B, G), dtype=torch.float32, device=U.device),
+               torch.empty((B, G), dtype=torch.float32, device=U.device))
+    tokens, logp, lse = out
+    dm = Dims(B, G, V, r, 0)
+    _check(lib().dspark_draft_markov_noalloc(ctypes.byref(dm), _ptr(U), _ptr(W1), _ptr(W2t),
+                                             wdt, _ptr(anchor), _ptr(forced),
+                                             float(temperature),
+                                             int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(tokens),
+                                             _ptr(logp), _ptr(lse), _stream_handle(stream)))
     return tokens, logp, lse
 
 

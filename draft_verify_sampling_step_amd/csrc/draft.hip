@@ -12,6 +12,8 @@
 // The next position decodes x_{k-1} from the atomic word.  After the last position one
 // merge kernel reduces the slots in slice order into lse and log p_d(x_k) (the winner's
 // logit is recomputed from U, W1 and W2t).
+#include <mutex>
+
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_bias.h"
@@ -214,21 +216,15 @@ size_t dspark_draft_workspace(const dspark_dims* d) {
   return draft_ws(d, ns, &b, &p, nullptr);
 }
 
-extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float* U,
-                                             const void* W1, const void* W2t, int wdt,
-                                             const int32_t* anchor, const int32_t* forced,
-                                             float temperature, uint64_t seed,
-                                             int32_t* tokens, float* logp, float* lse,
-                                             void* ws, size_t ws_bytes, void* stream) {
-  if (!dm || !U || !W1 || !W2t || !anchor || !tokens || !logp || !lse) return DSPARK_E_NULL;
-  if (!dims_ok(dm)) return DSPARK_E_SHAPE;
-  if (!dtype_ok(wdt)) return DSPARK_E_DTYPE;
-  if (!temp_ok(temperature)) return DSPARK_E_VALUE;
-  const size_t need = dspark_draft_workspace(dm);
-  if (!ws || ws_bytes < need) return DSPARK_E_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+namespace {
+
+// The draft with its scratch (packed winners and softmax partials) at `ws`, which holds at
+// least draft_ws(dm, plan.nslices) bytes; arguments already validated.
+dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const float* U,
+                        const void* W1, const void* W2t, int wdt, const int32_t* anchor,
+                        const int32_t* forced, float temperature, uint64_t seed,
+                        int32_t* tokens, float* logp, float* lse, void* ws, hipStream_t st) {
   const int B = dm->batch, G = dm->gamma, V = dm->vocab, r = dm->rank;
-  const DraftPlan plan = draft_plan(dm, wdt);
   unsigned long long* best;
   float2* part;
   draft_ws(dm, plan.nslices, &best, &part, ws);
@@ -236,6 +232,7 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
   if (plan.mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
+  // the winners start at zero (below every packed candidate) on every call
   hipLaunchKernelGGL(k_fill_u64, dim3(std::min(1024, (G * B + 255) / 256)), dim3(256), 0, st,
                      best, (size_t)G * B, 0ull);
   for (int k = 1; k <= G; ++k) {
@@ -279,4 +276,78 @@ extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float*
                        U, (const float*)W1, (const float*)W2t, anchor, forced, B, G, V, r, invT,
                        plan.nslices, tokens, logp, lse);
   return launch_status();
+}
+
+dspark_status draft_validate(const dspark_dims* dm, const float* U, const void* W1,
+                             const void* W2t, int wdt, const int32_t* anchor, int32_t* tokens,
+                             float* logp, float* lse, float temperature) {
+  if (!dm || !U || !W1 || !W2t || !anchor || !tokens || !logp || !lse) return DSPARK_E_NULL;
+  if (!dims_ok(dm)) return DSPARK_E_SHAPE;
+  if (!dtype_ok(wdt)) return DSPARK_E_DTYPE;
+  if (!temp_ok(temperature)) return DSPARK_E_VALUE;
+  return DSPARK_OK;
+}
+
+// ---- the variant that allocates nothing: its scratch is this file's device array ----
+// Each device holds its own copy of `scratch` for the life of the process; the host never
+// uses the name itself as an address, only the device address looked up once per device.
+constexpr size_t kDraftStaticScratch = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kDraftStaticScratch];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+dspark_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return DSPARK_E_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return DSPARK_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" dspark_status dspark_draft_markov(const dspark_dims* dm, const float* U,
+                                             const void* W1, const void* W2t, int wdt,
+                                             const int32_t* anchor, const int32_t* forced,
+                                             float temperature, uint64_t seed,
+                                             int32_t* tokens, float* logp, float* lse,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  const dspark_status v =
+      draft_validate(dm, U, W1, W2t, wdt, anchor, tokens, logp, lse, temperature);
+  if (v != DSPARK_OK) return v;
+  if (!ws || ws_bytes < dspark_draft_workspace(dm)) return DSPARK_E_WORKSPACE;
+  return draft_run(dm, draft_plan(dm, wdt), U, W1, W2t, wdt, anchor, forced, temperature,
+                   seed, tokens, logp, lse, ws, (hipStream_t)stream);
+}
+
+extern "C" dspark_status dspark_draft_markov_noalloc(const dspark_dims* dm, const float* U,
+                                                     const void* W1, const void* W2t, int wdt,
+                                                     const int32_t* anchor,
+                                                     const int32_t* forced, float temperature,
+                                                     uint64_t seed, int32_t* tokens,
+                                                     float* logp, float* lse, void* stream) {
+  const dspark_status v =
+      draft_validate(dm, U, W1, W2t, wdt, anchor, tokens, logp, lse, temperature);
+  if (v != DSPARK_OK) return v;
+  const DraftPlan plan = draft_plan(dm, wdt);
+  unsigned long long* b;
+  float2* p;
+  if (draft_ws(dm, plan.nslices, &b, &p, nullptr) > kDraftStaticScratch)
+    return DSPARK_E_WORKSPACE;
+  void* ws = nullptr;
+  const dspark_status sc = static_scratch(&ws);
+  if (sc != DSPARK_OK) return sc;
+  return draft_run(dm, plan, U, W1, W2t, wdt, anchor, forced, temperature, seed, tokens, logp,
+                   lse, ws, (hipStream_t)stream);
 }

@@ -129,6 +129,28 @@ dspark_status dspark_draft_markov(const dspark_dims* dims, const float* U, const
                                   size_t ws_bytes, void* stream);
 
 /*
+ * dspark_draft_markov for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation,
+ * kernels and results, bit for bit, with the same arguments except the workspace.  Its
+ * scratch (the per-position packed winners and softmax partials) is a 32 MiB array in
+ * device memory that the library holds on every GPU it runs on until the process ends;
+ * the call itself allocates nothing and calls no allocating routine.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (several streams or
+ * host threads) race and give undefined results, so serialise them.  The array keeps the
+ * last call's contents; each call clears what it needs cleared with a kernel (no memset),
+ * so the call can be captured in a graph.
+ * Returns DSPARK_E_WORKSPACE (nothing enqueued) when the draft's scratch for `dims` exceeds
+ * 32 MiB; dspark_workspace_bytes(DSPARK_OP_DRAFT, dims) <= 32 MiB guarantees it fits (e.g.
+ * B = 128, gamma = 16, V = 151936 needs 8.4 MB).  DSPARK_E_HIP if the array's device
+ * address cannot be looked up.  Other errors as for dspark_draft_markov.
+ */
+dspark_status dspark_draft_markov_noalloc(const dspark_dims* dims, const float* U,
+                                          const void* W1, const void* W2t, int wdt,
+                                          const int32_t* anchor, const int32_t* forced,
+                                          float temperature, uint64_t seed, int32_t* tokens,
+                                          float* logp, float* lse, void* stream);
+
+/*
  * Confidence head [CSDN Eq. 7; XTL §5 "Confidence Head"]:
  *   c[b][k-1] = 1 / (1 + exp(-(sum_j w[j] h[b][k-1][j] + sum_i w[d+i] W1[x_{b,k-1}][i])))
  * with x_{b,0} = anchor[b] and x_{b,k-1} = tokens[b][k-2]; no bias term.

@@ -179,6 +179,23 @@ def test_binding_fails_loudly_without_library(monkeypatch):
         ds.lib()
 
 
+def test_noalloc_draft_validation_and_size_limit():
+    """The allocation-free draft validates like the draft and refuses, before touching the
+    device, a shape whose scratch exceeds its 32 MiB array."""
+    L = ds.lib()
+
+    def call(dm, temp=1.0, wdt=1, U=P):
+        return L.dspark_draft_markov_noalloc(ctypes.byref(dm) if dm is not None else None, U,
+                                             P, P, wdt, P, None, temp, 1, P, P, P, None)
+    assert call(None) == 1
+    assert call(_dims(), U=None) == 1
+    assert call(_dims(B=0)) == 2
+    assert call(_dims(), wdt=5) == 3
+    assert call(_dims(), temp=-1.0) == 4
+    # 256 requests, 64 positions on the matrix-core path: 64 x 256 slices x 256 x 8 bytes
+    assert call(ds.Dims(256, 64, 151936, 256, 0)) == 5
+
+
 def test_gumbel_lattice_validation():
     L = ds.lib()
     assert L.dspark_gumbel_lattice(0, None, None) == 1
