@@ -16,6 +16,7 @@
 
 #include "dspark_dev.h"
 #include "dspark_host.h"
+#include "gemv.h"
 #include "mfma_bias.h"
 #include "rowbias.h"
 
@@ -181,16 +182,23 @@ namespace {
 
 struct DraftPlan {
   bool mfma;
+  bool gemv;       // the streaming kernel for few requests (gemv.hip)
   int nslices;     // partial slots per (position, request)
   int slice_len;   // row path only
+  GemvPlan gp;
 };
 
 DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   DraftPlan p{};
   p.mfma = mfma_bias_supported(d->batch, d->rank, wdt);
+  p.gemv = !p.mfma && draft_gemv_supported(d->batch, d->vocab, d->rank, wdt);
   if (p.mfma) {
     p.nslices = mfma_grid(d->vocab, d->batch, kModeDraft);
     p.slice_len = 0;
+  } else if (p.gemv) {
+    p.gp = draft_gemv_plan(d->vocab);
+    p.nslices = p.gp.nwg;
+    p.slice_len = p.gp.span;
   } else {
     RowSlices s = row_slices(d->vocab, d->batch);
     p.nslices = s.count;
@@ -251,6 +259,11 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
       const dspark_status ls = launch_mfma_bias(a, plan.nslices, st);
       prof_end(st, ls == DSPARK_OK ? 1 : -1);
       if (ls != DSPARK_OK) return DSPARK_E_HIP;
+    } else if (plan.gemv) {
+      prof_begin(st);
+      launch_draft_gemv(plan.gp, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced,
+                        bprev, bcur, pk, B, G, V, k, invT, key0, key1, st);
+      prof_end(st, 1);
     } else {
       prof_begin(st);
       const size_t sh = sizeof(float) * (r + 256 + 16);

@@ -180,6 +180,14 @@ MULTI_TILE = {
     "mt_b150_odd": workload.custom(name="mt_b150_odd", B=150, gamma=2, V=131073, r=256,
                                    d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
                                    table="serve"),
+    # the streaming kernel for few requests: 586 workgroups of one 224-row chunk each
+    "mt_gemv_b3_g4": workload.custom(name="mt_gemv_b3", B=3, gamma=4, V=131072, r=256, d=64,
+                                     bf16=True, wsigma=0.5, logits="zipf", sigma_mix=True,
+                                     table="serve"),
+    # ... and with two chunks per workgroup (more than 768 chunks)
+    "mt_gemv_b2_v262144": workload.custom(name="mt_gemv_b2", B=2, gamma=3, V=262144, r=256,
+                                          d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+                                          table="serve"),
 }
 
 
