@@ -59,23 +59,22 @@ __global__ __launch_bounds__(kGvThreads, 3) void k_draft_gemv(
   bool have_w1 = false;
   uint32_t wp[16];   // this lane's 32 W1 entries as bf16 pairs (widened where used)
   for (int v0 = v_lo; v0 < v_hi; v0 += kGvRows) {
-    // 1. this chunk's W2t slices and base-logit quad, before anything that depends on the
-    //    conditioning token
+    // 1. the first pass of this chunk's W2t slices and its base-logit quad, 2. the
+    //    conditioning token and this lane's 32 entries of its W1 row (first chunk only),
+    //    3. the other passes: loads complete in issue order, so the dots of pass p wait
+    //    for pass p (and W1) only, while the later passes are still streaming
     uint4 q[kGvPasses][4];
-#pragma unroll
-    for (int p = 0; p < kGvPasses; ++p) {
+    auto load_pass = [&](int p) {
       const int v = min(v0 + p * 32 + rowi, V - 1);
       const uint4* src = reinterpret_cast<const uint4*>(W2t + (size_t)v * kR + sub * 32);
 #pragma unroll
       for (int c = 0; c < 4; ++c) q[p][c] = src[c];
-    }
+    };
+    load_pass(0);
     const int vq = v0 + 4 * tid;                   // this thread's quad (tid < kGvRows / 4)
     const bool has_quad = tid < kGvRows / 4 && vq < v_hi;
     float4 uq = make_float4(0.f, 0.f, 0.f, 0.f);
     if (has_quad) uq = *reinterpret_cast<const float4*>(Urow + vq);
-    // 2. the conditioning token and this lane's 32 entries of its W1 row (once); the
-    //    scheduling barrier keeps the stream above issued first
-    __builtin_amdgcn_sched_barrier(0);
     if (!have_w1) {
       const int prev = gv_prev(anchor, forced, best_prev, b, G, k, V);
       const uint4* w1src = reinterpret_cast<const uint4*>(W1 + (size_t)prev * kR + sub * 32);
@@ -89,6 +88,10 @@ __global__ __launch_bounds__(kGvThreads, 3) void k_draft_gemv(
       }
       have_w1 = true;
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 1; p < kGvPasses; ++p) load_pass(p);
+    __builtin_amdgcn_sched_barrier(0);
     // 3. the bias of every row of the chunk (8 lanes per row, xor-combined)
 #pragma unroll
     for (int p = 0; p < kGvPasses; ++p) {
