@@ -194,19 +194,22 @@ def main():
         graph_note = f"capture failed: {exc}"
         graph_ok = False
     ms_step_eager = ms_step
+    ms_step_mean = ms_step
     if graph_ok:
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(args.steps):
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        gev[0].record(stream)
+        for i in range(args.steps):
             graph.replay()
-        g1.record(stream)
+            gev[i + 1].record(stream)
         torch.cuda.synchronize()
-        ms_step = g0.elapsed_time(g1) / args.steps
-        log(f"graph replay: {ms_step:.3f} ms/step (eager {ms_step_eager:.3f})")
+        per_step = [gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps)]
+        ms_step_mean = gev[0].elapsed_time(gev[-1]) / args.steps
+        ms_step = float(np.median(per_step))
+        log(f"graph replay: median {ms_step:.3f} ms/step, mean {ms_step_mean:.3f} "
+            f"(eager {ms_step_eager:.3f})")
         del graph
     else:
         log(f"graph replay not used: {graph_note}")
@@ -270,6 +273,32 @@ def main():
             torch.cuda.synchronize()
             verify_ms = vf0.elapsed_time(vf1) / args.steps
         del vgraph
+
+    # verification at the full block (ell = gamma for every request: the budget's upper
+    # bound, every target row read), as a checked graph replay like the call above
+    ell_full = torch.full((B,), G, dtype=torch.int32, device=dev)
+    vfull_ms, vfull_rej = timed_verify(ds, args, stream, graph_ok, U, W1, W2t, anchor, tokens,
+                                       logp, lse, T, ell_full, temp, inp.seed, nacc, outtok,
+                                       ws_v)
+    vfull_bytes = B * (G + 1) * V * 4 + ((V * r * 2 + vfull_rej * 2 * V * 4) if vfull_rej else 0)
+
+    # the target side of a closed-loop round on its own: the stand-in target's logits for
+    # this round's block (sigma 0.5, as in the loop below), then verification on them at
+    # this round's schedule -- timed apart from the loop, for the latency model
+    T_loop = torch.empty((B, G + 1, V), dtype=torch.float32, device=dev)
+    ds.dspark_markov_target(U, anchor, tokens, 0.5, 1, out=T_loop)
+    tt0 = torch.cuda.Event(enable_timing=True)
+    tt1 = torch.cuda.Event(enable_timing=True)
+    tt0.record(stream)
+    for _ in range(args.steps):
+        ds.dspark_markov_target(U, anchor, tokens, 0.5, 1, out=T_loop)
+    tt1.record(stream)
+    torch.cuda.synchronize()
+    target_ms = tt0.elapsed_time(tt1) / args.steps
+    vloop_ms, _ = timed_verify(ds, args, stream, False, U, W1, W2t, anchor, tokens, logp, lse,
+                               T_loop, ell, temp, inp.seed, nacc, outtok, ws_v)
+    del T_loop
+    torch.cuda.empty_cache()
 
     # the draft side of a round alone (draft, confidence, schedule)
     ds0 = torch.cuda.Event(enable_timing=True)
@@ -375,7 +404,10 @@ def main():
     pos_bytes = w2t_bytes + B * V * 4          # one position: W2t once, B base-logit rows
     launch_bytes = int(round(pos_bytes * kern_pos))
     achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
+    strict_bytes = int(round((w2t_bytes / G + B * V * 4) * kern_pos))
+    strict_achieved = strict_bytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg.name)
+    mfma_util = measured_mfma_util(cfg.name)
 
     rec = {
         "metric": METRIC,
@@ -385,6 +417,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_mean": round(ms_step_mean, 4),
         "ms_per_step_eager": round(ms_step_eager, 4),
         "launch": "HIP graph replay of the step (checked against the eager step)" if graph_ok
                   else f"eager ({graph_note})",
@@ -421,11 +454,24 @@ def main():
                 "bytes_per_launch": probe_bytes,
             },
             "frac_of_read_probe": round(achieved / probe_gbs, 4),
+            "strict": {
+                "kind": "W2t counted once per round (gamma positions) instead of once per "
+                        "position, so that on-die reuse of W2t across positions cannot "
+                        "inflate the fraction",
+                "bytes_per_launch": strict_bytes,
+                "achieved": round(strict_achieved, 1),
+                "frac": round(strict_achieved / HBM_PEAK_GBS, 4),
+            },
+            "mfma_util": mfma_util,
         },
         "draft_call_ms": round(draft_ms, 4),
         "verify_call_ms": round(verify_ms, 4),
         "verify_call_ms_eager": round(verify_ms_eager, 4),
         "verify_hbm_frac": round(verify_bytes / (verify_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "verify_full_block_ms": round(vfull_ms, 4),
+        "verify_full_block_hbm_frac": round(vfull_bytes / (vfull_ms * 1e-3) / 1e9 /
+                                            HBM_PEAK_GBS, 4),
+        "verify_full_block_rejections": vfull_rej,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_bytes": step_bytes,
         "schedule_topk_us": round(topk_us, 2),
@@ -434,10 +480,14 @@ def main():
         "loop_rounds": LOOP_R,
         "loop_round_ms": round(loop_round_ms, 4),
         "loop_draft_side_ms": round(draft_side_ms, 4),
-        "loop_verify_side_ms": round(loop_round_ms - draft_side_ms, 4),
+        "loop_target_side_ms": round(target_ms + vloop_ms, 4),
+        "loop_target_side_parts_ms": {"stand_in_target": round(target_ms, 4),
+                                      "verify": round(vloop_ms, 4)},
         "loop_tau_per_round": [round(float(x), 3) for x in loop_tau],
         "loop_tau": round(float(loop_tau.mean()), 4),
         "loop_ms_per_token": round(loop_round_ms / float(loop_tau.mean()), 4),
+        "loop_eq1_ms_per_token": round((draft_side_ms + target_ms + vloop_ms) /
+                                       float(loop_tau.mean()), 4),
         "loop_tokens_per_s": round(B * float(loop_tau.mean()) / (loop_round_ms * 1e-3), 1),
         "loss_call_ms": round(loss_ms, 4),
         "loss_hbm_frac": round(loss_bytes / (loss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -452,6 +502,16 @@ def main():
         if parallel is not None:
             rec["cpu_baseline_all_cores"] = parallel
     print(json.dumps(rec), flush=True)
+
+    # release what this run holds on the device before the interpreter exits: every stream
+    # drained, device tensors and events dropped, the allocator's cache and the binding's
+    # workspaces returned
+    torch.cuda.synchronize()
+    del U, W1, W2t, h, w, anchor, sps, T, tokens, logp, lse, conf, ell, theta, ntot, nacc
+    del outtok, alpha, ws_d, ws_v, ws_t, ev_d0, ev_d1, e0, e1
+    import gc
+    gc.collect()
+    ds.release_cached_workspaces()
 
 
 # the dominant kernel's source files, hashed in this order (the counter summary names it)
@@ -483,6 +543,82 @@ def measured_traffic(workload_name: str):
     return int(m_b.group(1))
 
 
+def _sha_bound_figure(path: str, pattern: str):
+    """A figure from a committed counter summary, or None when the summary is missing or the
+    draft kernel's source has changed since it was taken (its sha256 is recorded in it)."""
+    import hashlib
+    import re
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "draft_verify_sampling_step_amd", "csrc")
+    srcs = [os.path.join(csrc, f) for f in KERNEL_SOURCES]
+    if not (os.path.exists(path) and all(os.path.exists(f) for f in srcs)):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", text)
+    m_v = re.search(pattern, text)
+    if not (m_sha and m_v):
+        return None
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    return m_v.group(1) if h.hexdigest() == m_sha.group(1) else None
+
+
+def measured_mfma_util(workload_name: str):
+    """Matrix-core busy fraction of the draft position kernel (SQ counters, from the
+    committed summary bound to the kernel source), or None."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    v = _sha_bound_figure(os.path.join(here, "profiles", f"draft_position_{workload_name}_mfma.md"),
+                          r"matrix-core busy fraction:\s*([0-9.]+)")
+    return None if v is None else float(v)
+
+
+def timed_verify(ds, args, stream, use_graph, U, W1, W2t, anchor, tokens, logp, lse, T, ell,
+                 temp, seed, nacc, outtok, ws_v):
+    """Mean time of dspark_verify on these inputs (a graph replay checked against the eager
+    call when use_graph, else eager) and the number of rejected requests."""
+    import torch
+    ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, seed,
+                     out=(nacc, outtok, None), ws=ws_v)
+    torch.cuda.synchronize()
+    rej = int((nacc < ell.clamp(0, tokens.shape[1])).sum().item())
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        vref = (nacc.clone(), outtok.clone())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, seed,
+                             out=(nacc, outtok, None), ws=ws_v)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, seed,
+                             out=(nacc, outtok, None), ws=ws_v)
+        nacc.fill_(-7)
+        outtok.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        if torch.equal(vref[0], nacc) and torch.equal(vref[1], outtok):
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            del g
+            return e0.elapsed_time(e1) / args.steps, rej
+        del g
+    e0.record(stream)
+    for _ in range(args.steps):
+        ds.dspark_verify(U, W1, W2t, anchor, tokens, logp, lse, T, ell, temp, seed,
+                         out=(nacc, outtok, None), ws=ws_v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps, rej
+
+
 def draft_kernel_name(B: int, V: int, r: int) -> str:
     """The draft position kernel the library dispatches for this shape (bf16 weights)."""
     if r == 256 and 32 < B <= 256 and V % 4 == 0:
@@ -490,6 +626,9 @@ def draft_kernel_name(B: int, V: int, r: int) -> str:
             " (16x16x32 bf16 MFMA, 16-column waves)"
     if r == 256 and B >= 32:
         return "k_mfma_bias<NCB, draft> (32x32x16 bf16 MFMA, 32-column waves)"
+    if r == 256 and V % 4 == 0:
+        return "k_draft_gemv (streaming kernel for few requests, one vocabulary range per " \
+            "workgroup)"
     return "k_draft_row (row kernel, one request per workgroup row)"
 
 

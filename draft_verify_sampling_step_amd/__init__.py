@@ -16,6 +16,7 @@ There is no fallback: if the library is not built, importing succeeds but every 
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 import threading
@@ -89,6 +90,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64,
                                               _P, _P]
             L.dspark_gumbel_lattice.argtypes = [_I, _P, _P]
+            L.dspark_markov_target.argtypes = [D, _P, _P, _P, _F, _U64, _P, _P]
             L.dspark_loss_workspace_bytes.argtypes = [ctypes.c_int32] * 3
             L.dspark_loss_workspace_bytes.restype = _SZ
             L.dspark_draft_loss.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -109,7 +111,7 @@ def lib() -> ctypes.CDLL:
                        "dspark_confidence_calibrated", "dspark_sts_calibrate", "dspark_schedule",
                        "dspark_schedule_topk", "dspark_verify", "dspark_accept_rate_tv",
                        "dspark_draft_loss", "dspark_closed_loop", "dspark_rng_uniforms",
-                       "dspark_gumbel_lattice",
+                       "dspark_gumbel_lattice", "dspark_markov_target",
                        "dspark_profile_start", "dspark_profile_stop",
                        "dspark_stream_read_probe"):
                 getattr(L, fn).restype = _I
@@ -167,6 +169,18 @@ def workspace_bytes(op: int, B: int, gamma: int, V: int, r: int, d: int = 0) -> 
 
 
 _ws_cache: dict = {}
+
+
+def release_cached_workspaces():
+    """Drop the per-device workspaces the binding keeps between calls (also run at exit,
+    before the interpreter tears torch and the HIP runtime down)."""
+    _ws_cache.clear()
+    if torch.cuda.is_initialized():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+atexit.register(release_cached_workspaces)
 
 
 def _workspace(device: torch.device, nbytes: int, ws: Optional[torch.Tensor]):
@@ -335,6 +349,24 @@ def dspark_closed_loop(U, W1, W2t, h, w, anchor, sps, rounds: int, temperature: 
         _ptr(out["n_accept"]), _ptr(out["out_tokens"]), _ptr(out["pt_tok"]), _ptr(wsb),
         wsb.numel(), _stream_handle(stream)))
     return out
+
+
+def dspark_markov_target(U, anchor, tokens, target_sigma: float, target_seed: int, out=None,
+                         stream=None):
+    """The closed loop's stand-in target logits T [B][gamma+1][V] f32 for the drafted
+    tokens [B][gamma] (measurement and test support, not a step of the method)."""
+    B, G, V = U.shape
+    _f32(U, "U")
+    _i32(anchor, "anchor")
+    _i32(tokens, "tokens")
+    T = out if out is not None else torch.empty((B, G + 1, V), dtype=torch.float32,
+                                                device=U.device)
+    dm = Dims(B, G, V, 8, 0)
+    _check(lib().dspark_markov_target(ctypes.byref(dm), _ptr(U), _ptr(anchor), _ptr(tokens),
+                                      float(target_sigma),
+                                      int(target_seed) & 0xFFFFFFFFFFFFFFFF, _ptr(T),
+                                      _stream_handle(stream)))
+    return T
 
 
 def dspark_draft_loss(zd, zt, labels, conf_logit, alphas=(0.1, 0.9, 1.0), grads=True,

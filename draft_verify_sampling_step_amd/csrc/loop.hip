@@ -122,6 +122,38 @@ LoopWs loop_ws(const dspark_dims* d, void* base) {
 
 }  // namespace
 
+namespace {
+void launch_markov_target(const float* U, const int32_t* anchor, const int32_t* tokens, int B,
+                          int G, int V, float scale, uint32_t tk0, uint32_t tk1, float* T,
+                          hipStream_t st) {
+  const int nchunk = (V + kTargetChunk - 1) / kTargetChunk;
+  const size_t BG1 = (size_t)B * (G + 1);
+  const bool vec = V % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)T % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(k_markov_target<true>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0, st,
+                       U, anchor, tokens, G, V, nchunk, scale, tk0, tk1, T);
+  else
+    hipLaunchKernelGGL(k_markov_target<false>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0,
+                       st, U, anchor, tokens, G, V, nchunk, scale, tk0, tk1, T);
+}
+}  // namespace
+
+extern "C" dspark_status dspark_markov_target(const dspark_dims* dims, const float* U,
+                                              const int32_t* anchor, const int32_t* tokens,
+                                              float target_sigma, uint64_t target_seed,
+                                              float* T, void* stream) {
+  if (!dims || !U || !anchor || !tokens || !T) return DSPARK_E_NULL;
+  if (!dims_ok(dims)) return DSPARK_E_SHAPE;
+  if ((size_t)dims->batch * (dims->gamma + 1) * ((dims->vocab + kTargetChunk - 1) / kTargetChunk) >
+      0x7FFFFFFFull)
+    return DSPARK_E_SHAPE;
+  if (!std::isfinite(target_sigma) || target_sigma < 0.f) return DSPARK_E_VALUE;
+  launch_markov_target(U, anchor, tokens, dims->batch, dims->gamma, dims->vocab,
+                       (float)((double)target_sigma * std::sqrt(3.0)), (uint32_t)target_seed,
+                       (uint32_t)(target_seed >> 32), T, (hipStream_t)stream);
+  return launch_status();
+}
+
 extern "C" size_t dspark_loop_workspace_bytes(const dspark_dims* dims) {
   if (!dims_ok(dims)) return 0;
   return loop_ws(dims, nullptr).bytes;
@@ -152,11 +184,10 @@ extern "C" dspark_status dspark_closed_loop(
   hipStream_t st = (hipStream_t)stream;
   const int B = dims->batch, G = dims->gamma, V = dims->vocab;
   const size_t BG = (size_t)B * G, BG1 = (size_t)B * (G + 1);
-  const int nchunk = (V + kTargetChunk - 1) / kTargetChunk;
+  if (BG1 * ((V + kTargetChunk - 1) / kTargetChunk) > 0x7FFFFFFFull) return DSPARK_E_SHAPE;
   const float scale = (float)((double)target_sigma * std::sqrt(3.0));
   const uint32_t tk0 = (uint32_t)target_seed, tk1 = (uint32_t)(target_seed >> 32);
   const unsigned bgrid = (unsigned)((B + 255) / 256);
-  const bool vec_target = V % 4 == 0 && (uintptr_t)U % 16 == 0 && (uintptr_t)lw.T % 16 == 0;
   if (anchors) {
     hipLaunchKernelGGL(k_copy_i32, dim3(bgrid), dim3(256), 0, st, anchor, B, anchors);
     if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
@@ -189,12 +220,7 @@ extern "C" dspark_status dspark_closed_loop(
                           stream);
     }
     if (s != DSPARK_OK) return s;
-    if (vec_target)
-      hipLaunchKernelGGL(k_markov_target<true>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0, st,
-                         U, anc_t, tok_t, G, V, nchunk, scale, tk0, tk1, lw.T);
-    else
-      hipLaunchKernelGGL(k_markov_target<false>, dim3((unsigned)(BG1 * nchunk)), dim3(256), 0,
-                         st, U, anc_t, tok_t, G, V, nchunk, scale, tk0, tk1, lw.T);
+    launch_markov_target(U, anc_t, tok_t, B, G, V, scale, tk0, tk1, lw.T, st);
     if (launch_status() != DSPARK_OK) return DSPARK_E_HIP;
     s = dspark_verify(dims, U, W1, W2t, wdt, anc_t, tok_t, lw.logp, lw.lse, lw.T, ell_t,
                       temperature, seed_t, n_t, out_t, pt_tok ? pt_tok + (size_t)t * BG : nullptr,

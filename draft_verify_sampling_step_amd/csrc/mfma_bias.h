@@ -10,7 +10,8 @@
 // leaves registers: the epilogue of each 32 x 32 output tile reads the matching base
 // logits (and target logits) and does one of
 //   kModeDraft  z = (U + bias)/T; online (max, sum-exp); Gumbel-max race   [CSDN Eq. 4]
-//   kModeResid  rho = max(0, p_t - p_d); Gumbel race on ln rho            (verification)
+//   kModeResid  rho = max(0, p_t - p_d); Gumbel race on ln rho            (verification);
+//               with at most thin_max rows to do, a thin path without matrix cores
 //   kModeTV     sum_v min(p_d, p_t)                                      [CSDN Eq. 8]
 //
 // Layout (per workgroup of 4 waves): each wave keeps the gathered W1 rows of its column
@@ -41,8 +42,14 @@ struct MfmaBiasArgs {
   const unsigned long long* best_prev;   // draft: packed winners of position k-1
   unsigned long long* best_cur;          // draft: packed winners of position k (atomic max)
   float2* part;                          // draft: [slices][B] base-2 softmax state (max, sum)
-  float4* rpart;                         // resid: [slices][B] (residual score, index,
-                                         //        fallback score, index)
+  unsigned long long* res_best;          // resid: [B][2] packed (score, index) winners of
+                                         //        the residual race and of the p_t
+                                         //        fallback race, zero before the launch
+  int* res_arrive;                       // resid: arrival counter of this launch's
+                                         //        workgroups, zero before the launch
+  const int32_t* n_accept;               // resid: accepted prefix length per request
+  int32_t* out_tokens;                   // resid: [B][G+1]; the last workgroup to finish
+                                         //        writes each residual token at n_accept
   const float* T;                        // resid/tv: target logits [B][G+1][V]
   const float* lse_d;                    // resid/tv: draft lse [B][G]
   const float* lse_t_row;                // resid: lse of target row j_b [B]
@@ -54,9 +61,12 @@ struct MfmaBiasArgs {
   uint32_t key0, key1;
   int ncols;                             // columns of this launch (<= 256)
   int col0;                              // first global column of this launch
-  int thin_max;                          // resid: > 0 = leave at once when the launch
-                                         // has 1..thin_max residual rows (thin pass)
+  int thin_max;                          // resid: 1..thin_max residual rows take the
+                                         //        thin path (16 lanes per row, no MFMA)
 };
+
+// Residual rows per launch that take the thin path of the residual mode.
+constexpr int kResidThinMax = 2;
 
 // The MFMA path handles bf16 weights with r = 256 (16 k-steps of 16).
 inline bool mfma_bias_supported(int ncols, int r, int wdt) {

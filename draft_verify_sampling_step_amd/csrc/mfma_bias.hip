@@ -58,10 +58,178 @@ struct Shape {
   static constexpr size_t kRed = (size_t)TSPLIT * NC * 4 * 4;
   static constexpr size_t kLds = kOffMeta + kMetaBytes;
   static_assert(TSPLIT * 16 % NW == 0, "DMA split");
-  static_assert(kRed <= kOffMeta, "reduction scratch reuses the ring");
+  static_assert(kRed + 16 <= kOffMeta, "reduction scratch (and a flag) reuses the ring");
   static_assert(kLds * WG_PER_CU <= 160 * 1024, "LDS budget");
   static_assert(kWaitSS < 64, "vmcnt range");
 };
+
+// ---- residual mode helpers --------------------------------------------------------
+// Thin path: with at most kThinMax requests to resample (the usual case) the matrix-core
+// machinery would still stream W2t through 32-column blocks; instead every wave takes four
+// vocabulary rows per step, 16 lanes per row: lane part p holds elements 16 p .. 16 p + 15
+// of W2t[v] and of every listed request's W1[x_{j-1}], the dot products are summed over
+// the 16 lanes by DPP moves, and lane p < n runs request p's residual and fallback races
+// on row v.
+constexpr int kThinMax = kResidThinMax;
+
+// Sum over each 16-lane row of the wave by DPP moves (quad swaps 1,0,3,2 and 2,3,0,1, then
+// the half-row and row mirrors): each step adds a commutative pair, so all 16 lanes end
+// with the same total.
+__device__ __forceinline__ float dpp_row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// The thin path over this workgroup's slice of the vocabulary for the n <= kThinMax listed
+// columns clist[0..n) of the launch; scratch holds 4 * NW * kThinMax float4.  Each request's
+// best (score, index) of both races goes to its packed winner words.
+template <int NW>
+__device__ __forceinline__ void resid_thin(const MfmaBiasArgs& a, const int* clist, int n,
+                                           float4* scratch) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int part = lane & 15, quad = lane >> 4;
+  const int G = a.G, V = a.V;
+  float w1[kThinMax][16];
+  const float* urow = a.U;
+  const float* trow = a.T;
+  float ld = 0.f, lt = 0.f;
+  int myb = 0, myj = 1;
+#pragma unroll
+  for (int i = 0; i < kThinMax; ++i) {
+    int b = 0, j = 1;
+    if (i < n) { b = a.col0 + clist[i]; j = a.jrow[b]; }
+    const int prev = clamp_tok((j == 1) ? a.anchor[b] : a.tokens[(size_t)b * G + (j - 2)], V);
+    const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(a.W1 + (size_t)prev * kR + 16 * part);
+    const u32x4_t q0 = wp[0], q1 = wp[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w1[i][2 * e] = __uint_as_float(q0[e] << 16);
+      w1[i][2 * e + 1] = __uint_as_float(q0[e] & 0xFFFF0000u);
+      w1[i][8 + 2 * e] = __uint_as_float(q1[e] << 16);
+      w1[i][8 + 2 * e + 1] = __uint_as_float(q1[e] & 0xFFFF0000u);
+    }
+    if (i == part && i < n) {
+      myb = b;
+      myj = j;
+      urow = a.U + ((size_t)b * G + (j - 1)) * V;
+      trow = a.T + ((size_t)b * (G + 1) + (j - 1)) * V;
+      ld = a.lse_d[(size_t)b * G + (j - 1)] * kLog2e;
+      lt = a.lse_t_row[b] * kLog2e;
+    }
+  }
+  const float s2 = a.invT * kLog2e;
+  const PhiloxLane pl = philox_lane((uint32_t)myj, (uint32_t)myb, 2u, a.key0, a.key1);
+  const int len = (V + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int vb = blockIdx.x * len, ve = min(V, vb + len);
+  Cand c1{-INFINITY, 0xFFFFFFFFu, 0.f}, c2{-INFINITY, 0xFFFFFFFFu, 0.f};
+  // four row groups per iteration (rows v0 + 4 NW u + quad), every load issued first; rows
+  // past the slice load row v0 and are not raced
+  for (int v0 = vb + 4 * wave; v0 < ve; v0 += 16 * NW) {
+    u32x4_t xq[4][2];
+    float uq[4], tq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int vu = v0 + 4 * NW * u + quad;
+      const int vv = vu < ve ? vu : v0;
+      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(a.W2t + (size_t)vv * kR + 16 * part);
+      xq[u][0] = xp[0];
+      xq[u][1] = xp[1];
+      uq[u] = urow[vv];
+      tq[u] = trow[vv];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 4 * NW * u + quad;
+      float xf[16];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xf[2 * e] = __uint_as_float(xq[u][0][e] << 16);
+        xf[2 * e + 1] = __uint_as_float(xq[u][0][e] & 0xFFFF0000u);
+        xf[8 + 2 * e] = __uint_as_float(xq[u][1][e] << 16);
+        xf[8 + 2 * e + 1] = __uint_as_float(xq[u][1][e] & 0xFFFF0000u);
+      }
+      float d[kThinMax];
+#pragma unroll
+      for (int i = 0; i < kThinMax; ++i) {
+        d[i] = 0.f;
+        if (i < n) {   // uniform
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc = fmaf(xf[e], w1[i][e], acc);
+          d[i] = dpp_row_sum16(acc);
+        }
+      }
+      if (v < ve && part < n) {
+        float bias = d[0];
+#pragma unroll
+        for (int i = 1; i < kThinMax; ++i) bias = part == i ? d[i] : bias;
+        // base 2, as in the matrix-core epilogue: the same races, the same scores
+        const float zd2 = (uq[u] + bias) * s2;
+        const float zt2 = tq[u] * s2;
+        const float rho = ex2(zt2 - lt) - ex2(zd2 - ld);
+        const U4 w = philox_call((uint32_t)v >> 2, pl);
+        const uint32_t word =
+            (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
+        const float gn = neg_lglg(word);
+        if (rho > 0.f) {
+          const float sc = lg2(rho) + gn;
+          if (sc > c1.s) c1 = Cand{sc, (uint32_t)v, 0.f};
+        }
+        const float sc2 = zt2 + gn;
+        if (sc2 > c2.s) c2 = Cand{sc2, (uint32_t)v, 0.f};
+      }
+    }
+  }
+  // merge the candidates of request p over the 4 NW (wave, row quad) lanes, ties to the
+  // lower index
+  float4 (*s_cand)[kThinMax] = reinterpret_cast<float4 (*)[kThinMax]>(scratch);
+  if (part < n)
+    s_cand[wave * 4 + quad][part] =
+        make_float4(c1.s, __uint_as_float(c1.i), c2.s, __uint_as_float(c2.i));
+  __syncthreads();
+  if (tid < n) {
+    float s1 = -INFINITY, ss2 = -INFINITY;
+    uint32_t i1 = 0xFFFFFFFFu, i2 = 0xFFFFFFFFu;
+    for (int g = 0; g < 4 * NW; ++g) {
+      const float4 p = s_cand[g][tid];
+      const uint32_t pi1 = __float_as_uint(p.y), pi2 = __float_as_uint(p.w);
+      if (p.x > s1 || (p.x == s1 && pi1 < i1)) { s1 = p.x; i1 = pi1; }
+      if (p.z > ss2 || (p.z == ss2 && pi2 < i2)) { ss2 = p.z; i2 = pi2; }
+    }
+    const int b = a.col0 + clist[tid];
+    if (i1 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b], pack_score(s1, i1));
+    if (i2 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b + 1], pack_score(ss2, i2));
+  }
+}
+
+// After every thread of the workgroup has posted its winners: count the workgroup in; the
+// last of the launch to arrive writes, for every request of the launch with a residual
+// row, the residual winner (the p_t fallback when no residual was positive) after the
+// accepted prefix.  No workgroup waits for another.
+__device__ __forceinline__ void resid_finish(const MfmaBiasArgs& a, int* s_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's atomics have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(a.res_arrive, 1, __ATOMIC_ACQ_REL,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = before == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!*s_flag) return;
+  for (int c = threadIdx.x; c < a.ncols; c += blockDim.x) {
+    const int b = a.col0 + c;
+    if (a.jrow[b] == 0) continue;
+    const unsigned long long r1 =
+        __hip_atomic_load(&a.res_best[2 * b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long r2 =
+        __hip_atomic_load(&a.res_best[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t y = packed_index(r1 != 0ull ? r1 : r2);
+    a.out_tokens[(size_t)b * (a.G + 1) + a.n_accept[b]] = (int32_t)y;
+  }
+}
 
 template <int NCB> constexpr int kThreads = Shape<NCB, kModeDraft>::NT;
 template <int NCB> constexpr int kWgPerCu = Shape<NCB, kModeDraft>::WG_PER_CU;
@@ -131,9 +299,12 @@ k_mfma_bias(const MfmaBiasArgs a) {
     if (tid == NT - 1) clist[NC] = off + __popcll(bal);
     __syncthreads();
     n_live = clist[NC];
-    // none at all, or few enough for the thin pass: nothing to do here (uniform exit, no
-    // load issued yet)
-    if (n_live == 0 || n_live <= a.thin_max) return;
+    if (n_live == 0) return;   // nothing to resample (uniform exit, no load issued yet)
+    if (n_live <= a.thin_max) {
+      resid_thin<NW>(a, clist, n_live, reinterpret_cast<float4*>(smem + 4096));
+      resid_finish(a, clist + NC + 1 + NW);
+      return;
+    }
   }
   // ---- column metadata: request, position, conditioning token, logit row offsets, lse
   for (int c = tid; c < NC; c += NT) {
@@ -462,13 +633,15 @@ k_mfma_bias(const MfmaBiasArgs a) {
         if (e[0] > sc || (e[0] == sc && ev < v)) { sc = e[0]; v = ev; }
         if (e[2] > sc2 || (e[2] == sc2 && ev2 < v2)) { sc2 = e[2]; v2 = ev2; }
       }
-      a.rpart[(size_t)wg * a.B + b] = make_float4(sc, __uint_as_float(v), sc2, __uint_as_float(v2));
+      if (v != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b], pack_score(sc, v));
+      if (v2 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b + 1], pack_score(sc2, v2));
     } else {
       float sum = 0.f;
       for (int w = 0; w < TSPLIT; ++w) sum += red[((size_t)w * NC + c) * 4];
       a.tv_part[(size_t)wg * ((size_t)a.B * a.G) + (a.col0 + c)] = sum;
     }
   }
+  if constexpr (MODE == kModeResid) resid_finish(a, reinterpret_cast<int*>(red) + TSPLIT * NC * 4);
 }
 
 template <int NCB, int MODE, bool VEC4>
@@ -534,6 +707,7 @@ dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st
     MfmaBiasArgs a = args;
     a.col0 = args.col0 + c0;
     a.ncols = std::min(group, args.ncols - c0);
+    if (a.mode == kModeResid) a.res_arrive = args.res_arrive + c0 / group;   // per launch
     dspark_status s = DSPARK_OK;
     if (a.mode == kModeDraft)
       s = draft16_supported(a) ? launch_draft16(a, nwg, st) : launch_mode<kModeDraft>(a, nwg, st);

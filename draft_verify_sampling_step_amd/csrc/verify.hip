@@ -1,20 +1,24 @@
 // verify.hip -- rejection-sampling verification [XTL §1; AIMSG concept 2; CSDN roundtable:
 // accept with probability min(1, p_t/p_d)], lossless: the emitted tokens follow the
-// target distribution.
+// target distribution.  Three launches:
 //
 //  1. k_verify_rows    one streaming pass over the target rows 1..ell_b+1 of every request
-//                      (a flattened ragged set; workgroups of unused rows exit at once):
-//                      split-vocabulary (max, sum-exp) partials of T/temperature, and on
-//                      row ell_b+1 the Gumbel race of the bonus token (atomic max).
+//                      (a flattened ragged set that every workgroup maps for itself from
+//                      ell): split-vocabulary (max, sum-exp) partials of T/temperature,
+//                      and on row ell_b+1 the Gumbel race of the bonus token, one packed
+//                      (score, index) slot per slice.
 //  2. k_verify_decide  per request: lse of each row, p_t(x_k), the ordered accept tests
 //                      u * p_d(x_k) < p_t(x_k); n_b; the accepted prefix; the bonus token
-//                      when nothing was rejected, else the residual row j = n_b + 1.
+//                      when nothing was rejected, else the residual row j = n_b + 1; it
+//                      also zeroes the residual pass's winners and arrival counters.
 //  3. residual         for rejected requests, the draft row j is recomputed (Markov bias
 //                      for x_{j-1} plus U_j) and the residual max(0, p_t - p_d) is sampled
-//                      by a Gumbel race on ln rho (bf16 MFMA path for many requests, GEMV
-//                      rows otherwise); a p_t race on the same noise covers the case where
-//                      rounding leaves no positive residual.
-//  4. k_verify_final   writes the residual/fallback token after the accepted prefix.
+//                      by a Gumbel race on ln rho (bf16 matrix cores for many rejections,
+//                      a 16-lanes-per-row path for one or two, GEMV rows for other
+//                      weights); a p_t race on the same noise covers the case where
+//                      rounding leaves no positive residual.  Winners are posted as packed
+//                      atomic maxima; the last workgroup to arrive writes the tokens.
+// For more than kVerifyScanMax requests a plan kernel builds the ragged row list first.
 #include "dspark_dev.h"
 #include "dspark_host.h"
 #include "mfma_bias.h"
@@ -27,18 +31,19 @@ namespace dspark {
 // entries of one row)
 constexpr int kVerifyQuads = 8;
 
+// Requests up to which every workgroup of k_verify_rows maps the ragged row set itself
+// (a prefix sum of ell_b + 1 in LDS, 4 bytes per request); beyond, a plan kernel lists it.
+constexpr int kVerifyScanMax = 8192;
+
 // Flattened ragged row list: rows (b, k) with k <= ell_b + 1, in request order.  One
-// workgroup; writes the list, its length and the number of (row, slice) work items, and
-// clears the bonus-race words.
+// workgroup; writes the list, its length and the number of (row, slice) work items.
 __global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__ ell, int B,
                                                      int G, int nslices,
                                                      int32_t* __restrict__ rows,
-                                                     int32_t* __restrict__ counts,
-                                                     unsigned long long* __restrict__ bonus) {
+                                                     int32_t* __restrict__ counts) {
   __shared__ int32_t scan[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
-  for (int b = tid; b < B; b += 256) bonus[b] = 0ull;
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 256) {
@@ -68,23 +73,68 @@ __global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__
   }
 }
 
+__device__ __forceinline__ int clamp_ell(int L, int G) { return L < 0 ? 0 : (L > G ? G : L); }
+
 // Grid-stride over (row, slice) items.  Rows 1..ell_b: split-vocabulary (max, sum-exp)
 // partials of T/temperature (base 2).  Row ell_b + 1 needs no normaliser (only its bonus
-// token is drawn from it): the Gumbel race over it, merged by a 64-bit atomic max.
+// token is drawn from it): the Gumbel race over it, one packed (score, index) word per
+// slice.  Without a plan (rows == NULL) every workgroup first forms pre[b] = sum over
+// requests before b of (ell + 1) in LDS (dynamic, B + 1 ints) and maps an item by binary
+// search.
 __global__ __launch_bounds__(256, 8) void k_verify_rows(
     const float* __restrict__ T, const int32_t* __restrict__ ell,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, int G, int V,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, int B, int G, int V,
     int slice_len, int nslices, float invT, uint32_t key0, uint32_t key1,
-    float2* __restrict__ part, unsigned long long* __restrict__ bonus) {
+    float2* __restrict__ part, unsigned long long* __restrict__ bonus_part) {
+  extern __shared__ int32_t pre[];
   __shared__ float red[16];
-  const int nitems = counts[1];
+  __shared__ int32_t wsum[4];
   const float s2 = invT * 1.4426950408889634f;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  int nitems;
+  if (rows == nullptr) {
+    const int per = (B + 255) / 256;
+    const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += clamp_ell(ell[b], G) + 1;
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wv; ++w) run += wsum[w];
+    for (int b = b0; b < b1; ++b) {
+      pre[b] = run;
+      run += clamp_ell(ell[b], G) + 1;
+    }
+    if (tid == 0) pre[B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    nitems = pre[B] * nslices;
+  } else {
+    nitems = counts[1];
+  }
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int row = rows[item / nslices], s = item % nslices;
-    const int b = row / (G + 1), k = row % (G + 1) + 1;
-    const int Lb = ell[b];
-    const bool is_bonus = (k == (Lb < 0 ? 0 : (Lb > G ? G : Lb)) + 1);
+    const int rpos = item / nslices, s = item % nslices;
+    int b, row;
+    if (rows == nullptr) {
+      int lo = 0, hi = B - 1;   // the b with pre[b] <= rpos < pre[b + 1] (pre increases)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= rpos) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
+      row = b * (G + 1) + (rpos - pre[b]);
+    } else {
+      row = rows[rpos];
+      b = row / (G + 1);
+    }
+    const int k = row % (G + 1) + 1;
+    const bool is_bonus = (k == clamp_ell(ell[b], G) + 1);
     const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
     const float* trow = T + (size_t)row * V;
     if ((V & 3) == 0 && slice_len == 4 * 256 * kVerifyQuads) {
@@ -152,8 +202,9 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
             }
         }
         best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
-        if (threadIdx.x == 0 && best.i != 0xFFFFFFFFu)
-          atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
+        if (threadIdx.x == 0)
+          bonus_part[(size_t)b * nslices + s] =
+              best.i != 0xFFFFFFFFu ? pack_score(best.s, best.i) : 0ull;
       }
       continue;
     }
@@ -195,8 +246,9 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
       __syncthreads();
     } else {
       best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
-      if (threadIdx.x == 0 && best.i != 0xFFFFFFFFu)
-        atomic_max_u64(&bonus[b], pack_score(best.s, best.i));
+      if (threadIdx.x == 0)
+        bonus_part[(size_t)b * nslices + s] =
+            best.i != 0xFFFFFFFFu ? pack_score(best.s, best.i) : 0ull;
     }
   }
 }
@@ -204,16 +256,22 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
 // One wave per request, one lane per draft row k = lane + 1 (gamma <= 64): all rows of a
 // request are decided at once.  Lane k merges the base-2 slice partials of target row k in
 // slice order into its lse, then takes p_t(x_k) and the accept test u * p_d(x_k) < p_t(x_k).
-// The accepted prefix ends at the first rejected row, found by a ballot.
+// The accepted prefix ends at the first rejected row, found by a ballot.  The bonus token
+// is the best of row ell_b + 1's slice winners.  The residual pass's packed winners and
+// arrival counters (res_best [B][2], res_cnt [ncnt]) start from zero here.
 __global__ __launch_bounds__(256) void k_verify_decide(
     const float* __restrict__ T, const int32_t* __restrict__ tokens,
     const float* __restrict__ logp, const int32_t* __restrict__ ell,
-    const float2* __restrict__ part, const unsigned long long* __restrict__ bonus, int B, int G,
-    int V, int nslices, float invT, uint32_t key0, uint32_t key1,
+    const float2* __restrict__ part, const unsigned long long* __restrict__ bonus_part, int B,
+    int G, int V, int nslices, float invT, uint32_t key0, uint32_t key1,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
-    float* __restrict__ pt_tok, int32_t* __restrict__ jrow, float* __restrict__ lse_t_row) {
+    float* __restrict__ pt_tok, int32_t* __restrict__ jrow, float* __restrict__ lse_t_row,
+    unsigned long long* __restrict__ res_best, int32_t* __restrict__ res_cnt, int ncnt) {
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < ncnt; i += gridDim.x * blockDim.x)
+    res_cnt[i] = 0;
   if (b >= B) return;
+  if (lane < 2) res_best[2 * b + lane] = 0ull;
   const int Lb = ell[b];
   const int L = Lb < 0 ? 0 : (Lb > G ? G : Lb);   // ell outside [0, gamma] is clamped
   const int k = lane + 1;
@@ -246,8 +304,20 @@ __global__ __launch_bounds__(256) void k_verify_decide(
   const float lj = __shfl(lt, j > 0 ? j - 1 : 0, kWave);
   int32_t* out = out_tokens + (size_t)b * (G + 1);
   for (int i = lane; i <= G; i += kWave) out[i] = i < n ? tokens[(size_t)b * G + i] : -1;
+  unsigned long long bw = 0ull;   // the bonus winner: the largest packed slice winner
+  for (int s = lane; s < nslices; s += kWave) {
+    const unsigned long long q = bonus_part[(size_t)b * nslices + s];
+    bw = q > bw ? q : bw;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long q =
+        ((unsigned long long)(uint32_t)__shfl_xor((int)(uint32_t)(bw >> 32), o, kWave) << 32) |
+        (uint32_t)__shfl_xor((int)(uint32_t)bw, o, kWave);
+    bw = q > bw ? q : bw;
+  }
   if (lane == 0) {
-    if (j == 0) out[n] = (int32_t)packed_index(bonus[b]);
+    if (j == 0) out[n] = (int32_t)packed_index(bw);
     n_accept[b] = n;
     jrow[b] = j;
     lse_t_row[b] = j > 0 ? lj : 0.f;
@@ -262,7 +332,8 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
     const int32_t* __restrict__ tokens, const float* __restrict__ lse_d,
     const int32_t* __restrict__ jrow, const float* __restrict__ lse_t_row, int B, int G, int V,
     int r, int slice_len, float invT, uint32_t key0, uint32_t key1,
-    float4* __restrict__ res_part) {
+    unsigned long long* __restrict__ res_best, int32_t* __restrict__ res_cnt,
+    const int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens) {
   extern __shared__ float smem[];
   float* w1s = smem;
   float* bias_s = smem + r;
@@ -300,198 +371,20 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
   }
   b1 = block_cand(b1, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
   b2 = block_cand(b2, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
-  if (tid == 0)
-    res_part[(size_t)s * B + b] =
-        make_float4(b1.s, __uint_as_float(b1.i), b2.s, __uint_as_float(b2.i));
-}
-
-// Thin residual pass, for at most kThinMax requests with a residual row (the usual case:
-// few rejections per round) and bf16 weights of rank kR.  Grid: the nslices slices of the
-// residual partials; 256 threads.  Every workgroup first lists the requests with a residual
-// row in request order and leaves at once unless there are 1..kThinMax of them (the matrix-
-// core pass takes more, and leaves at once in this case).  Each wave then takes four
-// vocabulary rows per step, 16 lanes per row: lane part p holds elements 16 p .. 16 p + 15
-// of W2t[v] and of every listed request's W1[x_{j-1}], the dot products are summed over the
-// 16 lanes, and lane p < n runs the residual and fallback races of request p on row v with
-// the same arithmetic as the row kernel above.
-constexpr int kThinMax = 2;
-
-// Sum over each 16-lane row of the wave by DPP moves (quad swaps 1,0,3,2 and 2,3,0,1, then
-// the half-row and row mirrors): each step adds a commutative pair, so all 16 lanes end
-// with the same total.
-__device__ __forceinline__ float dpp_row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-  return x;
-}
-
-__global__ __launch_bounds__(256) void k_verify_resid_thin(
-    const float* __restrict__ U, const uint16_t* __restrict__ W1,
-    const uint16_t* __restrict__ W2t, const float* __restrict__ T,
-    const int32_t* __restrict__ anchor, const int32_t* __restrict__ tokens,
-    const float* __restrict__ lse_d, const int32_t* __restrict__ jrow,
-    const float* __restrict__ lse_t_row, int B, int G, int V, float invT, uint32_t key0,
-    uint32_t key1, int nslices, float4* __restrict__ res_part) {
-  __shared__ int s_list[kThinMax];
-  __shared__ int s_cnt;
-  __shared__ float4 s_cand[16][kThinMax];   // [wave * 4 + row quad][request]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (wave == 0) {
-    int cnt = 0;
-    for (int c0 = 0; c0 < B; c0 += kWave) {
-      const int bb = c0 + lane;
-      const bool act = bb < B && jrow[bb] > 0;
-      const unsigned long long bal = __ballot(act);
-      const int at = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-      if (act && at < kThinMax) s_list[at] = bb;
-      cnt += __popcll(bal);
+  if (tid == 0) {
+    if (b1.i != 0xFFFFFFFFu) atomic_max_u64(&res_best[2 * b], pack_score(b1.s, b1.i));
+    if (b2.i != 0xFFFFFFFFu) atomic_max_u64(&res_best[2 * b + 1], pack_score(b2.s, b2.i));
+    // the last of the request's slices to arrive writes its token after the prefix (the
+    // residual winner, or the p_t fallback when no residual was positive)
+    const int before = __hip_atomic_fetch_add(&res_cnt[b], 1, __ATOMIC_ACQ_REL,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (before == (int)gridDim.x - 1) {
+      const unsigned long long r1 =
+          __hip_atomic_load(&res_best[2 * b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long r2 =
+          __hip_atomic_load(&res_best[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      out_tokens[(size_t)b * (G + 1) + n_accept[b]] = (int32_t)packed_index(r1 ? r1 : r2);
     }
-    if (lane == 0) s_cnt = cnt;
-  }
-  __syncthreads();
-  const int n = s_cnt;
-  if (n == 0 || n > kThinMax) return;
-
-  const int part = lane & 15, quad = lane >> 4;
-  float w1[kThinMax][16];
-  const float* urow = U;
-  const float* trow = T;
-  float ld = 0.f, lt = 0.f;
-  int myb = 0, myj = 1;
-#pragma unroll
-  for (int i = 0; i < kThinMax; ++i) {
-    int b = 0, j = 1;
-    if (i < n) { b = s_list[i]; j = jrow[b]; }
-    const int prev = clamp_tok((j == 1) ? anchor[b] : tokens[(size_t)b * G + (j - 2)], V);
-    const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(W1 + (size_t)prev * kR + 16 * part);
-    const u32x4_t q0 = wp[0], q1 = wp[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w1[i][2 * e] = __uint_as_float(q0[e] << 16);
-      w1[i][2 * e + 1] = __uint_as_float(q0[e] & 0xFFFF0000u);
-      w1[i][8 + 2 * e] = __uint_as_float(q1[e] << 16);
-      w1[i][8 + 2 * e + 1] = __uint_as_float(q1[e] & 0xFFFF0000u);
-    }
-    if (i == part && i < n) {
-      myb = b;
-      myj = j;
-      urow = U + ((size_t)b * G + (j - 1)) * V;
-      trow = T + ((size_t)b * (G + 1) + (j - 1)) * V;
-      ld = lse_d[(size_t)b * G + (j - 1)];
-      lt = lse_t_row[b];
-    }
-  }
-  const int len = (V + nslices - 1) / nslices;
-  const int vb = blockIdx.x * len, ve = min(V, vb + len);
-  Cand c1{-INFINITY, 0xFFFFFFFFu, 0.f}, c2{-INFINITY, 0xFFFFFFFFu, 0.f};
-  // four row groups per iteration (rows v0 + 16 u + quad), every load issued first; rows
-  // past the slice load row v0 and are not raced
-  for (int v0 = vb + 4 * wave; v0 < ve; v0 += 64) {
-    u32x4_t xq[4][2];
-    float uq[4], tq[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int vu = v0 + 16 * u + quad;
-      const int vv = vu < ve ? vu : v0;
-      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(W2t + (size_t)vv * kR + 16 * part);
-      xq[u][0] = xp[0];
-      xq[u][1] = xp[1];
-      uq[u] = urow[vv];
-      tq[u] = trow[vv];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int v = v0 + 16 * u + quad;
-      float xf[16];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xf[2 * e] = __uint_as_float(xq[u][0][e] << 16);
-        xf[2 * e + 1] = __uint_as_float(xq[u][0][e] & 0xFFFF0000u);
-        xf[8 + 2 * e] = __uint_as_float(xq[u][1][e] << 16);
-        xf[8 + 2 * e + 1] = __uint_as_float(xq[u][1][e] & 0xFFFF0000u);
-      }
-      float d[kThinMax];
-#pragma unroll
-      for (int i = 0; i < kThinMax; ++i) {
-        d[i] = 0.f;
-        if (i < n) {   // uniform
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc = fmaf(xf[e], w1[i][e], acc);
-          d[i] = dpp_row_sum16(acc);
-        }
-      }
-      if (v < ve && part < n) {
-        float bias = d[0];
-#pragma unroll
-        for (int i = 1; i < kThinMax; ++i) bias = part == i ? d[i] : bias;
-        const float zd = (uq[u] + bias) * invT;
-        const float zt = tq[u] * invT;
-        const float rho = fast_exp(zt - lt) - fast_exp(zd - ld);
-        const U4 w = philox10((uint32_t)v >> 2, (uint32_t)myj, (uint32_t)myb, 2u, key0, key1);
-        const uint32_t word =
-            (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-        const float gn = gumbel_from_uniform(word_to_uniform(word));
-        if (rho > 0.f) {
-          const float sc = fast_log(rho) + gn;
-          if (sc > c1.s) c1 = Cand{sc, (uint32_t)v, 0.f};
-        }
-        const float sc2 = zt + gn;
-        if (sc2 > c2.s) c2 = Cand{sc2, (uint32_t)v, 0.f};
-      }
-    }
-  }
-  // merge the candidates of request p over the 16 (wave, row quad) lanes, ties to the lower
-  // index
-  if (part < n)
-    s_cand[wave * 4 + quad][part] =
-        make_float4(c1.s, __uint_as_float(c1.i), c2.s, __uint_as_float(c2.i));
-  __syncthreads();
-  if (tid < n) {
-    float s1 = -INFINITY, s2 = -INFINITY;
-    uint32_t i1 = 0xFFFFFFFFu, i2 = 0xFFFFFFFFu;
-    for (int g = 0; g < 16; ++g) {
-      const float4 p = s_cand[g][tid];
-      const uint32_t pi1 = __float_as_uint(p.y), pi2 = __float_as_uint(p.w);
-      if (p.x > s1 || (p.x == s1 && pi1 < i1)) { s1 = p.x; i1 = pi1; }
-      if (p.z > s2 || (p.z == s2 && pi2 < i2)) { s2 = p.z; i2 = pi2; }
-    }
-    res_part[(size_t)blockIdx.x * B + s_list[tid]] =
-        make_float4(s1, __uint_as_float(i1), s2, __uint_as_float(i2));
-  }
-}
-
-// One wave per request with a residual row: reduce the residual (and fallback p_t) races
-// over the slice partials in a fixed order; write the token after the accepted prefix.
-__global__ __launch_bounds__(256) void k_verify_final(const int32_t* __restrict__ jrow,
-                                                      const int32_t* __restrict__ n_accept,
-                                                      const float4* __restrict__ res_part,
-                                                      int nslices, int B, int G,
-                                                      int32_t* __restrict__ out_tokens) {
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (b >= B || jrow[b] == 0) return;
-  float s1 = -INFINITY, s2 = -INFINITY;
-  uint32_t i1 = 0xFFFFFFFFu, i2 = 0xFFFFFFFFu;
-  for (int s = lane; s < nslices; s += kWave) {
-    const float4 p = res_part[(size_t)s * B + b];
-    const uint32_t pi1 = __float_as_uint(p.y), pi2 = __float_as_uint(p.w);
-    if (p.x > s1 || (p.x == s1 && pi1 < i1)) { s1 = p.x; i1 = pi1; }
-    if (p.z > s2 || (p.z == s2 && pi2 < i2)) { s2 = p.z; i2 = pi2; }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float os1 = __shfl_xor(s1, o, kWave), os2 = __shfl_xor(s2, o, kWave);
-    const uint32_t oi1 = (uint32_t)__shfl_xor((int)i1, o, kWave);
-    const uint32_t oi2 = (uint32_t)__shfl_xor((int)i2, o, kWave);
-    if (os1 > s1 || (os1 == s1 && oi1 < i1)) { s1 = os1; i1 = oi1; }
-    if (os2 > s2 || (os2 == s2 && oi2 < i2)) { s2 = os2; i2 = oi2; }
-  }
-  if (lane == 0) {
-    // no positive residual anywhere (rounding): fall back to the p_t race
-    const uint32_t y = i1 != 0xFFFFFFFFu ? i1 : i2;
-    out_tokens[(size_t)b * (G + 1) + n_accept[b]] = (int32_t)y;
   }
 }
 
@@ -502,26 +395,29 @@ using namespace dspark;
 namespace {
 
 struct VerifyWs {
-  float2* part;
-  int32_t* rows;
-  int32_t* counts;
-  unsigned long long* bonus;
-  float4* res_part;
+  float2* part;                  // [B (G+1)][nslices] base-2 (max, sum) of target rows
+  int32_t* rows;                 // [B (G+1)] ragged row list (plan path only)
+  int32_t* counts;               // [2] its length and item count (plan path only)
+  unsigned long long* bonus;     // [B][nslices] packed winners of the bonus race per slice
+  unsigned long long* res_best;  // [B][2] packed residual / fallback winners
+  int32_t* res_cnt;              // [B] residual arrival counters (per request or launch)
   int32_t* jrow;
   float* lse_t_row;
   size_t bytes;
 };
 
-VerifyWs verify_ws(const dspark_dims* d, int nslices, int nres_slices, void* base) {
+VerifyWs verify_ws(const dspark_dims* d, int nslices, void* base) {
   Carve c(base);
   VerifyWs w;
-  w.part = c.take<float2>((size_t)d->batch * (d->gamma + 1) * nslices);
-  w.rows = c.take<int32_t>((size_t)d->batch * (d->gamma + 1));
+  const size_t B = d->batch;
+  w.part = c.take<float2>(B * (d->gamma + 1) * nslices);
+  w.rows = c.take<int32_t>(B * (d->gamma + 1));
   w.counts = c.take<int32_t>(2);
-  w.bonus = c.take<unsigned long long>((size_t)d->batch);
-  w.res_part = c.take<float4>((size_t)nres_slices * d->batch);
-  w.jrow = c.take<int32_t>(d->batch);
-  w.lse_t_row = c.take<float>(d->batch);
+  w.bonus = c.take<unsigned long long>(B * nslices);
+  w.res_best = c.take<unsigned long long>(2 * B);
+  w.res_cnt = c.take<int32_t>(B);
+  w.jrow = c.take<int32_t>(B);
+  w.lse_t_row = c.take<float>(B);
   w.bytes = align_up(c.off, 256);
   return w;
 }
@@ -537,8 +433,7 @@ constexpr int kVerifySlice = 4 * 256 * kVerifyQuads;
 
 size_t dspark_verify_workspace(const dspark_dims* d) {
   const int ns = (d->vocab + kVerifySlice - 1) / kVerifySlice;
-  const int nr = std::max(resid_slices(d, true), resid_slices(d, false));
-  return verify_ws(d, ns, nr, nullptr).bytes;
+  return verify_ws(d, ns, nullptr).bytes;
 }
 
 extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, const void* W1,
@@ -560,36 +455,40 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   const int nsl = (V + kVerifySlice - 1) / kVerifySlice;
   const bool mfma = mfma_bias_supported(B, r, wdt);
   const int nres = resid_slices(dm, mfma);
-  VerifyWs w = verify_ws(dm, nsl, nres, ws);
+  VerifyWs w = verify_ws(dm, nsl, ws);
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
   if (mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
-  hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
-                     w.counts, w.bonus);
+  // 1. target rows (with the ragged row list formed in every workgroup, or listed by the
+  //    plan kernel for very large batches)
+  const bool plan = B > kVerifyScanMax;
+  if (plan)
+    hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
+                       w.counts);
   const long long max_items = (long long)B * (G + 1) * nsl;
   const int grid = (int)std::min<long long>(max_items, 2048);
-  hipLaunchKernelGGL(k_verify_rows, dim3(grid), dim3(256), 0, st, T, ell, w.rows, w.counts, G,
-                     V, kVerifySlice, nsl, invT, key0, key1, w.part, w.bonus);
+  const size_t sh_rows = plan ? 0 : sizeof(int32_t) * ((size_t)B + 1);
+  hipLaunchKernelGGL(k_verify_rows, dim3(grid), dim3(256), sh_rows, st, T, ell,
+                     plan ? w.rows : nullptr, plan ? w.counts : nullptr, B, G, V, kVerifySlice,
+                     nsl, invT, key0, key1, w.part, w.bonus);
+  // 2. decisions (and the residual pass's winners and counters reset)
   hipLaunchKernelGGL(k_verify_decide, dim3((B + 3) / 4), dim3(256), 0, st, T, tokens, logp, ell,
                      w.part, w.bonus, B, G, V, nsl, invT, key0, key1, n_accept, out_tokens,
-                     pt_tok, w.jrow, w.lse_t_row);
+                     pt_tok, w.jrow, w.lse_t_row, w.res_best, w.res_cnt, B);
+  // 3. the residual draws; the last workgroup to finish writes the tokens
   if (mfma) {
     MfmaBiasArgs a{};
     a.mode = kModeResid;
     a.U = U; a.W1 = (const uint16_t*)W1; a.W2t = (const uint16_t*)W2t;
     a.anchor = anchor; a.tokens = tokens; a.T = T; a.lse_d = lse; a.lse_t_row = w.lse_t_row;
-    a.jrow = w.jrow; a.rpart = w.res_part;
+    a.jrow = w.jrow; a.res_best = w.res_best; a.res_arrive = w.res_cnt;
+    a.n_accept = n_accept; a.out_tokens = out_tokens;
     a.B = B; a.G = G; a.V = V; a.r = r; a.k = 0; a.invT = invT; a.key0 = key0; a.key1 = key1;
     a.ncols = B; a.col0 = 0;
-    // up to kThinMax residual rows take the thin pass; the matrix-core pass leaves at once
-    // then (and the thin one when there are more)
-    const bool thin = B <= 256;
-    a.thin_max = thin ? kThinMax : 0;
-    if (thin)
-      hipLaunchKernelGGL(k_verify_resid_thin, dim3(nres), dim3(256), 0, st, U,
-                         (const uint16_t*)W1, (const uint16_t*)W2t, T, anchor, tokens, lse,
-                         w.jrow, w.lse_t_row, B, G, V, invT, key0, key1, nres, w.res_part);
+    // one or two residual rows take the thin path inside the same kernel (one launch
+    // covers every column up to 256 requests)
+    a.thin_max = B <= mfma_column_group(kModeResid) ? kResidThinMax : 0;
     if (launch_mfma_bias(a, nres, st) != DSPARK_OK) return DSPARK_E_HIP;
   } else {
     const RowSlices rr = row_slices(V, B);
@@ -597,13 +496,13 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
     if (wdt == DSPARK_BF16)
       hipLaunchKernelGGL(k_verify_resid_row<uint16_t>, dim3(rr.count, B), dim3(256), sh, st, U,
                          (const uint16_t*)W1, (const uint16_t*)W2t, T, anchor, tokens, lse,
-                         w.jrow, w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_part);
+                         w.jrow, w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_best,
+                         w.res_cnt, n_accept, out_tokens);
     else
       hipLaunchKernelGGL(k_verify_resid_row<float>, dim3(rr.count, B), dim3(256), sh, st, U,
                          (const float*)W1, (const float*)W2t, T, anchor, tokens, lse, w.jrow,
-                         w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_part);
+                         w.lse_t_row, B, G, V, r, rr.len, invT, key0, key1, w.res_best,
+                         w.res_cnt, n_accept, out_tokens);
   }
-  hipLaunchKernelGGL(k_verify_final, dim3((B + 3) / 4), dim3(256), 0, st, w.jrow, n_accept,
-                     w.res_part, nres, B, G, out_tokens);
   return launch_status();
 }

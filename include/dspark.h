@@ -330,6 +330,20 @@ dspark_status dspark_closed_loop(const dspark_dims* dims, const float* U, const 
                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The closed loop's stand-in target on its own (not a step of the method; measurement and
+ * test support): T [B][gamma+1][V] fp32 with
+ *   T[b][j][v] = U[b][min(j, gamma-1)][v] + target_sigma sqrt(3) (2 u - 1),
+ *   u = u(target_seed, prev, 0, 3, v),   prev = anchor[b] (j = 0) or tokens[b][j-1],
+ * exactly the logits dspark_closed_loop verifies against, so that the target side of a
+ * round can be timed apart from the loop.  U, anchor, tokens as for dspark_draft_markov;
+ * target_sigma >= 0 (else DSPARK_E_VALUE).  Needs no workspace.
+ */
+dspark_status dspark_markov_target(const dspark_dims* dims, const float* U,
+                                   const int32_t* anchor, const int32_t* tokens,
+                                   float target_sigma, uint64_t target_seed, float* T,
+                                   void* stream);
+
+/*
  * Distribution-matching training loss of the draft and confidence heads, forward and
  * backward [XTL §9: a cross-entropy term on the true next token, an L1 (total-variation)
  * term between the draft and target distributions, a binary cross-entropy term training

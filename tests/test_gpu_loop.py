@@ -144,3 +144,18 @@ def test_closed_loop_is_deterministic():
                 x = x.view(torch.int32 if x.element_size() == 4 else torch.int64)
                 y = y.view(x.dtype)
             assert torch.equal(x, y), k
+
+
+@pytest.mark.parametrize("V", [1001, 4096])
+def test_stand_in_target_matches_oracle(V):
+    """The loop's stand-in target exported on its own (used to time the target side of a
+    round apart from the loop): every entry against the oracle's fp64 definition, within the
+    fp32 rounding of one add and one multiply."""
+    cfg = workload.custom(name="tgt", B=5, gamma=3, V=V, r=16, d=8)
+    inp = workload.generate(cfg, 2)
+    tokens = np.random.default_rng(V).integers(0, V, size=(cfg.B, cfg.gamma)).astype(np.int32)
+    D = DeviceInputs(inp)
+    T_g = host(ds.dspark_markov_target(D.U, D.anchor, ds.to_device(tokens), 0.7, 0xC105ED))
+    T_o = oracle.markov_target(inp.U, inp.anchor, tokens, 0.7, 0xC105ED)
+    err = np.abs(T_g.astype(np.float64) - T_o)
+    assert np.all(err <= 4e-7 * (np.abs(T_o) + 1.0)), err.max()
