@@ -101,6 +101,33 @@ __device__ __forceinline__ void atomic_max_u64(unsigned long long* p, unsigned l
 }
 
 // ------------------------------------------------------------------------------------
+// Cross-workgroup hand-off without hot spots: workgroup w of a launch posts its packed
+// winners with atomic maxima into sub-slot w % kSubSlots (so at most n / kSubSlots
+// workgroups share an address), then counts itself in on a two-level counter; exactly one
+// workgroup, the last to arrive, gets true and may read the merged sub-slots.  Each wave
+// waits for its own atomics before the workgroup barrier that precedes the count, and all
+// of these are device-scope atomics, performed at the device's coherence point in that
+// order.  `c` is a block of kArriveInts zeroed counters (9 counters 128 bytes apart).
+// ------------------------------------------------------------------------------------
+constexpr int kSubSlots = 8;
+constexpr int kArriveInts = 9 * 32;
+
+__device__ __forceinline__ bool arrive_last(int32_t* c, int w, int n) {
+  const int sub = w % kSubSlots;
+  const int in_sub = n / kSubSlots + (sub < n % kSubSlots ? 1 : 0);
+  const int nsub = n < kSubSlots ? n : kSubSlots;
+  if (__hip_atomic_fetch_add(c + 32 * sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+      in_sub - 1)
+    return false;
+  return __hip_atomic_fetch_add(c + 32 * kSubSlots, 1, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) == nsub - 1;
+}
+
+__device__ __forceinline__ unsigned long long atomic_load_u64(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------------------------
 // online softmax state (running max m, running sum l of exp(z - m))
 // ------------------------------------------------------------------------------------
 struct ML { float m, l; };

@@ -42,11 +42,11 @@ struct MfmaBiasArgs {
   const unsigned long long* best_prev;   // draft: packed winners of position k-1
   unsigned long long* best_cur;          // draft: packed winners of position k (atomic max)
   float2* part;                          // draft: [slices][B] base-2 softmax state (max, sum)
-  unsigned long long* res_best;          // resid: [B][2] packed (score, index) winners of
-                                         //        the residual race and of the p_t
-                                         //        fallback race, zero before the launch
-  int* res_arrive;                       // resid: arrival counter of this launch's
-                                         //        workgroups, zero before the launch
+  unsigned long long* res_best;          // resid: [kSubSlots][B][2] packed (score, index)
+                                         //        winners of the residual race and of the
+                                         //        p_t fallback race, zero before the launch
+  int* res_arrive;                       // resid: kArriveInts arrival counters of this
+                                         //        launch's workgroups, zero before it
   const int32_t* n_accept;               // resid: accepted prefix length per request
   int32_t* out_tokens;                   // resid: [B][G+1]; the last workgroup to finish
                                          //        writes each residual token at n_accept

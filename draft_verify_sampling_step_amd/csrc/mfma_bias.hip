@@ -200,8 +200,9 @@ __device__ __forceinline__ void resid_thin(const MfmaBiasArgs& a, const int* cli
       if (p.z > ss2 || (p.z == ss2 && pi2 < i2)) { ss2 = p.z; i2 = pi2; }
     }
     const int b = a.col0 + clist[tid];
-    if (i1 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b], pack_score(s1, i1));
-    if (i2 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b + 1], pack_score(ss2, i2));
+    unsigned long long* slot = a.res_best + ((size_t)(blockIdx.x % kSubSlots) * a.B + b) * 2;
+    if (i1 != 0xFFFFFFFFu) atomic_max_u64(&slot[0], pack_score(s1, i1));
+    if (i2 != 0xFFFFFFFFu) atomic_max_u64(&slot[1], pack_score(ss2, i2));
   }
 }
 
@@ -212,20 +213,20 @@ __device__ __forceinline__ void resid_thin(const MfmaBiasArgs& a, const int* cli
 __device__ __forceinline__ void resid_finish(const MfmaBiasArgs& a, int* s_flag) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's atomics have completed
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int before = __hip_atomic_fetch_add(a.res_arrive, 1, __ATOMIC_ACQ_REL,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = before == (int)gridDim.x - 1;
-  }
+  if (threadIdx.x == 0) *s_flag = arrive_last(a.res_arrive, blockIdx.x, gridDim.x);
   __syncthreads();
   if (!*s_flag) return;
   for (int c = threadIdx.x; c < a.ncols; c += blockDim.x) {
     const int b = a.col0 + c;
     if (a.jrow[b] == 0) continue;
-    const unsigned long long r1 =
-        __hip_atomic_load(&a.res_best[2 * b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long r2 =
-        __hip_atomic_load(&a.res_best[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long r1 = 0ull, r2 = 0ull;
+#pragma unroll
+    for (int q = 0; q < kSubSlots; ++q) {
+      const unsigned long long* slot = a.res_best + ((size_t)q * a.B + b) * 2;
+      const unsigned long long x1 = atomic_load_u64(&slot[0]), x2 = atomic_load_u64(&slot[1]);
+      r1 = x1 > r1 ? x1 : r1;
+      r2 = x2 > r2 ? x2 : r2;
+    }
     const uint32_t y = packed_index(r1 != 0ull ? r1 : r2);
     a.out_tokens[(size_t)b * (a.G + 1) + a.n_accept[b]] = (int32_t)y;
   }
@@ -633,8 +634,9 @@ k_mfma_bias(const MfmaBiasArgs a) {
         if (e[0] > sc || (e[0] == sc && ev < v)) { sc = e[0]; v = ev; }
         if (e[2] > sc2 || (e[2] == sc2 && ev2 < v2)) { sc2 = e[2]; v2 = ev2; }
       }
-      if (v != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b], pack_score(sc, v));
-      if (v2 != 0xFFFFFFFFu) atomic_max_u64(&a.res_best[2 * b + 1], pack_score(sc2, v2));
+      unsigned long long* slot = a.res_best + ((size_t)(wg % kSubSlots) * a.B + b) * 2;
+      if (v != 0xFFFFFFFFu) atomic_max_u64(&slot[0], pack_score(sc, v));
+      if (v2 != 0xFFFFFFFFu) atomic_max_u64(&slot[1], pack_score(sc2, v2));
     } else {
       float sum = 0.f;
       for (int w = 0; w < TSPLIT; ++w) sum += red[((size_t)w * NC + c) * 4];
@@ -707,7 +709,7 @@ dspark_status launch_mfma_bias(const MfmaBiasArgs& args, int nwg, hipStream_t st
     MfmaBiasArgs a = args;
     a.col0 = args.col0 + c0;
     a.ncols = std::min(group, args.ncols - c0);
-    if (a.mode == kModeResid) a.res_arrive = args.res_arrive + c0 / group;   // per launch
+    if (a.mode == kModeResid) a.res_arrive = args.res_arrive + (c0 / group) * kArriveInts;
     dspark_status s = DSPARK_OK;
     if (a.mode == kModeDraft)
       s = draft16_supported(a) ? launch_draft16(a, nwg, st) : launch_mode<kModeDraft>(a, nwg, st);

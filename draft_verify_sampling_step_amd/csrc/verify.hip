@@ -270,8 +270,10 @@ __global__ __launch_bounds__(256) void k_verify_decide(
   const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < ncnt; i += gridDim.x * blockDim.x)
     res_cnt[i] = 0;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < 2 * kSubSlots * B;
+       i += gridDim.x * blockDim.x)
+    res_best[i] = 0ull;
   if (b >= B) return;
-  if (lane < 2) res_best[2 * b + lane] = 0ull;
   const int Lb = ell[b];
   const int L = Lb < 0 ? 0 : (Lb > G ? G : Lb);   // ell outside [0, gamma] is clamped
   const int k = lane + 1;
@@ -372,17 +374,20 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
   b1 = block_cand(b1, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
   b2 = block_cand(b2, red, reinterpret_cast<uint32_t*>(red + 4), red + 8);
   if (tid == 0) {
-    if (b1.i != 0xFFFFFFFFu) atomic_max_u64(&res_best[2 * b], pack_score(b1.s, b1.i));
-    if (b2.i != 0xFFFFFFFFu) atomic_max_u64(&res_best[2 * b + 1], pack_score(b2.s, b2.i));
+    unsigned long long* slot = res_best + ((size_t)(s % kSubSlots) * B + b) * 2;
+    if (b1.i != 0xFFFFFFFFu) atomic_max_u64(&slot[0], pack_score(b1.s, b1.i));
+    if (b2.i != 0xFFFFFFFFu) atomic_max_u64(&slot[1], pack_score(b2.s, b2.i));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // the last of the request's slices to arrive writes its token after the prefix (the
     // residual winner, or the p_t fallback when no residual was positive)
-    const int before = __hip_atomic_fetch_add(&res_cnt[b], 1, __ATOMIC_ACQ_REL,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (before == (int)gridDim.x - 1) {
-      const unsigned long long r1 =
-          __hip_atomic_load(&res_best[2 * b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned long long r2 =
-          __hip_atomic_load(&res_best[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrive_last(res_cnt + (size_t)b * kArriveInts, s, gridDim.x)) {
+      unsigned long long r1 = 0ull, r2 = 0ull;
+      for (int q = 0; q < kSubSlots; ++q) {
+        const unsigned long long* sl = res_best + ((size_t)q * B + b) * 2;
+        const unsigned long long x1 = atomic_load_u64(&sl[0]), x2 = atomic_load_u64(&sl[1]);
+        r1 = x1 > r1 ? x1 : r1;
+        r2 = x2 > r2 ? x2 : r2;
+      }
       out_tokens[(size_t)b * (G + 1) + n_accept[b]] = (int32_t)packed_index(r1 ? r1 : r2);
     }
   }
@@ -399,8 +404,8 @@ struct VerifyWs {
   int32_t* rows;                 // [B (G+1)] ragged row list (plan path only)
   int32_t* counts;               // [2] its length and item count (plan path only)
   unsigned long long* bonus;     // [B][nslices] packed winners of the bonus race per slice
-  unsigned long long* res_best;  // [B][2] packed residual / fallback winners
-  int32_t* res_cnt;              // [B] residual arrival counters (per request or launch)
+  unsigned long long* res_best;  // [kSubSlots][B][2] packed residual / fallback winners
+  int32_t* res_cnt;              // [B][kArriveInts] arrival counters (per request or launch)
   int32_t* jrow;
   float* lse_t_row;
   size_t bytes;
@@ -414,8 +419,8 @@ VerifyWs verify_ws(const dspark_dims* d, int nslices, void* base) {
   w.rows = c.take<int32_t>(B * (d->gamma + 1));
   w.counts = c.take<int32_t>(2);
   w.bonus = c.take<unsigned long long>(B * nslices);
-  w.res_best = c.take<unsigned long long>(2 * B);
-  w.res_cnt = c.take<int32_t>(B);
+  w.res_best = c.take<unsigned long long>(2 * kSubSlots * B);
+  w.res_cnt = c.take<int32_t>(B * kArriveInts);
   w.jrow = c.take<int32_t>(B);
   w.lse_t_row = c.take<float>(B);
   w.bytes = align_up(c.off, 256);
@@ -475,7 +480,7 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   // 2. decisions (and the residual pass's winners and counters reset)
   hipLaunchKernelGGL(k_verify_decide, dim3((B + 3) / 4), dim3(256), 0, st, T, tokens, logp, ell,
                      w.part, w.bonus, B, G, V, nsl, invT, key0, key1, n_accept, out_tokens,
-                     pt_tok, w.jrow, w.lse_t_row, w.res_best, w.res_cnt, B);
+                     pt_tok, w.jrow, w.lse_t_row, w.res_best, w.res_cnt, B * kArriveInts);
   // 3. the residual draws; the last workgroup to finish writes the tokens
   if (mfma) {
     MfmaBiasArgs a{};
