@@ -43,8 +43,8 @@ def parse():
                     help="target length of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy three times (the "
-                         "reference for scaling hardware byte counters)")
+                    help="first run a plain 1 GiB device-to-device copy three times (the "
+                         "reference for scaling hardware byte counters), then the benchmark")
     return ap.parse_args()
 
 
@@ -71,8 +71,9 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
-        return
+        del src, dst
+        torch.cuda.empty_cache()
+        log(f"copy calibration: 3 device copies of {n} bytes")
 
     if not os.path.exists(ds.LIB_PATH):   # fail loudly before any work
         raise RuntimeError(f"{ds.LIB_PATH} is missing: build it first (__graft_entry__.build())")
