@@ -168,6 +168,11 @@ MULTI_TILE = {
     "mt_b64_g3": workload.custom(name="mt_b64_g3", B=64, gamma=3, V=131072, r=256, d=64,
                                  bf16=True, wsigma=0.5, logits="zipf", sigma_mix=True,
                                  table="serve"),
+    # 16-column draft kernel with a ragged last tile (V % 32 == 4: one run of four live
+    # rows) and workgroups of 8 and 9 steps
+    "mt_b100_v131076": workload.custom(name="mt_b100_v131076", B=100, gamma=2, V=131076,
+                                       r=256, d=64, bf16=True, wsigma=0.5, logits="zipf",
+                                       table="serve"),
     # 16-column draft kernel, 16-wave workgroups; TV over 400 columns (the last 16 on the
     # 32-column kernel)
     "mt_b200_g2_t07": workload.custom(name="mt_b200_g2_t07", B=200, gamma=2, V=131072, r=256,
