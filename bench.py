@@ -436,7 +436,9 @@ def main():
         },
         "roofline": {
             "kernel": draft_kernel_name(B, V, r) + ": fused bias + softmax + Gumbel race "
-                      "over W2t and the B base-logit rows, one draft position per launch",
+                      "over W2t and the B base-logit rows, "
+                      + ("one draft position per launch" if kern_pos == 1 else
+                         f"{kern_pos:g} draft positions per launch"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -622,6 +624,9 @@ def timed_verify(ds, args, stream, use_graph, U, W1, W2t, anchor, tokens, logp, 
 
 def draft_kernel_name(B: int, V: int, r: int) -> str:
     """The draft position kernel the library dispatches for this shape (bf16 weights)."""
+    if r == 256 and B <= 16 and V % 4 == 0 and V <= 256 * 40 * 16:
+        return "k_draft_resident (W2t held in accumulation registers and LDS for all gamma " \
+            "positions, one cooperative launch per draft call)"
     if r == 256 and 32 < B <= 256 and V % 4 == 0:
         return ("k_draft16<8, false>" if B <= 128 else "k_draft16<16, false>") + \
             " (16x16x32 bf16 MFMA, 16-column waves)"

@@ -34,9 +34,15 @@ def _hipcc() -> str:
     return "hipcc"
 
 
+# Per-file device code generation options.  resident.hip holds W2t in accumulation registers
+# and feeds them to the matrix cores as the A operand; with the VGPR form of MFMA its
+# accumulators and epilogue stay in ordinary vector registers (no copies between the files).
+FILE_FLAGS = {"resident.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                      if "is not a recognized feature" not in line and line.strip())

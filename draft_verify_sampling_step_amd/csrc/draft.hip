@@ -18,6 +18,7 @@
 #include "dspark_host.h"
 #include "gemv.h"
 #include "mfma_bias.h"
+#include "resident.h"
 #include "rowbias.h"
 
 namespace dspark {
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(256) void k_draft_final(
     const float2* __restrict__ part, const unsigned long long* __restrict__ best,
     const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
     const int32_t* __restrict__ anchor, const int32_t* __restrict__ forced, int B, int G, int V,
-    int r, float invT, int nslices, int32_t* __restrict__ tokens, float* __restrict__ logp,
-    float* __restrict__ lse) {
+    int r, float invT, int nslices, const uint32_t* __restrict__ fault,
+    int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
   __shared__ float red[4][8][3];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int noct = (B + 7) / 8;
@@ -169,9 +170,12 @@ __global__ __launch_bounds__(256) void k_draft_final(
   const float lz = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
   const float zx = (U[((size_t)b * G + kk) * V + x] + dot) * invT;
   const size_t o = (size_t)b * G + kk;
-  tokens[o] = won ? (int32_t)idx : -1;
-  lse[o] = lz;
-  logp[o] = won ? zx - lz : __builtin_nanf("");
+  // a draft kernel that gave up a bounded wait has left the slots incomplete
+  const bool failed =
+      fault && __hip_atomic_load(fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+  tokens[o] = won && !failed ? (int32_t)idx : -1;
+  lse[o] = failed ? __builtin_nanf("") : lz;
+  logp[o] = won && !failed ? zx - lz : __builtin_nanf("");
 }
 
 }  // namespace dspark
@@ -182,18 +186,25 @@ namespace {
 
 struct DraftPlan {
   bool mfma;
+  bool resident;   // all positions in one launch, W2t on chip (resident.hip)
   bool gemv;       // the streaming kernel for few requests (gemv.hip)
   int nslices;     // partial slots per (position, request)
   int slice_len;   // row path only
   GemvPlan gp;
+  ResidentPlan rp;
 };
 
 DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   DraftPlan p{};
   p.mfma = mfma_bias_supported(d->batch, d->rank, wdt);
-  p.gemv = !p.mfma && draft_gemv_supported(d->batch, d->vocab, d->rank, wdt);
+  p.rp = p.mfma ? ResidentPlan{false, 0} : resident_plan(d->batch, d->vocab, d->rank, wdt);
+  p.resident = p.rp.ok;
+  p.gemv = !p.mfma && !p.resident && draft_gemv_supported(d->batch, d->vocab, d->rank, wdt);
   if (p.mfma) {
     p.nslices = mfma_grid(d->vocab, d->batch, kModeDraft);
+    p.slice_len = 0;
+  } else if (p.resident) {
+    p.nslices = p.rp.nwg;
     p.slice_len = 0;
   } else if (p.gemv) {
     p.gp = draft_gemv_plan(d->vocab);
@@ -207,21 +218,44 @@ DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   return p;
 }
 
-size_t draft_ws(const dspark_dims* d, int nslices, unsigned long long** best, float2** part,
-                void* base) {
+// Scratch of a draft call: the packed winners [G][B], then the resident kernel's arrival
+// counters [G][kArriveInts], winner slots [G][B][nres] and fault word, all cleared by one
+// fill (in that order, contiguous, `nclear` 64-bit words; the counters and slots only when
+// the resident kernel runs, nres > 0), then the softmax partials [G][nslices][B].
+struct DraftWs {
+  unsigned long long* best;
+  int32_t* cnt;
+  unsigned long long* slot;
+  uint32_t* fault;
+  float2* part;
+  size_t nclear;
+  size_t bytes;
+};
+
+DraftWs draft_ws(const dspark_dims* d, int nslices, int nres, void* base) {
+  DraftWs w;
   Carve c(base);
-  *best = c.take<unsigned long long>((size_t)d->gamma * d->batch);
-  *part = c.take<float2>((size_t)d->gamma * nslices * d->batch);
-  return align_up(c.off, 256);
+  const size_t G = (size_t)d->gamma, B = (size_t)d->batch;
+  static_assert(kArriveInts % 2 == 0, "counters pack into 64-bit words");
+  const size_t ncnt = nres > 0 ? G * kArriveInts : 0;
+  const size_t nslot = G * B * (size_t)nres;
+  w.nclear = G * B + ncnt / 2 + nslot + 1;
+  w.best = c.take<unsigned long long>(w.nclear);
+  w.cnt = w.best ? reinterpret_cast<int32_t*>(w.best + G * B) : nullptr;
+  w.slot = w.cnt ? reinterpret_cast<unsigned long long*>(w.cnt + ncnt) : nullptr;
+  w.fault = w.slot ? reinterpret_cast<uint32_t*>(w.slot + nslot) : nullptr;
+  w.part = c.take<float2>(G * nslices * B);
+  w.bytes = align_up(c.off, 256);
+  return w;
 }
 
 }  // namespace
 
 size_t dspark_draft_workspace(const dspark_dims* d) {
-  unsigned long long* b;
-  float2* p;
-  const int ns = std::max(row_slices(d->vocab, d->batch).count, mfma_workgroups(d->vocab));
-  return draft_ws(d, ns, &b, &p, nullptr);
+  int ns = std::max(row_slices(d->vocab, d->batch).count, mfma_workgroups(d->vocab));
+  const int nres =
+      d->batch <= kResMaxBatch ? std::min((d->vocab + 15) / 16, kResMaxWorkgroups) : 0;
+  return draft_ws(d, std::max(ns, nres), nres, nullptr).bytes;
 }
 
 namespace {
@@ -233,17 +267,28 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
                         const int32_t* forced, float temperature, uint64_t seed,
                         int32_t* tokens, float* logp, float* lse, void* ws, hipStream_t st) {
   const int B = dm->batch, G = dm->gamma, V = dm->vocab, r = dm->rank;
-  unsigned long long* best;
-  float2* part;
-  draft_ws(dm, plan.nslices, &best, &part, ws);
+  const DraftWs w = draft_ws(dm, plan.nslices, plan.resident ? plan.nslices : 0, ws);
+  unsigned long long* best = w.best;
+  float2* part = w.part;
   const float invT = 1.0f / temperature;
   const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
   if (plan.mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
+  if (plan.resident && resident_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
-  // the winners start at zero (below every packed candidate) on every call
-  hipLaunchKernelGGL(k_fill_u64, dim3(std::min(1024, (G * B + 255) / 256)), dim3(256), 0, st,
-                     best, (size_t)G * B, 0ull);
-  for (int k = 1; k <= G; ++k) {
+  // the winners (zero is below every packed candidate), arrival counters and fault word
+  // start at zero on every call
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)std::min<size_t>(1024, (w.nclear + 255) / 256)),
+                     dim3(256), 0, st, best, w.nclear, 0ull);
+  if (plan.resident) {
+    prof_begin(st);
+    const dspark_status ls =
+        launch_draft_resident(plan.rp, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor,
+                              forced, best, part, w.cnt, w.slot, w.fault, B, G, V, invT, key0,
+                              key1, st);
+    prof_end(st, ls == DSPARK_OK ? G : -1);
+    if (ls != DSPARK_OK) return DSPARK_E_HIP;
+  }
+  for (int k = 1; k <= G && !plan.resident; ++k) {
     const unsigned long long* bprev = k > 1 ? best + (size_t)(k - 2) * B : nullptr;
     unsigned long long* bcur = best + (size_t)(k - 1) * B;
     float2* pk = part + (size_t)(k - 1) * plan.nslices * B;
@@ -283,11 +328,12 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
   if (wdt == DSPARK_BF16)
     hipLaunchKernelGGL(k_draft_final<uint16_t>, dim3(fblocks), dim3(256), 0, st, part,
                        best, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced, B, G,
-                       V, r, invT, plan.nslices, tokens, logp, lse);
+                       V, r, invT, plan.nslices, plan.resident ? w.fault : nullptr, tokens,
+                       logp, lse);
   else
     hipLaunchKernelGGL(k_draft_final<float>, dim3(fblocks), dim3(256), 0, st, part, best,
                        U, (const float*)W1, (const float*)W2t, anchor, forced, B, G, V, r, invT,
-                       plan.nslices, tokens, logp, lse);
+                       plan.nslices, nullptr, tokens, logp, lse);
   return launch_status();
 }
 
@@ -354,9 +400,8 @@ extern "C" dspark_status dspark_draft_markov_noalloc(const dspark_dims* dm, cons
       draft_validate(dm, U, W1, W2t, wdt, anchor, tokens, logp, lse, temperature);
   if (v != DSPARK_OK) return v;
   const DraftPlan plan = draft_plan(dm, wdt);
-  unsigned long long* b;
-  float2* p;
-  if (draft_ws(dm, plan.nslices, &b, &p, nullptr) > kDraftStaticScratch)
+  if (draft_ws(dm, plan.nslices, plan.resident ? plan.nslices : 0, nullptr).bytes >
+      kDraftStaticScratch)
     return DSPARK_E_WORKSPACE;
   void* ws = nullptr;
   const dspark_status sc = static_scratch(&ws);

@@ -185,11 +185,21 @@ MULTI_TILE = {
     "mt_b150_odd": workload.custom(name="mt_b150_odd", B=150, gamma=2, V=131073, r=256,
                                    d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
                                    table="serve"),
-    # the streaming kernel for few requests: 586 workgroups of one 224-row chunk each
+    # the resident draft for few requests: one workgroup per compute unit, 32 blocks of 16
+    # rows each, all in accumulation registers
     "mt_gemv_b3_g4": workload.custom(name="mt_gemv_b3", B=3, gamma=4, V=131072, r=256, d=64,
                                      bf16=True, wsigma=0.5, logits="zipf", sigma_mix=True,
                                      table="serve"),
-    # ... and with two chunks per workgroup (more than 768 chunks)
+    # ... with 7 or 8 blocks per workgroup in LDS and a ragged last block (V % 16 == 4)
+    "mt_res_b5_v160004": workload.custom(name="mt_res_b5", B=5, gamma=3, V=160004, r=256,
+                                         d=64, bf16=True, wsigma=0.5, logits="zipf",
+                                         table="serve"),
+    # ... at its largest vocabulary (40 blocks per workgroup, 8 in LDS) and 16 requests
+    "mt_res_b16_v163840": workload.custom(name="mt_res_b16", B=16, gamma=2, V=163840, r=256,
+                                          d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+                                          table="serve"),
+    # the streaming kernel for few requests, beyond the resident draft's vocabulary: two
+    # 224-row chunks per workgroup (more than 768 chunks)
     "mt_gemv_b2_v262144": workload.custom(name="mt_gemv_b2", B=2, gamma=3, V=262144, r=256,
                                           d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
                                           table="serve"),
