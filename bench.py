@@ -407,8 +407,9 @@ def main():
     achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
     strict_bytes = int(round((w2t_bytes / G + B * V * 4) * kern_pos))
     strict_achieved = strict_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic(cfg.name)
-    mfma_util = measured_mfma_util(cfg.name)
+    ksrc = kernel_sources(B, V, r)
+    traffic = measured_traffic(cfg.name, ksrc)
+    mfma_util = measured_mfma_util(cfg.name, ksrc)
 
     rec = {
         "metric": METRIC,
@@ -518,10 +519,15 @@ def main():
 
 
 # the dominant kernel's source files, hashed in this order (the counter summary names it)
-KERNEL_SOURCES = ("mfma16.hip", "mfma_common.h")
+def kernel_sources(B: int, V: int, r: int):
+    """The sources of the draft kernel this shape runs, whose sha256 binds the committed
+    counter summaries to it."""
+    if draft_kernel_name(B, V, r).startswith("k_draft_resident"):
+        return ("resident.hip", "mfma_common.h")
+    return ("mfma16.hip", "mfma_common.h")
 
 
-def measured_traffic(workload_name: str):
+def measured_traffic(workload_name: str, sources):
     """HBM bytes per launch of the draft position kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None when
     there is none for this workload or the kernel source has changed since it was taken."""
@@ -530,7 +536,7 @@ def measured_traffic(workload_name: str):
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"draft_position_{workload_name}_pmc.md")
     csrc = os.path.join(here, "draft_verify_sampling_step_amd", "csrc")
-    srcs = [os.path.join(csrc, f) for f in KERNEL_SOURCES]
+    srcs = [os.path.join(csrc, f) for f in sources]
     if not (os.path.exists(path) and all(os.path.exists(f) for f in srcs)):
         return None
     text = open(path).read()
@@ -546,14 +552,14 @@ def measured_traffic(workload_name: str):
     return int(m_b.group(1))
 
 
-def _sha_bound_figure(path: str, pattern: str):
+def _sha_bound_figure(path: str, pattern: str, sources):
     """A figure from a committed counter summary, or None when the summary is missing or the
     draft kernel's source has changed since it was taken (its sha256 is recorded in it)."""
     import hashlib
     import re
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "draft_verify_sampling_step_amd", "csrc")
-    srcs = [os.path.join(csrc, f) for f in KERNEL_SOURCES]
+    srcs = [os.path.join(csrc, f) for f in sources]
     if not (os.path.exists(path) and all(os.path.exists(f) for f in srcs)):
         return None
     text = open(path).read()
@@ -567,12 +573,12 @@ def _sha_bound_figure(path: str, pattern: str):
     return m_v.group(1) if h.hexdigest() == m_sha.group(1) else None
 
 
-def measured_mfma_util(workload_name: str):
+def measured_mfma_util(workload_name: str, sources):
     """Matrix-core busy fraction of the draft position kernel (SQ counters, from the
     committed summary bound to the kernel source), or None."""
     here = os.path.dirname(os.path.abspath(__file__))
     v = _sha_bound_figure(os.path.join(here, "profiles", f"draft_position_{workload_name}_mfma.md"),
-                          r"matrix-core busy fraction:\s*([0-9.]+)")
+                          r"matrix-core busy fraction:\s*([0-9.]+)", sources)
     return None if v is None else float(v)
 
 
