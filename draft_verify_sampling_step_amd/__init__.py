@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
             L.dspark_closed_loop.argtypes = [D, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _F,
                                              _U64, _F, _U64, ctypes.c_int32, _P, _P, _P, _P,
                                              _P, _P, _P, _P, _P, _P, _SZ, _P]
+            L.dspark_test_wait_limit.argtypes = [ctypes.c_int32]
             L.dspark_profile_start.argtypes = [_I]
             L.dspark_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(_I),
@@ -499,6 +500,13 @@ def dspark_gumbel_lattice(form: int, device="cuda", stream=None):
     out = torch.empty(1 << 23, dtype=torch.float32, device=device)
     _check(lib().dspark_gumbel_lattice(int(form), _ptr(out), _stream_handle(stream)))
     return out
+
+
+def dspark_test_wait_limit(polls: int):
+    """Failure-path testing only: polls >= 0 makes every bounded wait of the cooperative
+    kernels give up after `polls` polls (their calls then report failure); polls < 0
+    restores normal operation."""
+    _check(lib().dspark_test_wait_limit(int(polls)))
 
 
 def dspark_profile_start(max_launches: int = 4096):

@@ -37,6 +37,19 @@ __global__ void k_gumbel_lattice(int form, float* __restrict__ out) {
   out[m] = form == 0 ? gumbel_from_uniform(word_to_uniform(w)) : neg_lglg(w);
 }
 
+// The bounded waits of the cooperative kernels: 2^22 polls by default; a test may set a
+// small limit with an unreachable completion (dspark_test_wait_limit).
+namespace {
+constexpr uint32_t kDefaultWaitLimit = 1u << 22;
+std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
+std::atomic<uint32_t> g_wait_unreachable{0};
+}  // namespace
+
+WaitPolicy wait_policy() {
+  return WaitPolicy{g_wait_limit.load(std::memory_order_relaxed),
+                    g_wait_unreachable.load(std::memory_order_relaxed)};
+}
+
 // Launch timing: while enabled, the draft records a HIP event pair around each of its
 // per-position kernels on the caller's stream (measurement only).  The state is guarded
 // by a mutex; when timing is off the hooks cost one relaxed atomic load.
@@ -95,6 +108,17 @@ dspark_status LdsAttr::ensure(const void* kernel, int bytes) {
 }  // namespace dspark
 
 using namespace dspark;
+
+extern "C" dspark_status dspark_test_wait_limit(int32_t polls) {
+  if (polls < 0) {
+    g_wait_unreachable.store(0, std::memory_order_relaxed);
+    g_wait_limit.store(kDefaultWaitLimit, std::memory_order_relaxed);
+  } else {
+    g_wait_limit.store((uint32_t)polls, std::memory_order_relaxed);
+    g_wait_unreachable.store(1, std::memory_order_relaxed);
+  }
+  return DSPARK_OK;
+}
 
 extern "C" dspark_status dspark_profile_start(int max_launches) {
   if (max_launches < 1 || max_launches > (1 << 16)) return DSPARK_E_VALUE;

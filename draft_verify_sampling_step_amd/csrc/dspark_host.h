@@ -67,6 +67,15 @@ struct LdsAttr {
   dspark_status ensure(const void* kernel, int bytes);
 };
 
+// Bounded cross-workgroup waits of the cooperative kernels (resident draft, training loss):
+// the poll limit, and whether the completion a wait looks for is made unreachable (set
+// only through dspark_test_wait_limit, to run the give-up path deterministically).
+struct WaitPolicy {
+  uint32_t limit;
+  uint32_t unreachable;
+};
+WaitPolicy wait_policy();
+
 // Every matrix-core kernel variant's LDS attribute set on the current device.  The entry
 // points that may launch one call it after validating their arguments and before their
 // first launch, so a refusal returns before anything is enqueued.

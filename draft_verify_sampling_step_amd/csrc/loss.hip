@@ -74,6 +74,7 @@ struct LossArgs {
   int R, G, V, C, L, P;
   double a_ce, a_l1, a_conf, inv_W;
   uint32_t spin_limit;
+  uint32_t unreachable;   // testing: no published word is ever taken as published
 };
 
 __device__ __forceinline__ void raw_barrier() {
@@ -121,7 +122,7 @@ __device__ __forceinline__ bool await_words(const LossArgs& a, const unsigned lo
       all = all && (wb[i] >> 32) != 0ull;
       qb[i] = __uint_as_float((uint32_t)wb[i]);
     }
-    if (all) return true;
+    if (all && a.unreachable == 0u) return true;
     ++polls;
     if (polls > a.spin_limit ||
         (polls % kFaultCheckPolls == 0 &&
@@ -668,7 +669,9 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
   for (int k = 0; k < G; ++k) wsum += std::exp(-(double)k / G);
   a.inv_W = 1.0 / ((double)B * wsum);
   a.a_ce = alpha_ce; a.a_l1 = alpha_l1; a.a_conf = alpha_conf;
-  a.spin_limit = 1u << 22;
+  const WaitPolicy wp = wait_policy();
+  a.spin_limit = wp.limit;
+  a.unreachable = wp.unreachable;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(k_loss_init,
                      dim3((unsigned)std::min<size_t>(2048, (w.nwords + 255) / 256)), dim3(256),

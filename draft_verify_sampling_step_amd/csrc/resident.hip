@@ -84,6 +84,7 @@ struct ResArgs {
   float invT;
   uint32_t key0, key1;
   uint32_t spin_limit;
+  uint32_t unreachable;       // testing: no wait ever completes
 };
 
 // Both hand-offs leave the winners of position `pos` (0-based) in win[0 .. B-1] (LDS) for
@@ -118,7 +119,7 @@ __device__ bool res_wait_slots(const ResArgs& a, int pos, unsigned long long* wi
                  ? __hip_atomic_load(sl + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : ~0ull;
     }
-    bool missing = false;
+    bool missing = a.unreachable != 0u;
     mx = 0;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
@@ -163,7 +164,7 @@ __device__ bool res_wait_count(const ResArgs& a, int pos, unsigned long long* wi
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const int32_t* top = a.cnt + (size_t)pos * kArriveInts + 32 * kSubSlots;
-    const int want = a.nwg < kSubSlots ? a.nwg : kSubSlots;
+    const int want = (a.nwg < kSubSlots ? a.nwg : kSubSlots) + (int)a.unreachable;
     int ok = 1;
     if (lane == 0) {
       uint32_t polls = 0;
@@ -568,7 +569,9 @@ dspark_status launch_draft_resident(const ResidentPlan& p, const float* U, const
   a.best = best; a.part = part; a.cnt = cnt; a.slot = slot; a.fault = fault;
   a.B = B; a.G = G; a.V = V; a.nwg = p.nwg;
   a.invT = invT; a.key0 = key0; a.key1 = key1;
-  a.spin_limit = 1u << 22;
+  const WaitPolicy wp = wait_policy();
+  a.spin_limit = wp.limit;
+  a.unreachable = wp.unreachable;
   void* args[] = {&a};
   if (hipLaunchCooperativeKernel(res_kernel(B), dim3((unsigned)p.nwg),
                                  dim3(kResThreads), args, (unsigned)kResLds, st) != hipSuccess) {

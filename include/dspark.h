@@ -419,6 +419,19 @@ dspark_status dspark_profile_stop(double* mean_ms, int* launches,
                                   double* positions_per_launch);
 
 /*
+ * Failure-path testing (not part of the method, not for production use).  The cooperative
+ * kernels (the resident draft of dspark_draft_markov for up to 16 requests, and
+ * dspark_draft_loss) bound every wait on other workgroups: a wait that runs past its poll
+ * limit raises the call's fault word, every workgroup leaves, and the call reports its
+ * failure in its outputs (draft: every token -1, logp and lse NaN; loss: NaN).  With
+ * polls >= 0, later calls in this process limit each such wait to `polls` polls and make
+ * the completion it looks for unreachable, so that every wait gives up and the failure is
+ * reported while every kernel still ends; polls < 0 restores normal operation (2^22 polls,
+ * reachable completions).  Process-wide, on every device.  Always DSPARK_OK.
+ */
+dspark_status dspark_test_wait_limit(int32_t polls);
+
+/*
  * Achievable HBM read rate (measurement support, not part of the method).  Times `reps`
  * launches of a plain streaming-read kernel (16-byte loads, every byte read once, nothing
  * written) on `stream`; launch i reads the i-th of the buf_bytes / launch_bytes regions of
