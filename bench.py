@@ -14,7 +14,8 @@ the step timed as one HIP-graph replay of the eager step (its outputs checked ag
 eager step's in the same run; `ms_per_step_eager` is the eager time).
 `roofline` covers the dominant kernel, one draft position: its algorithmic bytes (W2t once
 and the B base-logit rows of the position) over its mean launch duration, measured with
-HIP events around each launch on the launch stream in a timed pass of its own; beside it,
+HIP events on the launch stream in a timed pass of its own (one pair around the gamma
+consecutive launches of each call, the span over gamma, dispatch gaps included); beside it,
 `read_probe` is a plain streaming read of the same bytes per launch, the achievable rate.
 `cpu_baseline` times the fp64 oracle on a bounded sample of requests on the host.
 """
@@ -216,7 +217,8 @@ def main():
         log(f"graph replay not used: {graph_note}")
 
     # the dominant kernel, one draft position (fused bias MFMA + softmax + Gumbel race):
-    # HIP events around each of its launches on the launch stream, in a pass of its own so
+    # HIP events around the consecutive launches of each call on the launch stream (the
+    # span over the launch count, dispatch gaps included), in a pass of its own so
     # that the events do not perturb the step timing above
     ds.dspark_profile_start(args.steps * G + 16)
     for _ in range(args.steps):

@@ -50,14 +50,16 @@ WaitPolicy wait_policy() {
                     g_wait_unreachable.load(std::memory_order_relaxed)};
 }
 
-// Launch timing: while enabled, the draft records a HIP event pair around each of its
-// per-position kernels on the caller's stream (measurement only).  The state is guarded
-// by a mutex; when timing is off the hooks cost one relaxed atomic load.
+// Launch timing: while enabled, the draft records one HIP event pair on the caller's
+// stream around the launches of its sampling kernel in a call (measurement only): the
+// span covers `launches` consecutive launches and the dispatch gaps between them.  The
+// state is guarded by a mutex; when timing is off the hooks cost one relaxed atomic load.
 namespace {
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
 int g_prof_n = 0;              // events recorded (pairs are complete when even)
 long long g_prof_positions = 0;
+long long g_prof_launches = 0;
 std::vector<hipEvent_t> g_prof_ev;
 
 void prof_release_events() {
@@ -73,16 +75,17 @@ void prof_begin(hipStream_t st) {
   (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
 }
 
-void prof_end(hipStream_t st, int positions) {
+void prof_end(hipStream_t st, int positions, int launches) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on.load(std::memory_order_relaxed) || (g_prof_n & 1) == 0) return;
-  if (positions < 0) {   // the launch was refused: drop its begin event
+  if (positions < 0 || launches < 1) {   // a launch was refused: drop the begin event
     --g_prof_n;
     return;
   }
   (void)hipEventRecord(g_prof_ev[g_prof_n++], st);
   g_prof_positions += positions;
+  g_prof_launches += launches;
 }
 
 namespace {
@@ -136,6 +139,7 @@ extern "C" dspark_status dspark_profile_start(int max_launches) {
   }
   g_prof_n = 0;
   g_prof_positions = 0;
+  g_prof_launches = 0;
   g_prof_on.store(true, std::memory_order_relaxed);
   return DSPARK_OK;
 }
@@ -156,14 +160,16 @@ extern "C" dspark_status dspark_profile_stop(double* mean_ms, int* launches,
     total += ms;
   }
   if (rc == DSPARK_OK) {
-    *launches = pairs;
-    *mean_ms = pairs ? total / pairs : 0.0;
-    *positions_per_launch = pairs ? (double)g_prof_positions / pairs : 0.0;
+    const long long n = g_prof_launches;
+    *launches = (int)n;
+    *mean_ms = n ? total / (double)n : 0.0;
+    *positions_per_launch = n ? (double)g_prof_positions / (double)n : 0.0;
   }
   // every recorded event has completed (or the device failed): none outlives the loop
   prof_release_events();
   g_prof_n = 0;
   g_prof_positions = 0;
+  g_prof_launches = 0;
   return rc;
 }
 

@@ -285,9 +285,11 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
         launch_draft_resident(plan.rp, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor,
                               forced, best, part, w.cnt, w.slot, w.fault, B, G, V, invT, key0,
                               key1, st);
-    prof_end(st, ls == DSPARK_OK ? G : -1);
+    prof_end(st, ls == DSPARK_OK ? G : -1, 1);
     if (ls != DSPARK_OK) return DSPARK_E_HIP;
   }
+  // one timing span over the G position launches (they run back to back on `st`)
+  if (!plan.resident) prof_begin(st);
   for (int k = 1; k <= G && !plan.resident; ++k) {
     const unsigned long long* bprev = k > 1 ? best + (size_t)(k - 2) * B : nullptr;
     unsigned long long* bcur = best + (size_t)(k - 1) * B;
@@ -300,17 +302,15 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
       a.part = pk;
       a.B = B; a.G = G; a.V = V; a.r = r; a.k = k; a.invT = invT; a.key0 = key0; a.key1 = key1;
       a.ncols = B;
-      prof_begin(st);
       const dspark_status ls = launch_mfma_bias(a, plan.nslices, st);
-      prof_end(st, ls == DSPARK_OK ? 1 : -1);
-      if (ls != DSPARK_OK) return DSPARK_E_HIP;
+      if (ls != DSPARK_OK) {
+        prof_end(st, -1, 0);
+        return DSPARK_E_HIP;
+      }
     } else if (plan.gemv) {
-      prof_begin(st);
       launch_draft_gemv(plan.gp, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced,
                         bprev, bcur, pk, B, G, V, k, invT, key0, key1, st);
-      prof_end(st, 1);
     } else {
-      prof_begin(st);
       const size_t sh = sizeof(float) * (r + 256 + 16);
       dim3 grid(plan.nslices, B);
       if (wdt == DSPARK_BF16)
@@ -321,9 +321,9 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
         hipLaunchKernelGGL(k_draft_row<float>, grid, dim3(256), sh, st, U, (const float*)W1,
                            (const float*)W2t, anchor, forced, bprev, bcur, pk, B, G, V, r, k,
                            invT, key0, key1, plan.slice_len);
-      prof_end(st, 1);
     }
   }
+  if (!plan.resident) prof_end(st, G, G);
   const int fblocks = G * ((B + 7) / 8);   // one workgroup per (position, 8 requests)
   if (wdt == DSPARK_BF16)
     hipLaunchKernelGGL(k_draft_final<uint16_t>, dim3(fblocks), dim3(256), 0, st, part,

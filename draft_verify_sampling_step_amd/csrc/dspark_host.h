@@ -53,11 +53,12 @@ inline int mfma_workgroups(int V) {
   return tiles < 1024 ? tiles : 1024;
 }
 
-// Launch timing (api.hip): while enabled, prof_begin/prof_end bracket one launch with a
-// pair of events on `st`; `positions` is the number of draft positions the launch covered
-// (a negative count withdraws a begin whose launch was refused).
+// Launch timing (api.hip): while enabled, prof_begin/prof_end bracket `launches`
+// consecutive launches of one kernel with a pair of events on `st`; `positions` is the
+// number of draft positions they covered (a negative count withdraws a begin whose launch
+// was refused).
 void prof_begin(hipStream_t st);
-void prof_end(hipStream_t st, int positions);
+void prof_end(hipStream_t st, int positions, int launches);
 
 // A kernel's dynamic-LDS limit raised to `bytes`, once per device (devices 0..63), safe to
 // call from several host threads: the first caller on a device sets the attribute under a

@@ -405,12 +405,14 @@ dspark_status dspark_gumbel_lattice(int form, float* out, void* stream);
 
 /*
  * Launch timing (measurement support, not part of the method).  Between
- * dspark_profile_start and dspark_profile_stop every launch of the sampling kernel of
- * dspark_draft_markov (one launch per draft position) is bracketed by a pair of HIP
- * events on the call's stream, for at most max_launches launches (1..65536; events are
- * created on the first call and kept).  dspark_profile_stop waits for the recorded events
- * and returns the mean duration of the bracketed launches in milliseconds, their count,
- * and the mean number of draft positions one launch covered.  Not thread-safe; meant for
+ * dspark_profile_start and dspark_profile_stop the launches of the sampling kernel of
+ * each dspark_draft_markov call (one launch per draft position, or one launch for all
+ * positions of the call) are bracketed by one pair of HIP events on the call's stream, for
+ * at most max_launches launches (1..65536; events are created on the first call and
+ * kept).  dspark_profile_stop waits for the recorded events and returns the mean duration
+ * per launch in milliseconds (the bracketed time over the number of launches, so the
+ * dispatch gaps between a call's consecutive launches are counted in), the number of
+ * launches, and the mean number of draft positions one launch covered.  Not thread-safe; meant for
  * one timing loop at a time.  Errors: DSPARK_E_VALUE (max_launches out of range),
  * DSPARK_E_NULL, DSPARK_E_HIP (event creation or timing failed).
  */
