@@ -18,6 +18,7 @@
 #include "dspark_host.h"
 #include "gemv.h"
 #include "mfma_bias.h"
+#include "mfma_common.h"
 #include "resident.h"
 #include "rowbias.h"
 
@@ -39,8 +40,10 @@ __device__ __forceinline__ int draft_prev(const int32_t* anchor, const int32_t* 
   return clamp_tok((int)packed_index(best_prev[b]), V);
 }
 
-// Row path: grid (slices, B), 256 threads.  Thread t of a tile owns vocab row tile0 + t.
-// Base-2 logits z2 = z log2 e; the partial is (max z2, sum 2^(z2 - max)).
+// Row path: grid (slices, B), 256 threads.  A step covers four tiles (kRowTile rows each,
+// biases in LDS); thread t then owns the four consecutive rows tile0 + 4t .. + 3, whose
+// uniforms are the four words of one Philox call.  Base-2 logits z2 = z log2 e; the
+// partial is (max z2, sum 2^(z2 - max)).
 template <typename WT>
 __global__ __launch_bounds__(256) void k_draft_row(
     const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
@@ -50,32 +53,48 @@ __global__ __launch_bounds__(256) void k_draft_row(
     uint32_t key1, int slice_len) {
   extern __shared__ float smem[];
   float* w1s = smem;            // [r]
-  float* bias_s = smem + r;     // [256]
-  float* red = bias_s + 256;    // [16]
+  float* bias_s = smem + r;     // [4 kRowTile]
+  float* red = bias_s + 4 * kRowTile;   // [16]
   const int b = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
-  const int v_begin = s * slice_len;
+  const int v_begin = s * slice_len;   // a multiple of kRowTile
   const int v_end = min(V, v_begin + slice_len);
   const int prev = draft_prev(anchor, forced, best_prev, b, G, k, V);
   const float s2 = invT * 1.4426950408889634f;
+  const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)b, 0u, key0, key1);
   load_w1_row<WT>(W1, prev, r, w1s);
   __syncthreads();
   const float* Urow = U + ((size_t)b * G + (k - 1)) * V;
   float m = -3.0e38f, l = 0.f;
   Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
-  for (int tile0 = v_begin; tile0 < v_end; tile0 += kRowTile) {
-    row_bias_tile<WT>(W2t, w1s, bias_s, r, tile0, v_end);
+  for (int tile0 = v_begin; tile0 < v_end; tile0 += 4 * kRowTile) {
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i)   // workgroup-uniform bound
+      if (tile0 + i * kRowTile < v_end)
+        row_bias_tile<WT>(W2t, w1s, bias_s + i * kRowTile, r, tile0 + i * kRowTile, v_end);
     __syncthreads();
-    const int v = tile0 + tid;
-    if (v < v_end) {
-      const float z = (Urow[v] + bias_s[tid]) * s2;
-      const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 0u, key0, key1);
-      const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-      const float score =
-          z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
-      const float mn = fmaxf(m, z);
-      l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(z - mn);
+    const int v0 = tile0 + 4 * tid;
+    if (v0 < v_end) {
+      const U4 w = philox_call((uint32_t)v0 >> 2, pl);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const int n = min(4, v_end - v0);
+      float z[4];
+      float qm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = i < n ? (Urow[v0 + i] + bias_s[4 * tid + i]) * s2 : -INFINITY;
+        qm = fmaxf(qm, z[i]);
+      }
+      const float mn = fmaxf(m, qm);
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= n) break;
+        add += __builtin_amdgcn_exp2f(z[i] - mn);
+        const float score = z[i] + neg_lglg(wd[i]);
+        if (score > best.s) best = Cand{score, (uint32_t)(v0 + i), 0.f};
+      }
+      l = l * __builtin_amdgcn_exp2f(m - mn) + add;
       m = mn;
-      if (score > best.s) best = Cand{score, (uint32_t)v, 0.f};
     }
     __syncthreads();
   }
@@ -311,7 +330,7 @@ dspark_status draft_run(const dspark_dims* dm, const DraftPlan& plan, const floa
       launch_draft_gemv(plan.gp, U, (const uint16_t*)W1, (const uint16_t*)W2t, anchor, forced,
                         bprev, bcur, pk, B, G, V, k, invT, key0, key1, st);
     } else {
-      const size_t sh = sizeof(float) * (r + 256 + 16);
+      const size_t sh = sizeof(float) * (r + 4 * kRowTile + 16);
       dim3 grid(plan.nslices, B);
       if (wdt == DSPARK_BF16)
         hipLaunchKernelGGL(k_draft_row<uint16_t>, grid, dim3(256), sh, st, U,

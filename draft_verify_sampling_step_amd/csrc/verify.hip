@@ -208,17 +208,27 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
       }
       continue;
     }
-    // any other vocabulary size: one entry per thread and step, online state
+    // any other vocabulary size: the normaliser one entry per thread and step (online
+    // state); the bonus race four consecutive entries per thread and step, which share one
+    // Philox call (v_begin is a multiple of 4)
     float m = -3.0e38f, l = 0.f;
     Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
-    for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
-      const float z = trow[v] * s2;
-      if (is_bonus) {
-        const U4 w = philox10((uint32_t)v >> 2, (uint32_t)k, (uint32_t)b, 2u, key0, key1);
-        const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-        const float sc = z - __builtin_amdgcn_logf(-__builtin_amdgcn_logf(word_to_uniform(word)));
-        if (sc > best.s) best = Cand{sc, (uint32_t)v, 0.f};
-      } else {
+    if (is_bonus) {
+      const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)b, 2u, key0, key1);
+      for (int v0 = v_begin + 4 * threadIdx.x; v0 < v_end; v0 += 4 * 256) {
+        const U4 w = philox_call((uint32_t)v0 >> 2, pl);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        const int n = min(4, v_end - v0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= n) break;
+          const float sc = fmaf(trow[v0 + i], s2, neg_lglg(wd[i]));
+          if (sc > best.s) best = Cand{sc, (uint32_t)(v0 + i), 0.f};
+        }
+      }
+    } else {
+      for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
+        const float z = trow[v] * s2;
         const float mn = fmaxf(m, z);
         l = l * ex2(m - mn) + ex2(z - mn);
         m = mn;
@@ -326,7 +336,8 @@ __global__ __launch_bounds__(256) void k_verify_decide(
   }
 }
 
-// Row residual: grid (slices, B), 256 threads.
+// Row residual: grid (slices, B), 256 threads.  As in the row draft, a step covers four
+// tiles and thread t owns the rows tile0 + 4t .. + 3, drawn from one Philox call.
 template <typename WT>
 __global__ __launch_bounds__(256) void k_verify_resid_row(
     const float* __restrict__ U, const WT* __restrict__ W1, const WT* __restrict__ W2t,
@@ -338,8 +349,8 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
     const int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens) {
   extern __shared__ float smem[];
   float* w1s = smem;
-  float* bias_s = smem + r;
-  float* red = bias_s + 256;
+  float* bias_s = smem + r;             // [4 kRowTile]
+  float* red = bias_s + 4 * kRowTile;   // [16]
   const int s = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = jrow[b];
   if (j == 0) return;
@@ -350,24 +361,34 @@ __global__ __launch_bounds__(256) void k_verify_resid_row(
   const float ld = lse_d[(size_t)b * G + (j - 1)], lt = lse_t_row[b];
   const float* urow = U + ((size_t)b * G + (j - 1)) * V;
   const float* trow = T + ((size_t)b * (G + 1) + (j - 1)) * V;
+  const PhiloxLane pl = philox_lane((uint32_t)j, (uint32_t)b, 2u, key0, key1);
   Cand b1{-INFINITY, 0xFFFFFFFFu, 0.f}, b2{-INFINITY, 0xFFFFFFFFu, 0.f};
-  for (int tile0 = v_begin; tile0 < v_end; tile0 += kRowTile) {
-    row_bias_tile<WT>(W2t, w1s, bias_s, r, tile0, v_end);
+  for (int tile0 = v_begin; tile0 < v_end; tile0 += 4 * kRowTile) {
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i)   // workgroup-uniform bound
+      if (tile0 + i * kRowTile < v_end)
+        row_bias_tile<WT>(W2t, w1s, bias_s + i * kRowTile, r, tile0 + i * kRowTile, v_end);
     __syncthreads();
-    const int v = tile0 + tid;
-    if (v < v_end) {
-      const float zd = (urow[v] + bias_s[tid]) * invT;
-      const float zt = trow[v] * invT;
-      const float rho = fast_exp(zt - lt) - fast_exp(zd - ld);
-      const U4 w = philox10((uint32_t)v >> 2, (uint32_t)j, (uint32_t)b, 2u, key0, key1);
-      const uint32_t word = (v & 3) == 0 ? w.x : (v & 3) == 1 ? w.y : (v & 3) == 2 ? w.z : w.w;
-      const float gn = gumbel_from_uniform(word_to_uniform(word));
-      if (rho > 0.f) {
-        const float sc = fast_log(rho) + gn;
-        if (sc > b1.s) b1 = Cand{sc, (uint32_t)v, 0.f};
+    const int v0 = tile0 + 4 * tid;
+    if (v0 < v_end) {
+      const U4 w = philox_call((uint32_t)v0 >> 2, pl);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      const int n = min(4, v_end - v0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= n) break;
+        const int v = v0 + i;
+        const float zd = (urow[v] + bias_s[4 * tid + i]) * invT;
+        const float zt = trow[v] * invT;
+        const float rho = fast_exp(zt - lt) - fast_exp(zd - ld);
+        const float gn = gumbel_from_uniform(word_to_uniform(wd[i]));
+        if (rho > 0.f) {
+          const float sc = fast_log(rho) + gn;
+          if (sc > b1.s) b1 = Cand{sc, (uint32_t)v, 0.f};
+        }
+        const float sc2 = zt + gn;
+        if (sc2 > b2.s) b2 = Cand{sc2, (uint32_t)v, 0.f};
       }
-      const float sc2 = zt + gn;
-      if (sc2 > b2.s) b2 = Cand{sc2, (uint32_t)v, 0.f};
     }
     __syncthreads();
   }
@@ -497,7 +518,7 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
     if (launch_mfma_bias(a, nres, st) != DSPARK_OK) return DSPARK_E_HIP;
   } else {
     const RowSlices rr = row_slices(V, B);
-    const size_t sh = sizeof(float) * (r + 256 + 16);
+    const size_t sh = sizeof(float) * (r + 4 * kRowTile + 16);
     if (wdt == DSPARK_BF16)
       hipLaunchKernelGGL(k_verify_resid_row<uint16_t>, dim3(rr.count, B), dim3(256), sh, st, U,
                          (const uint16_t*)W1, (const uint16_t*)W2t, T, anchor, tokens, lse,

@@ -203,6 +203,13 @@ MULTI_TILE = {
     "mt_gemv_b2_v262144": workload.custom(name="mt_gemv_b2", B=2, gamma=3, V=262144, r=256,
                                           d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
                                           table="serve"),
+    # the row kernels (fp32 weights, r = 64): slices of 1280 rows, i.e. a step of four
+    # 256-row tiles and a step of one, one Philox call per four rows; the last slice ends
+    # one row into its third tile, and the target-row pass (V % 4 != 0) ends on a one-entry
+    # slice
+    "mt_rows_fp32_b16_odd": workload.custom(name="mt_rows_fp32", B=16, gamma=2, V=131073,
+                                            r=64, d=64, wsigma=0.5, logits="zipf",
+                                            table="serve"),
 }
 
 
