@@ -75,12 +75,43 @@ __global__ __launch_bounds__(256) void k_verify_plan(const int32_t* __restrict__
 
 __device__ __forceinline__ int clamp_ell(int L, int G) { return L < 0 ? 0 : (L > G ? G : L); }
 
-// Grid-stride over (row, slice) items.  Rows 1..ell_b: split-vocabulary (max, sum-exp)
-// partials of T/temperature (base 2).  Row ell_b + 1 needs no normaliser (only its bonus
-// token is drawn from it): the Gumbel race over it, one packed (score, index) word per
-// slice.  Without a plan (rows == NULL) every workgroup first forms pre[b] = sum over
-// requests before b of (ell + 1) in LDS (dynamic, B + 1 ints) and maps an item by binary
-// search.
+// Workgroup (256 threads) merge of per-thread base-2 (max, sum) states in a fixed order;
+// thread 0 writes it to *out.  Uses red[0..8).
+__device__ __forceinline__ void rows_put_ml(float m, float l, float* red, float2* out) {
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
+    const float mn = fmaxf(m, om);
+    l = l * ex2(m - mn) + ol * ex2(om - mn);
+    m = mn;
+  }
+  if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = red[0], ll = red[4];
+    for (int i = 1; i < 4; ++i) {
+      const float mn = fmaxf(mm, red[i]);
+      ll = ll * ex2(mm - mn) + red[4 + i] * ex2(red[i] - mn);
+      mm = mn;
+    }
+    *out = make_float2(mm, ll);
+  }
+  __syncthreads();
+}
+
+// An item of the target-row pass: (request b, row id, slice s).
+struct RowItem { int b, row, s; };
+
+// Each workgroup takes a contiguous range of (row, slice) items, i.e. consecutive slices of
+// consecutive rows.  Rows 1..ell_b: split-vocabulary (max, sum-exp) partials of
+// T/temperature (base 2).  Row ell_b + 1 needs no normaliser (only its bonus token is
+// drawn from it): the Gumbel race over it, one packed (score, index) word per slice.
+// Without a plan (rows == NULL) every workgroup first forms pre[b] = sum over requests
+// before b of (ell + 1) in LDS (dynamic, B + 1 ints) and maps an item by binary search.
+// (Contiguous ranges measured faster than a grid-stride order, whose last round leaves
+// most workgroups idle; a second register buffer that loads the next item during the
+// current one halves the occupancy and was slower at the scheduled budget.)
 __global__ __launch_bounds__(256, 8) void k_verify_rows(
     const float* __restrict__ T, const int32_t* __restrict__ ell,
     const int32_t* __restrict__ rows, const int32_t* __restrict__ counts, int B, int G, int V,
@@ -117,9 +148,13 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
   } else {
     nitems = counts[1];
   }
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int rpos = item / nslices, s = item % nslices;
-    int b, row;
+  const int per = nitems / (int)gridDim.x, rem = nitems % (int)gridDim.x;
+  const int it0 = (int)blockIdx.x * per + min((int)blockIdx.x, rem);
+  const int it1 = it0 + per + ((int)blockIdx.x < rem ? 1 : 0);
+  auto locate = [&](int item) {
+    const int rpos = item / nslices;
+    RowItem r;
+    r.s = item % nslices;
     if (rows == nullptr) {
       int lo = 0, hi = B - 1;   // the b with pre[b] <= rpos < pre[b + 1] (pre increases)
       while (lo < hi) {
@@ -127,71 +162,58 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
         if (pre[mid] <= rpos) lo = mid;
         else hi = mid - 1;
       }
-      b = lo;
-      row = b * (G + 1) + (rpos - pre[b]);
+      r.b = lo;
+      r.row = lo * (G + 1) + (rpos - pre[lo]);
     } else {
-      row = rows[rpos];
-      b = row / (G + 1);
+      r.row = rows[rpos];
+      r.b = r.row / (G + 1);
     }
-    const int k = row % (G + 1) + 1;
-    const bool is_bonus = (k == clamp_ell(ell[b], G) + 1);
-    const int v_begin = s * slice_len, v_end = min(V, v_begin + slice_len);
-    const float* trow = T + (size_t)row * V;
-    if ((V & 3) == 0 && slice_len == 4 * 256 * kVerifyQuads) {
-      // every thread's eight 16-byte loads are issued before any is consumed; entries past
-      // the slice read as -inf
-      constexpr int kQ = kVerifyQuads;
-      f32x4_t q[kQ];
+    return r;
+  };
+
+  if ((V & 3) == 0 && slice_len == 4 * 256 * kVerifyQuads) {
+    constexpr int kQ = kVerifyQuads;
+    // every thread's eight 16-byte loads of an item; entries past the slice read as -inf
+    auto issue = [&](const RowItem& r, f32x4_t (&q)[kQ]) {
+      const int v_begin = r.s * slice_len, v_end = min(V, v_begin + slice_len);
+      const float* trow = T + (size_t)r.row * V;
 #pragma unroll
       for (int i = 0; i < kQ; ++i) {
-        const int v = v_begin + 4 * (threadIdx.x + 256 * i);
+        const int v = v_begin + 4 * (tid + 256 * i);
         q[i] = v < v_end ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(trow + v))
                          : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
+    };
+    auto consume = [&](const RowItem& r, const f32x4_t (&q)[kQ]) {
+      const int k = r.row % (G + 1) + 1;
+      const bool is_bonus = (k == clamp_ell(ell[r.b], G) + 1);
+      const int v_begin = r.s * slice_len;
       if (!is_bonus) {
-        // max first (a finite floor when every entry is padding), then one exponential per
-        // entry
+        // max first (a finite floor when every entry is padding), then one exponential
+        // per entry
         float mq = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kQ; ++i)
           mq = fmaxf(mq, fmaxf(fmaxf(q[i][0], q[i][1]), fmaxf(q[i][2], q[i][3])));
-        float m = fmaxf(mq * s2, -3.0e38f);
+        const float m = fmaxf(mq * s2, -3.0e38f);
         float lp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kQ; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) lp[j] += ex2(fmaf(q[i][j], s2, -m));
-        float l = (lp[0] + lp[1]) + (lp[2] + lp[3]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
-          const float mn = fmaxf(m, om);
-          l = l * ex2(m - mn) + ol * ex2(om - mn);
-          m = mn;
-        }
-        if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          float mm = red[0], ll = red[4];
-          for (int i = 1; i < 4; ++i) {
-            const float mn = fmaxf(mm, red[i]);
-            ll = ll * ex2(mm - mn) + red[4 + i] * ex2(red[i] - mn);
-            mm = mn;
-          }
-          part[(size_t)row * nslices + s] = make_float2(mm, ll);
-        }
-        __syncthreads();
+        rows_put_ml(m, (lp[0] + lp[1]) + (lp[2] + lp[3]), red,
+                    part + (size_t)r.row * nslices + r.s);
       } else {
         // four consecutive entries share one Philox call (words 0..3); the calls of a
         // batch run in lockstep
-        const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)b, 2u, key0, key1);
+        const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)r.b, 2u, key0, key1);
         Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
 #pragma unroll
         for (int i0 = 0; i0 < kQ; i0 += 4) {
           uint32_t c0[4], w[4][4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            c0[i] = (uint32_t)((v_begin + 4 * (threadIdx.x + 256 * (i0 + i))) >> 2);
+            c0[i] = (uint32_t)((v_begin + 4 * (tid + 256 * (i0 + i))) >> 2);
           philox_calls<4>(c0, pl, w);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -202,20 +224,33 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
             }
         }
         best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
-        if (threadIdx.x == 0)
-          bonus_part[(size_t)b * nslices + s] =
+        if (tid == 0)
+          bonus_part[(size_t)r.b * nslices + r.s] =
               best.i != 0xFFFFFFFFu ? pack_score(best.s, best.i) : 0ull;
       }
-      continue;
+    };
+    f32x4_t q[kQ];
+    for (int item = it0; item < it1; ++item) {
+      const RowItem r = locate(item);
+      issue(r, q);
+      consume(r, q);
     }
-    // any other vocabulary size: the normaliser one entry per thread and step (online
-    // state); the bonus race four consecutive entries per thread and step, which share one
-    // Philox call (v_begin is a multiple of 4)
-    float m = -3.0e38f, l = 0.f;
-    Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+    return;
+  }
+
+  // any other vocabulary size: the normaliser one entry per thread and step (online
+  // state); the bonus race four consecutive entries per thread and step, which share one
+  // Philox call (slices start at multiples of 4)
+  for (int item = it0; item < it1; ++item) {
+    const RowItem r = locate(item);
+    const int k = r.row % (G + 1) + 1;
+    const bool is_bonus = (k == clamp_ell(ell[r.b], G) + 1);
+    const int v_begin = r.s * slice_len, v_end = min(V, v_begin + slice_len);
+    const float* trow = T + (size_t)r.row * V;
     if (is_bonus) {
-      const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)b, 2u, key0, key1);
-      for (int v0 = v_begin + 4 * threadIdx.x; v0 < v_end; v0 += 4 * 256) {
+      const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)r.b, 2u, key0, key1);
+      Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
+      for (int v0 = v_begin + 4 * tid; v0 < v_end; v0 += 4 * 256) {
         const U4 w = philox_call((uint32_t)v0 >> 2, pl);
         const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
         const int n = min(4, v_end - v0);
@@ -226,39 +261,19 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
           if (sc > best.s) best = Cand{sc, (uint32_t)(v0 + i), 0.f};
         }
       }
+      best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
+      if (tid == 0)
+        bonus_part[(size_t)r.b * nslices + r.s] =
+            best.i != 0xFFFFFFFFu ? pack_score(best.s, best.i) : 0ull;
     } else {
-      for (int v = v_begin + threadIdx.x; v < v_end; v += 256) {
+      float m = -3.0e38f, l = 0.f;
+      for (int v = v_begin + tid; v < v_end; v += 256) {
         const float z = trow[v] * s2;
         const float mn = fmaxf(m, z);
         l = l * ex2(m - mn) + ex2(z - mn);
         m = mn;
       }
-    }
-    if (!is_bonus) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float om = __shfl_xor(m, o, kWave), ol = __shfl_xor(l, o, kWave);
-        const float mn = fmaxf(m, om);
-        l = l * ex2(m - mn) + ol * ex2(om - mn);
-        m = mn;
-      }
-      if (lane == 0) { red[wv] = m; red[4 + wv] = l; }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        float mm = red[0], ll = red[4];
-        for (int i = 1; i < 4; ++i) {
-          const float mn = fmaxf(mm, red[i]);
-          ll = ll * ex2(mm - mn) + red[4 + i] * ex2(red[i] - mn);
-          mm = mn;
-        }
-        part[(size_t)row * nslices + s] = make_float2(mm, ll);
-      }
-      __syncthreads();
-    } else {
-      best = block_cand(best, red + 8, reinterpret_cast<uint32_t*>(red + 12), red + 4);
-      if (threadIdx.x == 0)
-        bonus_part[(size_t)b * nslices + s] =
-            best.i != 0xFFFFFFFFu ? pack_score(best.s, best.i) : 0ull;
+      rows_put_ml(m, l, red, part + (size_t)r.row * nslices + r.s);
     }
   }
 }
@@ -492,6 +507,7 @@ extern "C" dspark_status dspark_verify(const dspark_dims* dm, const float* U, co
   if (plan)
     hipLaunchKernelGGL(k_verify_plan, dim3(1), dim3(256), 0, st, ell, B, G, nsl, w.rows,
                        w.counts);
+  // contiguous item ranges, eight workgroups per compute unit
   const long long max_items = (long long)B * (G + 1) * nsl;
   const int grid = (int)std::min<long long>(max_items, 2048);
   const size_t sh_rows = plan ? 0 : sizeof(int32_t) * ((size_t)B + 1);
