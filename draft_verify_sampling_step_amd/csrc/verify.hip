@@ -209,14 +209,14 @@ __global__ __launch_bounds__(256, 8) void k_verify_rows(
         const PhiloxLane pl = philox_lane((uint32_t)k, (uint32_t)r.b, 2u, key0, key1);
         Cand best{-INFINITY, 0xFFFFFFFFu, 0.f};
 #pragma unroll
-        for (int i0 = 0; i0 < kQ; i0 += 4) {
-          uint32_t c0[4], w[4][4];
+        for (int i0 = 0; i0 < kQ; i0 += 2) {
+          uint32_t c0[2], w[2][4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 2; ++i)
             c0[i] = (uint32_t)((v_begin + 4 * (tid + 256 * (i0 + i))) >> 2);
-          philox_calls<4>(c0, pl, w);
+          philox_calls<2>(c0, pl, w);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float sc = fmaf(q[i0 + i][j], s2, neg_lglg(w[i][j]));
