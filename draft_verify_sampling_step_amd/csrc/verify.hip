@@ -305,7 +305,9 @@ __global__ __launch_bounds__(256) void k_verify_decide(
   const bool live = k <= L;
   float lt = 0.f, pt = __builtin_nanf("");
   bool rejected = false;
-  if (live) {
+  // every draft row of the block is evaluated without waiting for ell (its loads do not
+  // depend on it); rows past ell are then discarded
+  if (k <= G) {
     const size_t row = (size_t)b * (G + 1) + (k - 1);
     const int x = clamp_tok(tokens[(size_t)b * G + (k - 1)], V);
     const float tx = T[row * V + x];
@@ -322,7 +324,11 @@ __global__ __launch_bounds__(256) void k_verify_decide(
     lt = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
     pt = fast_exp(tx * invT - lt);
     const U4 w = philox10(0u, (uint32_t)k, (uint32_t)b, 1u, key0, key1);
-    rejected = !(word_to_uniform(w.x) * fast_exp(lp) < pt);
+    rejected = live && !(word_to_uniform(w.x) * fast_exp(lp) < pt);
+    if (!live) {
+      lt = 0.f;
+      pt = __builtin_nanf("");
+    }
   }
   if (pt_tok && k <= G) pt_tok[(size_t)b * G + (k - 1)] = pt;
   const unsigned long long rej = __ballot(rejected);   // bit k-1: row k rejected
