@@ -636,7 +636,8 @@ def draft_kernel_name(B: int, V: int, r: int) -> str:
         return "k_draft_resident (W2t held in accumulation registers and LDS for all gamma " \
             "positions, one cooperative launch per draft call)"
     if r == 256 and 32 < B <= 256 and V % 4 == 0:
-        return ("k_draft16<8, false>" if B <= 128 else "k_draft16<16, false>") + \
+        nw = 4 if B <= 64 else (8 if B <= 128 else 16)
+        return f"k_draft16<{nw}, false>" + \
             " (16x16x32 bf16 MFMA, 16-column waves)"
     if r == 256 and B >= 32:
         return "k_mfma_bias<NCB, draft> (32x32x16 bf16 MFMA, 32-column waves)"

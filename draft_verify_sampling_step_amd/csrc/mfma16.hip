@@ -14,6 +14,11 @@
 // lane l of a block holds column l%16 and the four consecutive rows 4(l/16) + i, i < 4:
 // one aligned 16-byte logit load and one Philox4x32 call per block.  The base logits are
 // loaded in that layout and seed the accumulator, so the MFMA result is U + bias itself.
+//
+// Workgroup shapes: 8 waves (128 columns, two workgroups per CU) for 65..128 columns,
+// 16 waves (256 columns, one per CU) beyond, and 4 waves (64 columns, two per CU, so two
+// waves per SIMD) up to 64 columns: there a half-idle 8-wave workgroup would spend its
+// idle waves' MFMA and epilogue work on dummy columns, which measured 10-20% slower.
 #include "mfma_bias.h"
 #include "mfma_common.h"
 
@@ -27,7 +32,7 @@ struct Shape16 {
   static constexpr int NC = 16 * NW;          // columns
   static constexpr int SA = 4;                // W2t ring stages
   static constexpr int UD = 3;                // logit register buffers
-  static constexpr int WG_PER_CU = 16 / NW;   // four waves per SIMD
+  static constexpr int WG_PER_CU = NW == 4 ? 2 : 16 / NW;   // LDS: at most two rings
   static constexpr int NA = 16 / NW;          // DMA instructions per wave per step
   static constexpr int NU = TV ? 4 : 2;       // logit (and target) loads per wave per step
   // The stage of step s is waited for at step s.  A stage issued inside the loop (at step
@@ -53,7 +58,7 @@ struct Shape16 {
   // column metadata: logit row offset, column, conditioning token; TV adds the target row
   // offset and the two base-2 normalisers
   static constexpr size_t kLds = kOffMeta + (size_t)NC * (8 + 4 + 4) + (TV ? (size_t)NC * 16 : 0);
-  static_assert(NW == 8 || NW == 16, "16 or 32 DMA rows per wave pair");
+  static_assert(NW == 4 || NW == 8 || NW == 16, "whole DMA instructions per wave");
   static_assert(kLds * WG_PER_CU <= 160 * 1024, "LDS budget");
   static_assert(kWaitSS < 64, "vmcnt range");
 };
@@ -62,7 +67,7 @@ struct Shape16 {
 // position) columns instead of a draft position: p_d = 2^(z log2 e - lse_d), p_t from the
 // target slices loaded beside the logit slices, and the per-lane sum of min(p_d, p_t).
 template <int NW, bool TV = false>
-__global__ __launch_bounds__(64 * NW, 4) void k_draft16(const MfmaBiasArgs a) {
+__global__ __launch_bounds__(64 * NW, (NW == 4 ? 2 : 4)) void k_draft16(const MfmaBiasArgs a) {
   using S = Shape16<NW, TV>;
   constexpr int NC = S::NC, SA = S::SA, UD = S::UD;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -358,7 +363,8 @@ static dspark_status launch16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
 }
 
 dspark_status draft16_prepare() {
-  if (attr16<8>() != DSPARK_OK || attr16<16>() != DSPARK_OK || attr16<8, true>() != DSPARK_OK)
+  if (attr16<4>() != DSPARK_OK || attr16<8>() != DSPARK_OK || attr16<16>() != DSPARK_OK ||
+      attr16<8, true>() != DSPARK_OK)
     return DSPARK_E_HIP;
   return DSPARK_OK;
 }
@@ -370,6 +376,7 @@ bool draft16_supported(const MfmaBiasArgs& a) {
 
 dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
   if (a.mode == kModeTV) return launch16<8, true>(a, nwg, st);
+  if (a.ncols <= 64) return launch16<4>(a, nwg, st);
   return a.ncols <= 128 ? launch16<8>(a, nwg, st) : launch16<16>(a, nwg, st);
 }
 

@@ -164,12 +164,17 @@ def test_round_parity_second_seed():
 # V = 131072 is 4096 tiles of 32 rows: 8 tiles per workgroup for 33-128 columns (512
 # workgroups), 16 for 32 or more than 128 columns (256 workgroups).
 MULTI_TILE = {
-    # 16-column draft kernel, 8-wave workgroups; TV over 192 columns (two launches)
+    # 16-column draft kernel, 4-wave workgroups (up to 64 requests); TV over 192 columns
+    # (two launches)
     "mt_b64_g3": workload.custom(name="mt_b64_g3", B=64, gamma=3, V=131072, r=256, d=64,
                                  bf16=True, wsigma=0.5, logits="zipf", sigma_mix=True,
                                  table="serve"),
-    # 16-column draft kernel with a ragged last tile (V % 32 == 4: one run of four live
-    # rows) and workgroups of 8 and 9 steps
+    # ... with 24 idle columns (the last wave has none live) and a ragged last tile
+    "mt_b40_v131076": workload.custom(name="mt_b40_v131076", B=40, gamma=2, V=131076, r=256,
+                                      d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+                                      table="serve"),
+    # 16-column draft kernel, 8-wave workgroups with 28 idle columns, a ragged last tile
+    # (V % 32 == 4: one run of four live rows) and workgroups of 8 and 9 steps
     "mt_b100_v131076": workload.custom(name="mt_b100_v131076", B=100, gamma=2, V=131076,
                                        r=256, d=64, bf16=True, wsigma=0.5, logits="zipf",
                                        table="serve"),
