@@ -635,15 +635,15 @@ def draft_kernel_name(B: int, V: int, r: int) -> str:
     if r == 256 and B <= 16 and V % 4 == 0 and V <= 256 * 40 * 16:
         return "k_draft_resident (W2t held in accumulation registers and LDS for all gamma " \
             "positions, one cooperative launch per draft call)"
+    if r == 256 and B == 1 and V % 4 == 0:
+        return "k_draft_gemv (streaming kernel for one request, one vocabulary range per " \
+            "workgroup)"
     if r == 256 and 32 < B <= 256 and V % 4 == 0:
         nw = 4 if B <= 64 else (8 if B <= 128 else 16)
         return f"k_draft16<{nw}, false>" + \
             " (16x16x32 bf16 MFMA, 16-column waves)"
-    if r == 256 and B >= 32:
+    if r == 256:
         return "k_mfma_bias<NCB, draft> (32x32x16 bf16 MFMA, 32-column waves)"
-    if r == 256 and V % 4 == 0:
-        return "k_draft_gemv (streaming kernel for few requests, one vocabulary range per " \
-            "workgroup)"
     return "k_draft_row (row kernel, one request per workgroup row)"
 
 

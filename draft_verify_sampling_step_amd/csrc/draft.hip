@@ -215,10 +215,14 @@ struct DraftPlan {
 
 DraftPlan draft_plan(const dspark_dims* d, int wdt) {
   DraftPlan p{};
-  p.mfma = mfma_bias_supported(d->batch, d->rank, wdt);
-  p.rp = p.mfma ? ResidentPlan{false, 0} : resident_plan(d->batch, d->vocab, d->rank, wdt);
+  // up to 16 requests: W2t resident across the positions; one request beyond the resident
+  // kernel's vocabulary: the streaming kernel; else the matrix-core kernels, which stream
+  // W2t once per position for all requests (the streaming kernel streams it per request)
+  p.rp = resident_plan(d->batch, d->vocab, d->rank, wdt);
   p.resident = p.rp.ok;
-  p.gemv = !p.mfma && !p.resident && draft_gemv_supported(d->batch, d->vocab, d->rank, wdt);
+  p.gemv = !p.resident && d->batch == 1 &&
+           draft_gemv_supported(d->batch, d->vocab, d->rank, wdt);
+  p.mfma = !p.resident && !p.gemv && mfma_bias_supported(d->batch, d->rank, wdt);
   if (p.mfma) {
     p.nslices = mfma_grid(d->vocab, d->batch, kModeDraft);
     p.slice_len = 0;

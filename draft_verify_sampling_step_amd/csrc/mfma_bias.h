@@ -68,9 +68,11 @@ struct MfmaBiasArgs {
 // Residual rows per launch that take the thin path of the residual mode.
 constexpr int kResidThinMax = 2;
 
-// The MFMA path handles bf16 weights with r = 256 (16 k-steps of 16).
+// The MFMA path handles bf16 weights with r = 256 (16 k-steps of 16), any column count: it
+// streams W2t once per launch whatever the columns, where the row kernels stream it once
+// per column (the draft of one request prefers its own kernels, see draft.hip).
 inline bool mfma_bias_supported(int ncols, int r, int wdt) {
-  return wdt == DSPARK_BF16 && r == 256 && ncols >= 32;
+  return wdt == DSPARK_BF16 && r == 256 && ncols >= 1;
 }
 
 // Workgroups of one launch over V for `ncols` columns in `mode` (all resident at once).

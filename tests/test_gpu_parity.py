@@ -203,10 +203,15 @@ MULTI_TILE = {
     "mt_res_b16_v163840": workload.custom(name="mt_res_b16", B=16, gamma=2, V=163840, r=256,
                                           d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
                                           table="serve"),
-    # the streaming kernel for few requests, beyond the resident draft's vocabulary: two
-    # 224-row chunks per workgroup (more than 768 chunks)
-    "mt_gemv_b2_v262144": workload.custom(name="mt_gemv_b2", B=2, gamma=3, V=262144, r=256,
-                                          d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+    # beyond the resident draft's vocabulary: two requests on the 32-column matrix-core
+    # kernels (30 idle columns; residual and TV passes too)
+    "mt_b2_v262144": workload.custom(name="mt_b2_v262144", B=2, gamma=3, V=262144, r=256,
+                                     d=64, bf16=True, wsigma=0.5, logits="peaked_flat",
+                                     table="serve"),
+    # ... and one request on the streaming kernel: two 224-row chunks per workgroup (more
+    # than 768 chunks)
+    "mt_gemv_b1_v262144": workload.custom(name="mt_gemv_b1", B=1, gamma=3, V=262144, r=256,
+                                          d=64, bf16=True, wsigma=0.5, logits="zipf",
                                           table="serve"),
     # the row kernels (fp32 weights, r = 64): slices of 1280 rows, i.e. a step of four
     # 256-row tiles and a step of one, one Philox call per four rows; the last slice ends
