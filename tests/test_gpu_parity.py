@@ -132,6 +132,12 @@ SMALL = {
     "gamma1_v2": workload.custom(B=2, gamma=1, V=2, r=8, d=8),
     "mfma_b32": workload.custom(B=32, gamma=3, V=3072, r=256, d=128, bf16=True, wsigma=0.1,
                                 logits="zipf", table="serve"),
+    # the 32-column matrix-core kernels below 32 columns: one request with V % 4 != 0 (no
+    # resident or streaming kernel for it), and 20 requests (draft, residual and TV)
+    "mfma_b1_v_odd": workload.custom(B=1, gamma=5, V=3001, r=256, d=64, bf16=True,
+                                     wsigma=0.3, logits="zipf", table="serve"),
+    "mfma_b20": workload.custom(B=20, gamma=3, V=4096, r=256, d=64, bf16=True, wsigma=0.3,
+                                logits="zipf", sigma_mix=True, table="serve"),
     "mfma_b40_ragged": workload.custom(B=40, gamma=4, V=5000, r=256, d=64, bf16=True,
                                        wsigma=0.1, logits="zipf", sigma_mix=True,
                                        table="serve"),
