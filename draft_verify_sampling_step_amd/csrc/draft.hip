@@ -160,6 +160,7 @@ __global__ __launch_bounds__(256) void k_draft_final(
   const int x = won ? (int)idx : 0;
   const int prev = draft_prev(anchor, forced, kk > 0 ? best + (size_t)(kk - 1) * B : nullptr,
                               bb, G, kk + 1, V);
+  const float ux = U[((size_t)bb * G + kk) * V + x];   // issued with the dot's loads
   float dot = 0.f;
   for (int i = ph; i < r; i += 32)
     dot = fmaf(Elem<WT>::get(W1, (size_t)prev * r + i), Elem<WT>::get(W2t, (size_t)x * r + i),
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void k_draft_final(
     dot += red[w][i8][2];
   }
   const float lz = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
-  const float zx = (U[((size_t)b * G + kk) * V + x] + dot) * invT;
+  const float zx = (ux + dot) * invT;
   const size_t o = (size_t)b * G + kk;
   // a draft kernel that gave up a bounded wait has left the slots incomplete
   const bool failed =
