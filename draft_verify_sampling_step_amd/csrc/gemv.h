@@ -1,4 +1,4 @@
-// gemv.h -- the draft position kernel for few requests with bf16 weights of rank 256
+// gemv.h -- the draft position kernel for one request with bf16 weights of rank 256
 // (gemv.hip): one workgroup per contiguous vocabulary range and request.
 #pragma once
 
@@ -11,7 +11,8 @@ struct GemvPlan {
   int nwg;    // workgroups per request (at most 1024)
 };
 
-// bf16 weights, r = 256, fewer than 32 requests, V % 4 == 0 (16-byte logit quads)
+// bf16 weights, r = 256, fewer than 32 requests, V % 4 == 0 (16-byte logit quads); the
+// draft plan takes it for one request only
 bool draft_gemv_supported(int B, int V, int r, int wdt);
 GemvPlan draft_gemv_plan(int V);
 

@@ -1,8 +1,10 @@
-// gemv.hip -- the draft position kernel for few requests (B < 32) with bf16 weights of rank
-// 256: the Markov bias W1[x_{k-1}] . W2t[v] of one request is a matrix-vector product
-// [CSDN Eq. 4; XTL §4], and one position streams all of W2t (V x 512 bytes) once per
-// request.  The kernel is therefore a plain HBM stream, laid out so that nothing waits on
-// the serial chain of the draft:
+// gemv.hip -- the draft position kernel for one request with bf16 weights of rank 256, where
+// the resident draft does not apply: the Markov bias W1[x_{k-1}] . W2t[v] is a
+// matrix-vector product [CSDN Eq. 4; XTL §4], and one position streams all of W2t
+// (V x 512 bytes).  (The kernel takes a grid row per request and so streams W2t once per
+// request; from two requests on the matrix-core kernels, which stream it once for all, are
+// used instead.)  The kernel is a plain HBM stream, laid out so that nothing waits on the
+// serial chain of the draft:
 //   - a workgroup owns a contiguous range of the vocabulary, kGvRows rows per chunk, and
 //     the grid is at most 768 workgroups (three per CU at the kernel's register count), so
 //     for one request every workgroup is resident from the start (no second round of
