@@ -18,7 +18,8 @@
 // Workgroup shapes: 8 waves (128 columns, two workgroups per CU) for 65..128 columns,
 // 16 waves (256 columns, one per CU) beyond, and 4 waves (64 columns, two per CU, so two
 // waves per SIMD) up to 64 columns: there a half-idle 8-wave workgroup would spend its
-// idle waves' MFMA and epilogue work on dummy columns, which measured 10-20% slower.
+// idle waves' MFMA and epilogue work on dummy columns, which measured 10-20% slower.  The
+// TV mode takes the 4- and 8-wave shapes (up to 128 columns per launch).
 #include "mfma_bias.h"
 #include "mfma_common.h"
 
@@ -364,7 +365,7 @@ static dspark_status launch16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
 
 dspark_status draft16_prepare() {
   if (attr16<4>() != DSPARK_OK || attr16<8>() != DSPARK_OK || attr16<16>() != DSPARK_OK ||
-      attr16<8, true>() != DSPARK_OK)
+      attr16<4, true>() != DSPARK_OK || attr16<8, true>() != DSPARK_OK)
     return DSPARK_E_HIP;
   return DSPARK_OK;
 }
@@ -375,7 +376,8 @@ bool draft16_supported(const MfmaBiasArgs& a) {
 }
 
 dspark_status launch_draft16(const MfmaBiasArgs& a, int nwg, hipStream_t st) {
-  if (a.mode == kModeTV) return launch16<8, true>(a, nwg, st);
+  if (a.mode == kModeTV)
+    return a.ncols <= 64 ? launch16<4, true>(a, nwg, st) : launch16<8, true>(a, nwg, st);
   if (a.ncols <= 64) return launch16<4>(a, nwg, st);
   return a.ncols <= 128 ? launch16<8>(a, nwg, st) : launch16<16>(a, nwg, st);
 }
