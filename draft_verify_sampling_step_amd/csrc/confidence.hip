@@ -9,11 +9,25 @@
 namespace dspark {
 
 // Sum of w[j] * x[j] over j < n, lanes striding 8 elements (16-byte loads for bf16 when
-// both pointers are 16-byte aligned), element by element otherwise.
+// both pointers are 16-byte aligned), element by element otherwise.  Each lane adds its
+// terms in index order; the loads of up to eight rounds are issued before the first add.
 template <typename TA, typename TB>
 __device__ __forceinline__ float lane_dot(const TA* w, const TB* x, int n, int lane) {
   float acc = 0.f;
-  for (int j = lane; j < n; j += kWave) acc = fmaf(Elem<TA>::get(w, j), Elem<TB>::get(x, j), acc);
+  for (int jb = lane; jb < n; jb += 8 * kWave) {
+    float a[8], b[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (jb + t * kWave < n) {
+        a[t] = Elem<TA>::get(w, jb + t * kWave);
+        b[t] = Elem<TB>::get(x, jb + t * kWave);
+      }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (jb + t * kWave >= n) break;
+      acc = fmaf(a[t], b[t], acc);
+    }
+  }
   return acc;
 }
 
@@ -23,23 +37,47 @@ __device__ __forceinline__ float lane_dot<uint16_t, uint16_t>(const uint16_t* w,
                                                              int lane) {
   float acc = 0.f;
   const bool aligned = ((((uintptr_t)w) | ((uintptr_t)x)) & 15) == 0;
-  int j0 = 0;
+  int jt = 0;
   if (aligned) {
     const int nv = n & ~511;   // whole 64-lane x 8-element rounds
-    for (int j = lane * 8; j < nv; j += kWave * 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(w + j);
-      const uint4 b = *reinterpret_cast<const uint4*>(x + j);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+    for (int jb = lane * 8; jb < nv; jb += 8 * kWave * 8) {
+      uint4 a[8], b[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc = fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc);
-        acc = fmaf(__uint_as_float(av[q] & 0xFFFF0000u), __uint_as_float(bv[q] & 0xFFFF0000u),
-                   acc);
+      for (int t = 0; t < 8; ++t)
+        if (jb + t * kWave * 8 < nv) {
+          a[t] = *reinterpret_cast<const uint4*>(w + jb + t * kWave * 8);
+          b[t] = *reinterpret_cast<const uint4*>(x + jb + t * kWave * 8);
+        }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (jb + t * kWave * 8 >= nv) break;
+        const uint32_t av[4] = {a[t].x, a[t].y, a[t].z, a[t].w};
+        const uint32_t bv[4] = {b[t].x, b[t].y, b[t].z, b[t].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fmaf(__uint_as_float(av[q] << 16), __uint_as_float(bv[q] << 16), acc);
+          acc = fmaf(__uint_as_float(av[q] & 0xFFFF0000u),
+                     __uint_as_float(bv[q] & 0xFFFF0000u), acc);
+        }
       }
     }
-    j0 = nv;
+    jt = nv;
   }
-  for (int j = j0 + lane; j < n; j += kWave) acc = fmaf(bf16_to_f32(w[j]), bf16_to_f32(x[j]), acc);
+  // the rest element by element
+  for (int jb = jt + lane; jb < n; jb += 8 * kWave) {
+    float a[8], b[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (jb + t * kWave < n) {
+        a[t] = bf16_to_f32(w[jb + t * kWave]);
+        b[t] = bf16_to_f32(x[jb + t * kWave]);
+      }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (jb + t * kWave >= n) break;
+      acc = fmaf(a[t], b[t], acc);
+    }
+  }
   return acc;
 }
 

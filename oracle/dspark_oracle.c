@@ -274,7 +274,9 @@ void ora_schedule(int32_t B, int32_t gamma, const double* c, const double* sps, 
         tau = tau_next;
         N = N + 1;
         best = theta_next;
-        ell[cand[t].b] = cand[t].j;
+        /* with every c <= 1 a request's candidates are taken in j order, so this is its
+         * newest j; above 1 (outside the sigmoid's range) it is the largest admitted j */
+        if (cand[t].j > ell[cand[t].b]) ell[cand[t].b] = cand[t].j;
     }
     *theta = best;
     *n_total = N;

@@ -369,6 +369,15 @@ def test_schedule_edge_cases_bit_exact():
         sr = 1000.0 / (12.0 + 0.05 * np.arange(Br * (Gr + 1) + 1))
         cases.append((cr, sr, 0))
         cases.append((cr, sr, 1))
+    # every c = 1/2: a_{b,j} = 2^-(j+1) for every request, so the walk stops inside a group
+    # of equal a spread over all requests (admitted in request order)
+    half = np.full((16, 8), 0.5, np.float32)
+    cases.append((half, 1000.0 / (10 + np.arange(16 * 9 + 1)), 0))
+    cases.append((half, 1000.0 / (10 + 0.3 * np.arange(16 * 9 + 1)), 0))
+    # confidences above 1 (outside the sigmoid's range): runs sorted by insertion first
+    up = rng.choice([0.5, 1.0, 2.0], size=(9, 5)).astype(np.float32)
+    cases.append((up, 1000.0 / (10 + np.arange(9 * 6 + 1)), 0))
+    cases.append((up, np.full(9 * 6 + 1, 2.0), 1))
     for c, sps_, mode in cases:
         ell_o, th_o, n_o = oracle.schedule(c, sps_, mode)
         ell_g, th_g, n_g = ds.dspark_schedule(dev(c), dev(np.asarray(sps_, np.float64)), mode)
@@ -390,6 +399,11 @@ def test_schedule_topk_bit_exact():
                   4095))
     cases.append((rng.uniform(size=(1, 4)).astype(np.float32), np.full(6, 3.0), 2))
     cases.append((rng.uniform(size=(3, 5)).astype(np.float32), np.full(19, 2.0), 7))
+    # prefixes that end inside a group of equal a spread over many requests
+    half = np.full((16, 8), 0.5, np.float32)
+    cases += [(half, np.full(16 * 9 + 1, 2.0), K) for K in (1, 7, 15, 16, 17, 40, 100, 127)]
+    up = rng.choice([0.5, 1.0, 2.0], size=(9, 5)).astype(np.float32)   # unsorted runs
+    cases += [(up, np.full(9 * 6 + 1, 2.0), K) for K in (3, 10, 21, 44)]
     for c_, sps_, K in cases:
         ell_o, th_o, n_o = oracle.schedule_topk(c_, sps_, K)
         ell_g, th_g, n_g = ds.dspark_schedule_topk(dev(c_), dev(np.asarray(sps_, np.float64)), K)

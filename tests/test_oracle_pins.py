@@ -343,6 +343,20 @@ def test_schedule_tie_order_request_then_position():
     assert list(ell) == [2] and theta == 3.0
 
 
+def test_schedule_confidence_above_one_reports_the_largest_admitted_position():
+    """Outside the sigmoid's range (c > 1) a request's survival can grow, so its admitted
+    positions need not come in j order; ell_b is then the largest admitted j (greedy and
+    top-K alike).  c = (1/2, 2): a = (1/2, 1), so position 2 is taken before position 1."""
+    c = np.array([[0.5, 2.0]], np.float32)
+    flat = np.full(4, 2.0)            # every admission raises Theta: both are taken
+    ell, theta, n = oracle.schedule(c, flat, 0)
+    assert list(ell) == [2] and n == 3 and theta == (1.0 + 1.0 + 0.5) * 2.0
+    ell, theta, n = oracle.schedule_topk(c, flat, 1)   # only the first in order
+    assert list(ell) == [2] and n == 2 and theta == 2.0 * 2.0
+    ell, _, n = oracle.schedule_topk(c, flat, 2)
+    assert list(ell) == [2] and n == 3
+
+
 def _tau(c, ell):
     """tau(ell) = B + sum_b sum_{j<=ell_b} prod_{i<=j} c_bi (expected output tokens)."""
     B = c.shape[0]
