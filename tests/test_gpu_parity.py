@@ -273,6 +273,47 @@ def test_residual_pass_by_rejection_count(nrej, V, wsigma):
     torch.cuda.synchronize()
 
 
+# more requests than the target-row pass maps in LDS (8192): the rows are listed by the
+# plan kernel; the matrix-core kernels run 33 column groups per position
+MANY = {
+    "many_rows_fp32": workload.custom(B=8200, gamma=2, V=200, r=8, d=16, wsigma=0.3,
+                                      logits="zipf", table="serve"),
+    "many_mfma_bf16": workload.custom(B=8200, gamma=2, V=1024, r=256, d=16, bf16=True,
+                                      wsigma=0.3, logits="zipf", table="serve"),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(MANY))
+def test_many_requests(name):
+    """Draft, confidence and verification (a ragged budget and the full block) for every
+    request; the scheduler's own limit (B * gamma <= 4096) keeps it out of this shape."""
+    cfg = MANY[name]
+    _flush(f"many requests {name}: {cfg}")
+    inp = workload.generate(cfg, 3)
+    D = DeviceInputs(inp)
+    od = par_draft(inp)
+    tok_o = od["tokens"]
+    forced = dev(tok_o)
+    tg, lg, sg = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, cfg.temperature,
+                                        inp.seed, forced=forced)
+    tg_h, lg_h, sg_h = host(tg), host(lg), host(sg)
+    mism = compare_tokens(tg_h, tok_o, od["gap"], "draft tokens")
+    assert_abs(sg_h, od["lse"], "draft lse", 1e-4)
+    assert_rel(np.exp(lg_h.astype(np.float64)), np.exp(od["logp"]), "p_d(x_k)", mask=~mism)
+    c_o = oracle.confidence(inp.h, inp.W1, inp.w, inp.anchor, tok_o)
+    assert_rel(host(ds.dspark_confidence(D.h, D.W1, D.w, D.anchor, forced)), c_o, "confidence")
+    T = workload.synthesize_target(inp, tok_o)
+    Td = dev(T)
+    for ell in ((np.arange(cfg.B) % (cfg.gamma + 1)).astype(np.int32),
+                np.full(cfg.B, cfg.gamma, np.int32)):
+        _flush(f"many requests {name}: verify, ell sum {int(ell.sum())}")
+        n_g, out_g, pt_g = ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, forced, lg, sg, Td,
+                                            dev(ell), cfg.temperature, inp.seed)
+        check_verify(inp, tok_o, T, ell, host(n_g), host(out_g), host(pt_g))
+    torch.cuda.synchronize()
+
+
 def test_graph_replay_matches_eager():
     """A round (draft, confidence, schedule, verify) captured in a HIP graph: every replay,
     with eager work and synchronisation between replays, equals the eager round bit for bit."""
