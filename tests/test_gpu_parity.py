@@ -130,6 +130,12 @@ SMALL = {
     "bf16_rows_b16": workload.custom(B=16, gamma=4, V=2048, r=256, d=64, bf16=True,
                                      wsigma=0.1, logits="zipf", table="serve"),
     "gamma1_v2": workload.custom(B=2, gamma=1, V=2, r=8, d=8),
+    # the longest draft (gamma = 64: one decision lane per row, 65 output slots), on the
+    # row kernels and on the resident draft
+    "gamma64_rows": workload.custom(B=2, gamma=64, V=300, r=8, d=8, wsigma=0.3,
+                                    logits="zipf", table="serve"),
+    "gamma64_resident": workload.custom(B=3, gamma=64, V=1024, r=256, d=16, bf16=True,
+                                        wsigma=0.3, logits="zipf", table="serve"),
     "mfma_b32": workload.custom(B=32, gamma=3, V=3072, r=256, d=128, bf16=True, wsigma=0.1,
                                 logits="zipf", table="serve"),
     # the 32-column matrix-core kernels below 32 columns: one request with V % 4 != 0 (no
