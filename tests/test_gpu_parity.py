@@ -136,6 +136,11 @@ SMALL = {
                                     logits="zipf", table="serve"),
     "gamma64_resident": workload.custom(B=3, gamma=64, V=1024, r=256, d=16, bf16=True,
                                         wsigma=0.3, logits="zipf", table="serve"),
+    # the largest rank (row kernels) and a wide hidden state with odd d, so the confidence
+    # head's bf16 rows are not 16-byte aligned (element loads, several batches of rounds)
+    "wide_r1024_d5001": workload.custom(B=3, gamma=3, V=700, r=1024, d=5001, bf16=True,
+                                        wsigma=0.05, logits="zipf", table="serve"),
+    "wide_r1024_fp32": workload.custom(B=2, gamma=2, V=513, r=1024, d=4608, wsigma=0.05),
     "mfma_b32": workload.custom(B=32, gamma=3, V=3072, r=256, d=128, bf16=True, wsigma=0.1,
                                 logits="zipf", table="serve"),
     # the 32-column matrix-core kernels below 32 columns: one request with V % 4 != 0 (no
