@@ -37,7 +37,11 @@ def _hipcc() -> str:
 # Per-file device code generation options.  resident.hip holds W2t in accumulation registers
 # and feeds them to the matrix cores as the A operand; with the VGPR form of MFMA its
 # accumulators and epilogue stay in ordinary vector registers (no copies between the files).
-FILE_FLAGS = {"resident.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# loss.hip claims rows with one lane's returning atomic whose value is used an exchange
+# later; the atomic optimizer would rewrite it into a wave-wide form that reads the result
+# back at once, and so wait for the round trip there.
+FILE_FLAGS = {"resident.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "loss.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:

@@ -20,8 +20,11 @@
 // Instead one cooperative launch keeps every logit on chip from its single read to the
 // gradient write:
 //   * a row's vocabulary is cut into C chunks of at most 8192 entries; a "stream" of C
-//     workgroups (chunk c of rows p, p + P, p + 2P, ...) works through its rows together,
-//     P streams at once, every workgroup resident (cooperative launch);
+//     workgroups (chunk c of each of its rows) works through its rows together, P streams
+//     at once, every workgroup resident (cooperative launch).  Stream p starts with rows p
+//     and p + P; every further row is claimed from a row counter one exchange ahead, so
+//     the streams that run faster (their workgroups placed first on their compute units)
+//     take more rows;
 //   * a workgroup is eight waves (two per SIMD, so two workgroups pack evenly on a compute
 //     unit), 16 entries of the current row per lane in registers; the next row's chunk
 //     streams into LDS by direct global-to-LDS loads, which the compiler's wait counting
@@ -34,8 +37,8 @@
 //     no store-completion wait and no cache-wide fence is involved;
 //   * every wait is bounded: a poll that runs past its limit raises a fault word, the
 //     stream stops, and the loss is written as NaN.
-// HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 48 bytes of
-// published partials per chunk and row (cleared before the launch).
+// HBM traffic: 8 bytes read and 4 written per logit (the gradient), plus 56 bytes of
+// published words per chunk and row (cleared before the launch).
 #include <atomic>
 
 #include "dspark_dev.h"
@@ -69,7 +72,9 @@ struct LossArgs {
   float* terms;         // [R][3] or null
   double* rowloss;      // [R] weighted row contributions
   unsigned long long* part1;   // [R][C][4] published (max_d, sum_d, max_t, sum_t)
-  unsigned long long* part2;   // [R][C][2] published (l1, S)
+  unsigned long long* part2;   // [R][C][3] published (l1, S, chunk 0 only: the row after
+                               // the next one of the stream, claimed; R when none)
+  unsigned int* row_ctr;       // rows claimed beyond the first 2P (cleared before launch)
   uint32_t* fault;
   int R, G, V, C, L, P;
   double a_ce, a_l1, a_conf, inv_W;
@@ -86,22 +91,26 @@ __device__ __forceinline__ void raw_barrier() {
 // Wave 0: publish this workgroup's partials -- lanes 0..na-1 hold the values of slot_a,
 // lanes na..na+nb-1 those of slot_b.  Each lane's word is a device-scope atomic store that
 // needs no ordering against any other (see kSlotValid), so nothing waits for it.
+// Lane raw_lane (if any) publishes raw_bits as the word's value instead of a float.
 __device__ __forceinline__ void publish(unsigned long long* slot_a, int na,
-                                        unsigned long long* slot_b, int nb, double v, int lane) {
+                                        unsigned long long* slot_b, int nb, double v, int lane,
+                                        int raw_lane = -1, uint32_t raw_bits = 0u) {
   unsigned long long* w = lane < na ? slot_a + lane : (lane < na + nb ? slot_b + (lane - na) : nullptr);
+  const uint32_t bits = lane == raw_lane ? raw_bits : __float_as_uint((float)v);
   if (w)
-    __hip_atomic_store(w, kSlotValid | (unsigned long long)__float_as_uint((float)v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w, kSlotValid | (unsigned long long)bits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Poll the NA words at pa and the NB words at pb (device-scope atomic loads, which bypass
-// the non-coherent caches) until every one is published; their values into qa, qb.  Returns
+// the non-coherent caches) until every one is published -- of pa's words only the first
+// na_need must be, the others are read as they are; their values into qa, qb.  Returns
 // false when the wait gave up: its poll limit ran out (the fault word is raised) or another
 // workgroup raised the fault word.
 template <int NA, int NB>
 __device__ __forceinline__ bool await_words(const LossArgs& a, const unsigned long long* pa,
                                             const unsigned long long* pb, float* qa,
-                                            float* qb) {
+                                            float* qb, int na_need = NA) {
   uint32_t polls = 0;
   for (;;) {
     unsigned long long wa[NA], wb[NB > 0 ? NB : 1];
@@ -114,7 +123,7 @@ __device__ __forceinline__ bool await_words(const LossArgs& a, const unsigned lo
     bool all = true;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      all = all && (wa[i] >> 32) != 0ull;
+      all = all && (i >= na_need || (wa[i] >> 32) != 0ull);
       qa[i] = __uint_as_float((uint32_t)wa[i]);
     }
 #pragma unroll
@@ -291,6 +300,7 @@ struct LossShared {
   float r2[3];               // current row: (S, w alpha_ce, w alpha_l1)
   int y;                     // current row: the label, clamped into the vocabulary
   int stop;
+  int rn2;                   // the stream's row after the next one (R: none)
   double lse;                // wave 0's: lse of the current row's draft logits (kept in LDS
                              // rather than across the sweeps in registers)
 };
@@ -375,17 +385,21 @@ __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, 
   double l1 = 0.0, S = 0.0, m_d = -INFINITY, s_d = 0.0, m_t = -INFINITY, s_t = 0.0;
   bool mine = true;
   for (int cc = lane; cc < a.C && mine; cc += kWave) {
-    const unsigned long long* p2 = a.part2 + ((size_t)r * a.C + cc) * 2;
-    float q2[2], q1[4];
+    const unsigned long long* p2 = a.part2 + ((size_t)r * a.C + cc) * 3;
+    const unsigned long long* p1 = a.part1 + ((size_t)rn * a.C + cc) * 4;
+    // chunk 0 also carries the claimed row (a third word; the other chunks leave theirs
+    // unpublished)
+    float q2[3], q1[4];
+    const int need = cc == 0 ? 3 : 2;
+    mine = has_next ? await_words<3, 4>(a, p2, p1, q2, q1, need)
+                    : await_words<3, 0>(a, p2, nullptr, q2, nullptr, need);
     if (has_next) {
-      mine = await_words<2, 4>(a, p2, a.part1 + ((size_t)rn * a.C + cc) * 4, q2, q1);
       ml_add(m_d, s_d, q1[0], q1[1]);
       ml_add(m_t, s_t, q1[2], q1[3]);
-    } else {
-      mine = await_words<2, 0>(a, p2, nullptr, q2, nullptr);
     }
     l1 += (double)q2[0];
     S += (double)q2[1];
+    if (cc == 0) sh.rn2 = (int)__float_as_uint(q2[2]);
   }
   ok = __ballot(!mine) == 0ull;
   if (!ok) return;
@@ -481,8 +495,17 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
   }
   raw_barrier();
 
-  for (int r = p; r < a.R && !sh.stop; r += a.P) {
-    const int rn = r + a.P;
+  // The stream's first two rows are p and p + P; each later one is claimed from the row
+  // counter by lane 2 of chunk 0's lead wave an exchange before that exchange publishes it
+  // (so the claim's round trip is long over when its value is used): `pending` is the row
+  // after the next one.
+  auto claim = [&]() -> uint32_t {   // (R < 2^24 rows: no overflow)
+    return __hip_atomic_fetch_add(a.row_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int r = p, rn = p + a.P;
+  uint32_t pending = 0u;   // a claim: the row 2P + pending
+  if (c == 0 && lead && lane == 2 && rn < a.R) pending = claim();
+  while (r < a.R && !sh.stop) {
     const bool has_next = rn < a.R;
     // 1. partials
     const float Md = sh.r1[0], Ld = sh.r1[1], Mt = sh.r1[2], Lt = sh.r1[3];
@@ -515,11 +538,14 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
     raw_barrier();
     // 2. the stream's exchange
     if (lead) {
-      double v = has_next ? combine_waves1(sh, lane - 2 < 0 ? 63 : lane - 2) : 0.0;
+      const int na = c == 0 ? 3 : 2;   // chunk 0: l1, S and the claimed row
+      double v = has_next ? combine_waves1(sh, lane - na < 0 ? 63 : lane - na) : 0.0;
       if (lane < 2)
         for (int w = 0; w < kLossWaves; ++w) v += (double)sh.w2[w][lane];
-      publish(a.part2 + ((size_t)r * a.C + c) * 2, 2,
-              a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v, lane);
+      publish(a.part2 + ((size_t)r * a.C + c) * 3, na,
+              a.part1 + ((size_t)(has_next ? rn : r) * a.C + c) * 4, has_next ? 4 : 0, v, lane,
+              c == 0 ? 2 : -1,
+              has_next ? min(2u * (uint32_t)a.P + pending, (uint32_t)a.R) : (uint32_t)a.R);
       bool ok = true;
       combine_step(a, sh, r, rn, has_next, c, rs, lane, ok);
       if (lane == 0) sh.stop = ok ? 0 : 1;
@@ -542,15 +568,20 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
       }
       store_grad<VEC>(a, r, c, tid, g);
     }
+    const int rn2 = sh.rn2;
+    if (c == 0 && lead && lane == 2 && rn2 < a.R) pending = claim();   // for the next exchange
     if (has_next) {
       read_stage(stage, tid, d, t);
-      if (rn + a.P < a.R) stage_row<VEC>(a, rn + a.P, c, tid, wave, stage_lds, stage);
+      if (rn2 < a.R) stage_row<VEC>(a, rn2, c, tid, wave, stage_lds, stage);
     }
+    r = rn;
+    rn = rn2;
   }
   if constexpr (VEC) wait_vm<0>();   // nothing in flight into LDS when the workgroup ends
 }
 
-// clears the published words (part1 and part2, n words from `words`) and the fault word
+// clears the published words (part1, part2 and the row counter, n words from `words`) and
+// the fault word
 __global__ __launch_bounds__(256) void k_loss_init(unsigned long long* __restrict__ words,
                                                    size_t n, uint32_t* __restrict__ fault) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
@@ -581,8 +612,9 @@ using namespace dspark;
 namespace {
 
 struct LossWs {
-  unsigned long long* part1;   // published words: part1 then part2, one block
+  unsigned long long* part1;   // published words: part1, part2 and the row counter, one block
   unsigned long long* part2;
+  unsigned int* row_ctr;
   size_t nwords;
   double* rowloss;
   uint32_t* fault;
@@ -595,9 +627,10 @@ LossWs loss_ws(int R, int V, void* base) {
   const int C = loss_chunks(V);
   Carve c(base);
   LossWs w;
-  w.nwords = (size_t)R * C * 6;
+  w.nwords = (size_t)R * C * 7 + 1;
   w.part1 = c.take<unsigned long long>(w.nwords);
   w.part2 = w.part1 ? w.part1 + (size_t)R * C * 4 : nullptr;
+  w.row_ctr = w.part1 ? reinterpret_cast<unsigned int*>(w.part1 + (size_t)R * C * 7) : nullptr;
   w.rowloss = c.take<double>((size_t)R);
   w.fault = c.take<uint32_t>(1);
   w.bytes = align_up(c.off, 256);
@@ -660,6 +693,7 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
   a.zd = zd; a.zt = zt; a.labels = labels; a.conf = conf_logit;
   a.grad = grad_zd; a.grad_conf = grad_conf; a.terms = terms;
   a.rowloss = w.rowloss; a.part1 = w.part1; a.part2 = w.part2; a.fault = w.fault;
+  a.row_ctr = w.row_ctr;
   a.R = R; a.G = G; a.V = V;
   a.C = loss_chunks(V);
   a.L = (V + 4 * a.C - 1) / (4 * a.C) * 4;
