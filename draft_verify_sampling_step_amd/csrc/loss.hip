@@ -70,11 +70,13 @@ struct LossArgs {
   float* grad;          // [R][V] or null
   float* grad_conf;     // [R] or null
   float* terms;         // [R][3] or null
-  double* rowloss;      // [R] weighted row contributions
+  double* rowloss;      // [R] weighted row contributions (device-scope atomic stores)
+  double* loss;         // [1] out: their sum, taken by the last workgroup to finish
   unsigned long long* part1;   // [R][C][4] published (max_d, sum_d, max_t, sum_t)
   unsigned long long* part2;   // [R][C][3] published (l1, S, chunk 0 only: the row after
                                // the next one of the stream, claimed; R when none)
   unsigned int* row_ctr;       // rows claimed beyond the first 2P (cleared before launch)
+  unsigned int* done_ctr;      // workgroups finished (cleared before launch)
   uint32_t* fault;
   int R, G, V, C, L, P;
   double a_ce, a_l1, a_conf, inv_W;
@@ -422,7 +424,9 @@ __device__ __forceinline__ void combine_step(const LossArgs& a, LossShared& sh, 
       const double softplus = (double)fmaxf(lf, 0.f) + (double)log1pf(e);
       const double bce = softplus - at * l;
       const double cs = lf >= 0.f ? 1.0 / (1.0 + (double)e) : (double)e / (1.0 + (double)e);
-      a.rowloss[r] = wk * (a.a_ce * ce + a.a_l1 * l1 + a.a_conf * bce);
+      // read by the last workgroup to finish, at the device's coherence point
+      __hip_atomic_store(a.rowloss + r, wk * (a.a_ce * ce + a.a_l1 * l1 + a.a_conf * bce),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.terms) {
         a.terms[3 * (size_t)r] = (float)ce;
         a.terms[3 * (size_t)r + 1] = (float)l1;
@@ -577,32 +581,42 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
     r = rn;
     rn = rn2;
   }
-  if constexpr (VEC) wait_vm<0>();   // nothing in flight into LDS when the workgroup ends
+  // nothing in flight into LDS when the workgroup ends; this workgroup's row outputs have
+  // reached the coherence point before it counts itself in
+  wait_vm<0>();
+  raw_barrier();
+  if (tid == 0)
+    sh.stop = __hip_atomic_fetch_add(a.done_ctr, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.P * a.C) - 1u;
+  raw_barrier();
+  if (!sh.stop) return;
+  // the last one: the loss as a fixed-order sum (256 strided partial sums, then a tree),
+  // NaN after a fault
+  __shared__ double psum[256];
+  if (tid < 256) {
+    double v = 0.0;
+    for (int i = tid; i < a.R; i += 256)
+      v += __hip_atomic_load(a.rowloss + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    psum[tid] = v;
+  }
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) psum[tid] += psum[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0)
+    a.loss[0] = __hip_atomic_load(a.fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u
+                    ? (double)NAN
+                    : psum[0];
 }
 
-// clears the published words (part1, part2 and the row counter, n words from `words`) and
+// clears the published words (part1, part2 and the two counters, n words from `words`) and
 // the fault word
 __global__ __launch_bounds__(256) void k_loss_init(unsigned long long* __restrict__ words,
                                                    size_t n, uint32_t* __restrict__ fault) {
   const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
   for (size_t j = i; j < n; j += (size_t)gridDim.x * blockDim.x) words[j] = 0ull;
   if (i == 0) *fault = 0u;
-}
-
-// loss = sum of the row contributions in a fixed order (deterministic), NaN after a fault
-__global__ __launch_bounds__(256) void k_loss_sum(const double* __restrict__ rowloss, int R,
-                                                  const uint32_t* __restrict__ fault,
-                                                  double* __restrict__ loss) {
-  __shared__ double part[256];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < R; i += 256) s += rowloss[i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) loss[0] = *fault ? NAN : part[0];
 }
 
 }  // namespace dspark
@@ -612,9 +626,10 @@ using namespace dspark;
 namespace {
 
 struct LossWs {
-  unsigned long long* part1;   // published words: part1, part2 and the row counter, one block
+  unsigned long long* part1;   // published words: part1, part2 and the two counters, one block
   unsigned long long* part2;
   unsigned int* row_ctr;
+  unsigned int* done_ctr;
   size_t nwords;
   double* rowloss;
   uint32_t* fault;
@@ -627,10 +642,11 @@ LossWs loss_ws(int R, int V, void* base) {
   const int C = loss_chunks(V);
   Carve c(base);
   LossWs w;
-  w.nwords = (size_t)R * C * 7 + 1;
+  w.nwords = (size_t)R * C * 7 + 2;
   w.part1 = c.take<unsigned long long>(w.nwords);
   w.part2 = w.part1 ? w.part1 + (size_t)R * C * 4 : nullptr;
   w.row_ctr = w.part1 ? reinterpret_cast<unsigned int*>(w.part1 + (size_t)R * C * 7) : nullptr;
+  w.done_ctr = w.part1 ? reinterpret_cast<unsigned int*>(w.part1 + (size_t)R * C * 7 + 1) : nullptr;
   w.rowloss = c.take<double>((size_t)R);
   w.fault = c.take<uint32_t>(1);
   w.bytes = align_up(c.off, 256);
@@ -694,6 +710,8 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
   a.grad = grad_zd; a.grad_conf = grad_conf; a.terms = terms;
   a.rowloss = w.rowloss; a.part1 = w.part1; a.part2 = w.part2; a.fault = w.fault;
   a.row_ctr = w.row_ctr;
+  a.done_ctr = w.done_ctr;
+  a.loss = loss;
   a.R = R; a.G = G; a.V = V;
   a.C = loss_chunks(V);
   a.L = (V + 4 * a.C - 1) / (4 * a.C) * 4;
@@ -718,6 +736,5 @@ extern "C" dspark_status dspark_draft_loss(int32_t B, int32_t G, int32_t V, cons
     (void)hipGetLastError();
     return DSPARK_E_HIP;
   }
-  hipLaunchKernelGGL(k_loss_sum, dim3(1), dim3(256), 0, st, w.rowloss, R, w.fault, loss);
-  return launch_status();
+  return DSPARK_OK;
 }
