@@ -186,7 +186,7 @@ __device__ __forceinline__ int fresh(int x) {
 }
 
 template <bool VEC>
-__device__ __forceinline__ void stage_row(const LossArgs& a, int r, int c, int ct_, int wave,
+__device__ __forceinline__ void stage_row(const LossArgs& a, int r, int c, int ct_,
                                           uint32_t stage_lds, float* stage) {
   const int ct = fresh(ct_);
   const int c0 = c * a.L;
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
   float d[kLossPer], t[kLossPer];
 
   // prologue: row p's normalisers
-  stage_row<VEC>(a, p, c, tid, wave, stage_lds, stage);
+  stage_row<VEC>(a, p, c, tid, stage_lds, stage);
   wait_stage<VEC>();
   {
     ML md, mt;
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
     }
   }
   read_stage(stage, tid, d, t);
-  if (p + a.P < a.R) stage_row<VEC>(a, p + a.P, c, tid, wave, stage_lds, stage);
+  if (p + a.P < a.R) stage_row<VEC>(a, p + a.P, c, tid, stage_lds, stage);
   raw_barrier();
   if (lead) {
     const double v = combine_waves1(sh, lane);
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kLossThreads, kLossWavesPerSimd) void k_draft_loss(
     if (c == 0 && lead && lane == 2 && rn2 < a.R) pending = claim();   // for the next exchange
     if (has_next) {
       read_stage(stage, tid, d, t);
-      if (rn2 < a.R) stage_row<VEC>(a, rn2, c, tid, wave, stage_lds, stage);
+      if (rn2 < a.R) stage_row<VEC>(a, rn2, c, tid, stage_lds, stage);
     }
     r = rn;
     rn = rn2;

@@ -16,8 +16,8 @@
 namespace dspark {
 
 // grid (slices, B, gamma)
-__global__ __launch_bounds__(256) void k_tv_rows(const float* __restrict__ T, int B, int G,
-                                                 int V, int slice_len, int nslices, float invT,
+__global__ __launch_bounds__(256) void k_tv_rows(const float* __restrict__ T, int G, int V,
+                                                 int slice_len, int nslices, float invT,
                                                  float2* __restrict__ part) {
   __shared__ float red[16];
   const int s = blockIdx.x, b = blockIdx.y, kk = blockIdx.z;
@@ -196,7 +196,7 @@ extern "C" dspark_status dspark_accept_rate_tv(const dspark_dims* dm, const floa
   const float invT = 1.0f / temperature;
   if (mfma && mfma_prepare() != DSPARK_OK) return DSPARK_E_HIP;
 
-  hipLaunchKernelGGL(k_tv_rows, dim3(rs.count, B, G), dim3(256), 0, st, T, B, G, V, rs.len,
+  hipLaunchKernelGGL(k_tv_rows, dim3(rs.count, B, G), dim3(256), 0, st, T, G, V, rs.len,
                      rs.count, invT, w.part);
   hipLaunchKernelGGL(k_tv_lse, dim3((n + 255) / 256), dim3(256), 0, st, w.part, n, rs.count,
                      w.lse_t);
