@@ -291,6 +291,11 @@ MANY = {
                                       logits="zipf", table="serve"),
     "many_mfma_bf16": workload.custom(B=8200, gamma=2, V=1024, r=256, d=16, bf16=True,
                                       wsigma=0.3, logits="zipf", table="serve"),
+    # the largest batch the calls accept (65535 requests: the row kernels' grid height)
+    "max_batch_fp32": workload.custom(B=65535, gamma=1, V=64, r=8, d=8, wsigma=0.3,
+                                      logits="zipf", table="serve"),
+    "max_batch_bf16": workload.custom(B=65535, gamma=1, V=256, r=256, d=8, bf16=True,
+                                      wsigma=0.3, logits="zipf", table="serve"),
 }
 
 
