@@ -106,9 +106,11 @@ def check_loss(tr, rows=None, g=None, scale=1.0):
     (3, 4, 10001, 2, {"labels_oob": True}),      # V % 4 != 0: direct loads; clamped labels
     (1, 1, 1, 3, {}),                            # one-token vocabulary: p_d = p_t = 1
     (2, 2, 4, 4, {}),                            # one quad
-    (32, 16, 5000, 5, {}),                       # more rows than streams: rows in turn
+    (32, 16, 5000, 5, {}),                       # more rows than streams: rows claimed
     (2, 4, 9000, 6, {"neg_inf_band": (4400, 9000)}),   # a whole chunk at -inf
     (4, 16, 151936, 7, {}),                      # the full vocabulary, 38 chunks per row
+    (1, 2, (1 << 22) - 5, 8, {}),                # the largest vocabulary: 512 chunks per
+                                                 # row (each poller lane takes 8), V % 4 != 0
 ])
 def test_draft_loss_matches_oracle(B, G, V, seed, extra):
     _flush(f"draft loss B={B} G={G} V={V} seed={seed} {extra}")

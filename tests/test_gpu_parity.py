@@ -141,6 +141,9 @@ SMALL = {
     "wide_r1024_d5001": workload.custom(B=3, gamma=3, V=700, r=1024, d=5001, bf16=True,
                                         wsigma=0.05, logits="zipf", table="serve"),
     "wide_r1024_fp32": workload.custom(B=2, gamma=2, V=513, r=1024, d=4608, wsigma=0.05),
+    # a vocabulary of 2^22 + 3 entries (row kernels; every index past 2^22)
+    "huge_vocab_fp32": workload.custom(B=2, gamma=2, V=(1 << 22) + 3, r=8, d=8, wsigma=0.3,
+                                       logits="zipf", table="serve"),
     "mfma_b32": workload.custom(B=32, gamma=3, V=3072, r=256, d=128, bf16=True, wsigma=0.1,
                                 logits="zipf", table="serve"),
     # the 32-column matrix-core kernels below 32 columns: one request with V % 4 != 0 (no
