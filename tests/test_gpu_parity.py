@@ -136,6 +136,10 @@ SMALL = {
                                     logits="zipf", table="serve"),
     "gamma64_resident": workload.custom(B=3, gamma=64, V=1024, r=256, d=16, bf16=True,
                                         wsigma=0.3, logits="zipf", table="serve"),
+    # gamma = 64 at 64 requests: 4096 candidates, the scheduler's limit; the 4-wave draft
+    # kernel, 32 TV launches
+    "gamma64_b64_mfma": workload.custom(B=64, gamma=64, V=2048, r=256, d=16, bf16=True,
+                                        wsigma=0.3, logits="zipf", table="serve"),
     # the largest rank (row kernels) and a wide hidden state with odd d, so the confidence
     # head's bf16 rows are not 16-byte aligned (element loads, several batches of rounds)
     "wide_r1024_d5001": workload.custom(B=3, gamma=3, V=700, r=1024, d=5001, bf16=True,
