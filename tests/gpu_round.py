@@ -183,7 +183,7 @@ def par_accept_tv(inp, tokens, T_rows, rows=None):
     return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]))
 
 
-def check_verify(inp, tokens_ref, T, ell, gpu_n, gpu_out, gpu_pt, rows=None):
+def check_verify(inp, tokens_ref, T, ell, gpu_n, gpu_out, gpu_pt, rows=None, rel=REL):
     """Compare GPU verification outputs with the oracle for `rows` (default: all).
     T holds either every request or exactly the requests `rows`, in that order."""
     cfg = inp.cfg
@@ -196,7 +196,7 @@ def check_verify(inp, tokens_ref, T, ell, gpu_n, gpu_out, gpu_pt, rows=None):
     # p_t(x_k) for k <= ell_b
     G = cfg.gamma
     kmask = np.arange(G)[None, :] < ell[rows][:, None]
-    assert_rel(pt_g, ref["pt_tok"], "p_t(x_k)", mask=kmask)
+    assert_rel(pt_g, ref["pt_tok"], "p_t(x_k)", rel=rel, mask=kmask)
     assert np.all(np.isnan(pt_g[~kmask])), "p_t beyond ell must be NaN"
     for i, b in enumerate(rows):
         n_r = int(ref["n_accept"][i])
