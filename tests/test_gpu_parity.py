@@ -135,6 +135,7 @@ SMALL = {
     "bf16_rows_b16": workload.custom(B=16, gamma=4, V=2048, r=256, d=64, bf16=True,
                                      wsigma=0.1, logits="zipf", table="serve"),
     "gamma1_v2": workload.custom(B=2, gamma=1, V=2, r=8, d=8),
+    "no_hidden_d0": workload.custom(B=4, gamma=3, V=500, r=16, d=0),   # h empty: W1 part only
     # the longest draft (gamma = 64: one decision lane per row, 65 output slots), on the
     # row kernels and on the resident draft
     "gamma64_rows": workload.custom(B=2, gamma=64, V=300, r=8, d=8, wsigma=0.3,

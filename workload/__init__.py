@@ -114,6 +114,8 @@ def _rng(seed: int, cfg: Config, stream: int) -> np.random.Generator:
 def _normal(rng, shape, sigma, chunk_rows=256):
     """fp32 N(0, sigma^2) of the given shape, drawn in row chunks to bound memory."""
     out = np.empty(shape, dtype=np.float32)
+    if out.size == 0:           # e.g. no hidden state (d = 0)
+        return out
     flat = out.reshape(-1, shape[-1])
     for i in range(0, flat.shape[0], chunk_rows):
         blk = rng.standard_normal(size=(min(chunk_rows, flat.shape[0] - i), shape[-1]),
