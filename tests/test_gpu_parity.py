@@ -507,6 +507,24 @@ def test_sts_calibration_matches_oracle(n, G, n_t, n_bins, seed):
     assert_abs(host(ece_g), ece_o, "sts ece", 1e-9)
 
 
+@pytest.mark.parametrize("hb,wb,vb", [(h, w, v) for h in (0, 1) for w in (0, 1)
+                                      for v in (0, 1)])
+def test_confidence_every_dtype_combination(hb, wb, vb):
+    """The confidence head with h, W1 and w each fp32 or bf16 (eight kernel instantiations),
+    d = 1000 (two 512-entry rounds of 16-byte loads and an element tail) and r = 96."""
+    rng = np.random.default_rng(11)
+    B, G, V, r, d = 6, 5, 700, 96, 1000
+    h = rng.standard_normal((B, G, d)).astype(np.float32)
+    W1 = (0.1 * rng.standard_normal((V, r))).astype(np.float32)
+    w = (0.05 * rng.standard_normal(d + r)).astype(np.float32)
+    h, W1, w = (workload.to_bf16_bits(x) if flag else x for x, flag in ((h, hb), (W1, wb), (w, vb)))
+    anchor = rng.integers(0, V, size=B).astype(np.int32)
+    tokens = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    c_o = oracle.confidence(h, W1, w, anchor, tokens)
+    c_g = ds.dspark_confidence(dev(h), dev(W1), dev(w), dev(anchor), dev(tokens))
+    assert_rel(host(c_g), c_o, f"confidence h{hb} W1{wb} w{vb}")
+
+
 def test_calibrated_confidence_matches_oracle():
     cfg = SMALL["bf16_rows_b16"]
     inp = workload.generate(cfg, 1)
