@@ -8,6 +8,8 @@ that a stale tile would move the normaliser and the tokens.  The workload config
 at full size run in the benchmark's launch configuration and compare every request (the
 oracle runs on a thread pool).  See tests/gpu_round.py for the protocol and tolerances.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -523,6 +525,36 @@ def test_confidence_every_dtype_combination(hb, wb, vb):
     c_o = oracle.confidence(h, W1, w, anchor, tokens)
     c_g = ds.dspark_confidence(dev(h), dev(W1), dev(w), dev(anchor), dev(tokens))
     assert_rel(host(c_g), c_o, f"confidence h{hb} W1{wb} w{vb}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_rows_b16", "mfma_b64_v_odd", "mfma_b128"])
+def test_token_ids_out_of_range_are_clamped(name):
+    """Anchor and forced ids below 0 or at/above V (a caller's error) are used as the
+    clamped ids 0 and V - 1 wherever they index a table: the draft and the confidence head
+    equal the oracle's on the clamped ids."""
+    cfg = SMALL[name]
+    inp = workload.generate(cfg, 5)
+    D = DeviceInputs(inp)
+    V = cfg.V
+    raw_anchor = inp.anchor.copy()
+    raw_anchor[0], raw_anchor[-1] = -5, V + 10
+    rng = np.random.default_rng(5)
+    raw_forced = rng.integers(0, V, size=(cfg.B, cfg.gamma)).astype(np.int32)
+    raw_forced[0, 0], raw_forced[-1, -1] = -1, V
+    raw_forced[cfg.B // 2, 0] = 2**31 - 1
+    anchor_c, forced_c = np.clip(raw_anchor, 0, V - 1), np.clip(raw_forced, 0, V - 1)
+    inp_c = dataclasses.replace(inp, anchor=anchor_c)
+    od = par_draft(inp_c, forced=forced_c)
+    tg, lg, sg = ds.dspark_draft_markov(D.U, D.W1, D.W2t, dev(raw_anchor), cfg.temperature,
+                                        inp.seed, forced=dev(raw_forced))
+    tg_h, lg_h, sg_h = host(tg), host(lg), host(sg)
+    mism = compare_tokens(tg_h, od["tokens"], od["gap"], "draft tokens (clamped ids)")
+    assert_abs(sg_h, od["lse"], "draft lse (clamped ids)", 1e-4)
+    assert_rel(np.exp(lg_h.astype(np.float64)), np.exp(od["logp"]), "p_d(x_k) (clamped ids)",
+               mask=~mism)
+    c_o = oracle.confidence(inp.h, inp.W1, inp.w, anchor_c, forced_c)
+    c_g = ds.dspark_confidence(D.h, D.W1, D.w, dev(raw_anchor), dev(raw_forced))
+    assert_rel(host(c_g), c_o, "confidence (clamped ids)")
 
 
 def test_calibrated_confidence_matches_oracle():
