@@ -557,6 +557,57 @@ def test_token_ids_out_of_range_are_clamped(name):
     assert_rel(host(c_g), c_o, "confidence (clamped ids)")
 
 
+def test_calls_on_concurrent_streams_match_sequential_calls():
+    """Draft and verification of three batches (the 16-column matrix-core draft, the
+    resident draft's cooperative launch, the row kernels) enqueued together on three
+    streams, each with its own workspaces, three times over: every output equals the same
+    calls made one after another on one stream, bit for bit."""
+    names = ["mfma_b128", "bf16_rows_b16", "tiny"]
+    runs = []
+    for name in names:
+        cfg = SMALL[name]
+        inp = workload.generate(cfg, 4)
+        D = DeviceInputs(inp)
+        B, G, V, r = cfg.B, cfg.gamma, cfg.V, cfg.r
+        tok, lp, ls = ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, cfg.temperature,
+                                             inp.seed)
+        T = dev(workload.synthesize_target(inp, host(tok)))
+        ell = dev(np.full(B, G, np.int32))
+        ws_d = torch.empty(ds.workspace_bytes(ds.OP_DRAFT, B, G, V, r), dtype=torch.uint8,
+                           device="cuda")
+        ws_v = torch.empty(ds.workspace_bytes(ds.OP_VERIFY, B, G, V, r), dtype=torch.uint8,
+                           device="cuda")
+        outs = (torch.empty_like(tok), torch.empty_like(lp), torch.empty_like(ls),
+                torch.empty(B, dtype=torch.int32, device="cuda"),
+                torch.empty((B, G + 1), dtype=torch.int32, device="cuda"),
+                torch.empty((B, G), dtype=torch.float32, device="cuda"))
+        runs.append((cfg, inp, D, T, ell, ws_d, ws_v, outs))
+
+    def enqueue(run, stream):
+        cfg, inp, D, T, ell, ws_d, ws_v, o = run
+        ds.dspark_draft_markov(D.U, D.W1, D.W2t, D.anchor, cfg.temperature, inp.seed,
+                               out=o[:3], ws=ws_d, stream=stream)
+        ds.dspark_verify(D.U, D.W1, D.W2t, D.anchor, o[0], o[1], o[2], T, ell,
+                         cfg.temperature, inp.seed, out=o[3:], ws=ws_v, stream=stream)
+
+    for run in runs:
+        enqueue(run, None)
+    torch.cuda.synchronize()
+    ref = [[t.clone() for t in run[-1]] for run in runs]
+    streams = [torch.cuda.Stream() for _ in runs]
+    for rep in range(3):
+        for run in runs:
+            for t in run[-1]:
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        for run, st in zip(runs, streams):
+            enqueue(run, st)
+        torch.cuda.synchronize()
+        for name, run, want in zip(names, runs, ref):
+            for a, b in zip(run[-1], want):
+                assert torch.equal(a, b), f"{name}: concurrent call {rep} differs"
+
+
 def test_calibrated_confidence_matches_oracle():
     cfg = SMALL["bf16_rows_b16"]
     inp = workload.generate(cfg, 1)
