@@ -496,6 +496,10 @@ def test_schedule_topk_bit_exact():
     (50000, 6, 64, 15, 1),
     (3001, 3, 7, 10, 2),          # a ragged last chunk, a short grid
     (65536, 16, 256, 15, 3),      # the serve128 draft length, a fine grid
+    (1000, 2, 1, 1, 4),           # one temperature, one bin
+    (20000, 4, 5, 256, 5),        # the most bins
+    (777, 8, 3, 2, 6),            # a short ragged set, two bins
+    (5000, 12, 9, 1, 7),          # one bin: ECE = |sum p - sum y| / n
 ])
 def test_sts_calibration_matches_oracle(n, G, n_t, n_bins, seed):
     """Chosen temperatures exactly (the seeds keep every runner-up ECE at least 1e-9 away)
